@@ -1,0 +1,249 @@
+"""CPU oracle for the quantized gated Delta-rule decode step (ctypes binding).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the CPU
+baseline leg of the benchmark, never by the product path.  It shares no code
+with the HIP library; the arithmetic lives in ``sq_oracle.c`` (plain C, FP64
+recurrence between a pinned fp32 dequantizer and quantizer).
+
+Pins: every function here is checked, in the CPU tests, against closed
+forms, identities, brute force on tiny inputs or an unquantized FP64
+recurrence.  There is no worked numeric example on the pages to compare with.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sq_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libsq_oracle.so")
+_lib = None
+
+
+def build_lib() -> str:
+    """Compile the oracle (always recompiles).  No fast-math, no contraction."""
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(
+        ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+         "-fno-fast-math", "-pthread", _SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build_lib()
+        L = ctypes.CDLL(_LIB_PATH)
+        i32, i64, vp, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+        L.sqo_qmax.restype = i32
+        L.sqo_qmax.argtypes = [i32]
+        L.sqo_row_bytes.restype = i64
+        L.sqo_row_bytes.argtypes = [i32, i32]
+        L.sqo_record_bytes.restype = i64
+        L.sqo_record_bytes.argtypes = [i32, i32, i32]
+        L.sqo_pack_row.restype = i32
+        L.sqo_pack_row.argtypes = [i32, i32, vp, vp]
+        L.sqo_unpack_row.restype = None
+        L.sqo_unpack_row.argtypes = [i32, i32, vp, vp]
+        L.sqo_quantize.restype = None
+        L.sqo_quantize.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+        L.sqo_dequantize.restype = None
+        L.sqo_dequantize.argtypes = [i32, i32, vp, vp, vp, vp]
+        L.sqo_gated_delta_f64.restype = None
+        L.sqo_gated_delta_f64.argtypes = [i32, i32, vp, vp, vp, vp, vp, ctypes.c_double, vp]
+        L.sqo_quant_step_codes.restype = None
+        L.sqo_quant_step_codes.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32,
+                                           vp, vp]
+        L.sqo_record_unpack.restype = i32
+        L.sqo_record_unpack.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+        L.sqo_record_pack.restype = i32
+        L.sqo_record_pack.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+        L.sqo_records_quantize.restype = i32
+        L.sqo_records_quantize.argtypes = [i32, i32, i32, vp, vp, vp, vp, i32]
+        L.sqo_records_dequantize.restype = i32
+        L.sqo_records_dequantize.argtypes = [i32, i32, i32, vp, vp, vp, vp, i32]
+        L.sqo_records_step.restype = i32
+        L.sqo_records_step.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       vp, i32]
+        L.sqo_f64_step.restype = i32
+        L.sqo_f64_step.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32]
+        L.sqo_f32_step.restype = i32
+        L.sqo_f32_step.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def n_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+# ---------------------------------------------------------------- format
+def qmax(bits: int) -> int:
+    return lib().sqo_qmax(bits)
+
+
+def row_bytes(bits: int, dv: int) -> int:
+    return lib().sqo_row_bytes(bits, dv)
+
+
+def record_bytes(bits: int, dk: int, dv: int) -> int:
+    return lib().sqo_record_bytes(bits, dk, dv)
+
+
+def pack_row(bits: int, codes) -> np.ndarray:
+    codes = _c(codes, np.int32)
+    out = np.zeros(row_bytes(bits, codes.size), np.uint8)
+    if lib().sqo_pack_row(bits, codes.size, _p(codes), _p(out)) != 0:
+        raise ValueError("code out of range for %d bits" % bits)
+    return out
+
+
+def unpack_row(bits: int, data, n: int) -> np.ndarray:
+    data = _c(data, np.uint8)
+    out = np.empty(n, np.int32)
+    lib().sqo_unpack_row(bits, n, _p(data), _p(out))
+    return out
+
+
+# ---------------------------------------------------------------- quantizer
+def quantize(bits: int, S) -> tuple:
+    """Pinned fp32 dual-axis quantizer: returns (Q int32, r f32 [dk], c f32 [dv])."""
+    S = _c(S, np.float32)
+    dk, dv = S.shape
+    Q = np.empty((dk, dv), np.int32)
+    r = np.empty(dk, np.float32)
+    c = np.empty(dv, np.float32)
+    lib().sqo_quantize(bits, dk, dv, _p(S), _p(Q), _p(r), _p(c))
+    return Q, r, c
+
+
+def dequantize(Q, r, c) -> np.ndarray:
+    Q = _c(Q, np.int32)
+    r = _c(r, np.float32)
+    c = _c(c, np.float32)
+    dk, dv = Q.shape
+    S = np.empty((dk, dv), np.float32)
+    lib().sqo_dequantize(dk, dv, _p(Q), _p(r), _p(c), _p(S))
+    return S
+
+
+# ---------------------------------------------------------------- recurrence
+def gated_delta_f64(S, alpha, q, k, v, beta) -> tuple:
+    """One FP64 gated Delta-rule step on a copy of S: returns (S', y)."""
+    S = np.array(S, dtype=np.float64, order="C")
+    dk, dv = S.shape
+    y = np.empty(dv, np.float64)
+    a, q, k, v = (_c(x, np.float64) for x in (alpha, q, k, v))
+    lib().sqo_gated_delta_f64(dk, dv, _p(S), _p(a), _p(q), _p(k), _p(v), float(beta), _p(y))
+    return S, y
+
+
+def quant_step_codes(kda: bool, bits: int, Q, r, c, q, k, v, beta, g) -> np.ndarray:
+    """Quantized step on unpacked codes (any bits 2..24); Q, r, c updated in place."""
+    assert Q.dtype == np.int32 and r.dtype == np.float32 and c.dtype == np.float32
+    assert Q.flags.c_contiguous
+    dk, dv = Q.shape
+    y = np.empty(dv, np.float64)
+    g = np.atleast_1d(_c(g, np.float32))
+    q, k, v = (_c(x, np.float32) for x in (q, k, v))
+    lib().sqo_quant_step_codes(int(kda), bits, dk, dv, _p(Q), _p(r), _p(c), _p(q), _p(k),
+                               _p(v), float(beta), _p(g), _p(y))
+    return y
+
+
+def record_pack(bits, Q, r, c) -> np.ndarray:
+    Q = _c(Q, np.int32)
+    dk, dv = Q.shape
+    rec = np.zeros(record_bytes(bits, dk, dv), np.uint8)
+    r = _c(r, np.float32)
+    c = _c(c, np.float32)
+    if lib().sqo_record_pack(bits, dk, dv, _p(Q), _p(r), _p(c), _p(rec)) != 0:
+        raise ValueError("code out of range")
+    return rec
+
+
+def record_unpack(bits, dk, dv, rec) -> tuple:
+    rec = _c(rec, np.uint8)
+    Q = np.empty((dk, dv), np.int32)
+    r = np.empty(dk, np.float32)
+    c = np.empty(dv, np.float32)
+    lib().sqo_record_unpack(bits, dk, dv, _p(rec), _p(Q), _p(r), _p(c))
+    return Q, r, c
+
+
+# ---------------------------------------------------------------- batches
+def records_quantize(base: np.ndarray, offs, bits, S, dk, dv):
+    offs = _c(offs, np.int64)
+    bits = _c(bits, np.uint8)
+    S = _c(S, np.float32)
+    assert base.dtype == np.uint8 and base.flags.c_contiguous
+    assert S.size == offs.size * dk * dv
+    if lib().sqo_records_quantize(offs.size, dk, dv, _p(bits), _p(offs), _p(base), _p(S),
+                                  n_threads()) != 0:
+        raise ValueError("bad arguments")
+
+
+def records_dequantize(base: np.ndarray, offs, bits, dk, dv) -> np.ndarray:
+    offs = _c(offs, np.int64)
+    bits = _c(bits, np.uint8)
+    S = np.empty((offs.size, dk, dv), np.float32)
+    base = _c(base, np.uint8)
+    if lib().sqo_records_dequantize(offs.size, dk, dv, _p(bits), _p(offs), _p(base),
+                                    _p(S), n_threads()) != 0:
+        raise ValueError("bad arguments")
+    return S
+
+
+def records_step(kda: bool, base: np.ndarray, offs, bits, dk, dv, q, k, v, beta, g) -> np.ndarray:
+    """Quantized decode step, in place on the records at base + offs[row]; returns y (f64)."""
+    offs = _c(offs, np.int64)
+    bits = _c(bits, np.uint8)
+    n = offs.size
+    assert base.dtype == np.uint8 and base.flags.c_contiguous
+    y = np.empty((n, dv), np.float64)
+    q, k, v, beta, g = (_c(x, np.float32) for x in (q, k, v, beta, g))
+    if lib().sqo_records_step(int(kda), n, dk, dv, _p(bits), _p(offs), _p(base), _p(q), _p(k),
+                              _p(v), _p(beta), _p(g), _p(y), n_threads()) != 0:
+        raise ValueError("bad arguments")
+    return y
+
+
+def f64_step(kda: bool, S: np.ndarray, q, k, v, beta, g) -> np.ndarray:
+    """Unquantized FP64 step on states S[n, dk, dv] (in place); returns y."""
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    n, dk, dv = S.shape
+    y = np.empty((n, dv), np.float64)
+    q, k, v, beta, g = (_c(x, np.float32) for x in (q, k, v, beta, g))
+    if lib().sqo_f64_step(int(kda), n, dk, dv, _p(S), _p(q), _p(k), _p(v), _p(beta), _p(g), _p(y),
+                          n_threads()) != 0:
+        raise ValueError("bad arguments")
+    return y
+
+
+def f32_step(kda: bool, S: np.ndarray, q, k, v, beta, g) -> np.ndarray:
+    """Step on fp32-stored states S[n, dk, dv] (widen, FP64 step, round back)."""
+    assert S.dtype == np.float32 and S.flags.c_contiguous
+    n, dk, dv = S.shape
+    y = np.empty((n, dv), np.float64)
+    q, k, v, beta, g = (_c(x, np.float32) for x in (q, k, v, beta, g))
+    if lib().sqo_f32_step(int(kda), n, dk, dv, _p(S), _p(q), _p(k), _p(v), _p(beta), _p(g), _p(y),
+                          n_threads()) != 0:
+        raise ValueError("bad arguments")
+    return y

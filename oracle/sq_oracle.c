@@ -1,0 +1,411 @@
+/*
+ * sq_oracle.c -- CPU oracle for the quantized gated Delta-rule decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the plain, slow reference that the HIP
+ * path is checked against.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load it; the product path never does.
+ * It shares no code, header or table with the HIP library.
+ *
+ * Sources (the pages on STEPQuant, arXiv 2609.38169):
+ *  - "Paper Explained: STEPQuant" (ta-paperlens), section "The mechanism:
+ *    rewriting state with the delta rule" (paper section 2.1): per head a
+ *    d_k x d_v state; fade it with the retention gate D_t, look up what k_t
+ *    retrieves, write only the difference to v_t with strength beta_t, read
+ *    the output with q_t.  GDN: one scalar gate per head; KDA: one gate per
+ *    key channel.  The equation itself is missing from the page; the
+ *    reading used here is
+ *        S_t = (I - beta k k^T) D_t S_{t-1} + beta k v^T,   y_t = S_t^T q_t,
+ *    evaluated in the order the words give it (decay, look-up, delta write,
+ *    read-out).
+ *  - hyper.ai summary, "Method" paragraph 1: the reconstructed state is
+ *    updated in floating point and the output computed, then the updated
+ *    state is quantized for storage (symmetric uniform quantization).
+ *  - hyper.ai summary, "Method" paragraph 4: the state is stored as row
+ *    factors x column factors x low-bit integers, each scaled entry going to
+ *    the nearest level.  The closed scale rule used here (the impact-weighted
+ *    fit has no formula on the pages) is: c_j = max_i |S_ij|, then
+ *    r_i = max_j |S_ij / c_j| / qmax.
+ *
+ * Precision: the step runs in FP64 between an fp32 dequantizer and an fp32
+ * quantizer whose operation order is fixed here (see sqo_quantize).  Build
+ * with -ffp-contract=off and without fast-math so that every fp32 operation
+ * is one correctly rounded IEEE operation.
+ *
+ * Parity pins: see the oracle tests.  Every function below is pinned by at
+ * least one closed form, identity, brute-force or convergence check.
+ */
+#include <float.h>
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* Storage format of one (slot, head) record                          */
+/* ------------------------------------------------------------------ */
+/*
+ * record = codes[d_k rows][packed d_v codes] | r[d_k] fp32 | c[d_v] fp32
+ * Codes are b-bit two's complement integers in [-qmax, qmax],
+ * qmax = 2^(b-1) - 1.  Each row is a little-endian bit stream: code j of
+ * the row occupies bits [b*j, b*j + b) of the row's bytes.  So
+ *   8-bit: byte j is code j;
+ *   4-bit: byte n holds code 2n (low nibble) and code 2n+1 (high nibble);
+ *   6-bit: bytes 3n..3n+2 hold codes 4n..4n+3 at bits 0, 6, 12, 18 of the
+ *          24-bit little-endian word they form.
+ */
+
+int sqo_qmax(int bits) { return (1 << (bits - 1)) - 1; }
+
+int64_t sqo_row_bytes(int bits, int dv) { return ((int64_t)dv * bits + 7) / 8; }
+
+int64_t sqo_record_bytes(int bits, int dk, int dv) {
+    return (int64_t)dk * sqo_row_bytes(bits, dv) + 4 * (int64_t)dk + 4 * (int64_t)dv;
+}
+
+/* Pack n codes of one row.  Returns 0, or -1 if a code is out of range. */
+int sqo_pack_row(int bits, int n, const int32_t *codes, uint8_t *out) {
+    const int64_t nbytes = sqo_row_bytes(bits, n);
+    const int32_t q = sqo_qmax(bits);
+    memset(out, 0, (size_t)nbytes);
+    for (int j = 0; j < n; ++j) {
+        if (codes[j] < -q || codes[j] > q) return -1;
+        const uint32_t field = (uint32_t)codes[j] & ((1u << bits) - 1u);
+        for (int t = 0; t < bits; ++t) {
+            const int64_t bit = (int64_t)j * bits + t;
+            if (field >> t & 1u) out[bit >> 3] |= (uint8_t)(1u << (bit & 7));
+        }
+    }
+    return 0;
+}
+
+/* Unpack n codes of one row (sign-extending each b-bit field). */
+void sqo_unpack_row(int bits, int n, const uint8_t *in, int32_t *codes) {
+    for (int j = 0; j < n; ++j) {
+        uint32_t field = 0;
+        for (int t = 0; t < bits; ++t) {
+            const int64_t bit = (int64_t)j * bits + t;
+            field |= (uint32_t)(in[bit >> 3] >> (bit & 7) & 1u) << t;
+        }
+        int32_t v = (int32_t)field;
+        if (field >> (bits - 1) & 1u) v -= (int32_t)(1u << bits);
+        codes[j] = v;
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Pinned fp32 quantizer and dequantizer                               */
+/* ------------------------------------------------------------------ */
+/*
+ * Dual-axis symmetric round-to-nearest quantizer (hyper.ai "Method" para 4,
+ * closed scale rule).  All in fp32, one rounding per operation:
+ *   c_j  = max_i |S_ij|
+ *   ic_j = c_j >= FLT_MIN ? 1/c_j : 0        (else c_j stored as 0)
+ *   m_i  = max_j (|S_ij| * ic_j)
+ *   r_i  = m_i / qmax
+ *   ir_i = r_i >= FLT_MIN ? 1/r_i : 0        (else r_i stored as 0)
+ *   Q_ij = clamp(round_half_even((S_ij * ic_j) * ir_i), -qmax, qmax)
+ */
+void sqo_quantize(int bits, int dk, int dv, const float *S, int32_t *Q, float *r, float *c) {
+    const float qmax = (float)sqo_qmax(bits);
+    float *ic = (float *)malloc(sizeof(float) * (size_t)dv);
+    for (int j = 0; j < dv; ++j) {
+        float m = 0.0f;
+        for (int i = 0; i < dk; ++i) {
+            const float a = fabsf(S[(size_t)i * dv + j]);
+            if (a > m) m = a;
+        }
+        if (m >= FLT_MIN) {
+            c[j] = m;
+            ic[j] = 1.0f / m;
+        } else {
+            c[j] = 0.0f;
+            ic[j] = 0.0f;
+        }
+    }
+    for (int i = 0; i < dk; ++i) {
+        float m = 0.0f;
+        for (int j = 0; j < dv; ++j) {
+            const float t = fabsf(S[(size_t)i * dv + j]) * ic[j];
+            if (t > m) m = t;
+        }
+        float ri = m / qmax;
+        float iri;
+        if (ri >= FLT_MIN) {
+            iri = 1.0f / ri;
+        } else {
+            ri = 0.0f;
+            iri = 0.0f;
+        }
+        r[i] = ri;
+        for (int j = 0; j < dv; ++j) {
+            const float s = S[(size_t)i * dv + j] * ic[j];
+            const float x = s * iri;
+            float qv = nearbyintf(x); /* default rounding mode: half to even */
+            if (qv > qmax) qv = qmax;
+            if (qv < -qmax) qv = -qmax;
+            Q[(size_t)i * dv + j] = (int32_t)qv;
+        }
+    }
+    free(ic);
+}
+
+/* S_ij = ((float)Q_ij * r_i) * c_j, two rounded fp32 products. */
+void sqo_dequantize(int dk, int dv, const int32_t *Q, const float *r, const float *c, float *S) {
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) {
+            const float t = (float)Q[(size_t)i * dv + j] * r[i];
+            S[(size_t)i * dv + j] = t * c[j];
+        }
+}
+
+/* ------------------------------------------------------------------ */
+/* Gated Delta rule, FP64                                              */
+/* ------------------------------------------------------------------ */
+/*
+ * One step on a double state S (d_k x d_v, row i = key channel i), in the
+ * order of the mechanism section: decay, look-up, delta write, read-out.
+ *   D     = diag(alpha),  alpha_i = exp(g) (GDN, g scalar) or exp(g_i) (KDA)
+ *   Sd    = D S
+ *   v_old = Sd^T k                      (what k currently retrieves)
+ *   u     = beta (v - v_old)            (the difference, scaled by beta)
+ *   S'    = Sd + k u^T                  (write it along k)
+ *   y     = S'^T q                      (read-out through q)
+ * alpha is supplied by the caller (already exponentiated).
+ */
+void sqo_gated_delta_f64(int dk, int dv, double *S, const double *alpha, const double *q,
+                         const double *k, const double *v, double beta, double *y) {
+    double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= alpha[i];
+    for (int j = 0; j < dv; ++j) {
+        double vo = 0.0;
+        for (int i = 0; i < dk; ++i) vo += k[i] * S[(size_t)i * dv + j];
+        u[j] = beta * (v[j] - vo);
+    }
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += k[i] * u[j];
+    for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += q[i] * S[(size_t)i * dv + j];
+        y[j] = acc;
+    }
+    free(u);
+}
+
+/* Retention factors from the log-gate: alpha_i = (float)exp((double)g).
+ * The kernels hold the gate in fp32, so the oracle rounds exp(g) to fp32 too. */
+static void gate_alpha(int kda, int dk, const float *g, double *alpha) {
+    for (int i = 0; i < dk; ++i) {
+        const float gi = kda ? g[i] : g[0];
+        alpha[i] = (double)(float)exp((double)gi);
+    }
+}
+
+/*
+ * Quantized step on one head with unpacked codes (any bits 2..24):
+ * dequantize -> FP64 gated delta step -> round S' to fp32 -> quantize.
+ * y receives the read-out of the unrequantized S' (hyper.ai "Method" para 1:
+ * the output is computed before the state is quantized for storage).
+ */
+void sqo_quant_step_codes(int kda, int bits, int dk, int dv, int32_t *Q, float *r, float *c,
+                          const float *q, const float *k, const float *v, float beta,
+                          const float *g, double *y) {
+    const size_t n = (size_t)dk * dv;
+    float *S = (float *)malloc(sizeof(float) * n);
+    double *Sd = (double *)malloc(sizeof(double) * n);
+    double *vec = (double *)malloc(sizeof(double) * (size_t)(3 * dk + dv));
+    double *alpha = vec, *qd = vec + dk, *kd = vec + 2 * dk, *vd = vec + 3 * dk;
+    sqo_dequantize(dk, dv, Q, r, c, S);
+    for (size_t e = 0; e < n; ++e) Sd[e] = (double)S[e];
+    gate_alpha(kda, dk, g, alpha);
+    for (int i = 0; i < dk; ++i) {
+        qd[i] = q[i];
+        kd[i] = k[i];
+    }
+    for (int j = 0; j < dv; ++j) vd[j] = v[j];
+    sqo_gated_delta_f64(dk, dv, Sd, alpha, qd, kd, vd, (double)beta, y);
+    for (size_t e = 0; e < n; ++e) S[e] = (float)Sd[e];
+    sqo_quantize(bits, dk, dv, S, Q, r, c);
+    free(S);
+    free(Sd);
+    free(vec);
+}
+
+/* ------------------------------------------------------------------ */
+/* Records                                                             */
+/* ------------------------------------------------------------------ */
+
+int sqo_record_unpack(int bits, int dk, int dv, const uint8_t *rec, int32_t *Q, float *r, float *c) {
+    const int64_t rb = sqo_row_bytes(bits, dv);
+    for (int i = 0; i < dk; ++i) sqo_unpack_row(bits, dv, rec + (size_t)i * rb, Q + (size_t)i * dv);
+    memcpy(r, rec + (size_t)dk * rb, sizeof(float) * (size_t)dk);
+    memcpy(c, rec + (size_t)dk * rb + 4 * (size_t)dk, sizeof(float) * (size_t)dv);
+    return 0;
+}
+
+int sqo_record_pack(int bits, int dk, int dv, const int32_t *Q, const float *r, const float *c,
+                    uint8_t *rec) {
+    const int64_t rb = sqo_row_bytes(bits, dv);
+    for (int i = 0; i < dk; ++i)
+        if (sqo_pack_row(bits, dv, Q + (size_t)i * dv, rec + (size_t)i * rb) != 0) return -1;
+    memcpy(rec + (size_t)dk * rb, r, sizeof(float) * (size_t)dk);
+    memcpy(rec + (size_t)dk * rb + 4 * (size_t)dk, c, sizeof(float) * (size_t)dv);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Row-parallel drivers                                                */
+/* ------------------------------------------------------------------ */
+/*
+ * A "row" is one (request, head) unit.  Rows are independent; the drivers
+ * only spread them over threads and never change the arithmetic.
+ * Inputs are fp32 (bf16 widened exactly by the caller):
+ *   q, k, v: [n, d]; beta: [n]; g: [n] (GDN) or [n, d_k] (KDA).
+ */
+typedef struct {
+    int op, kda, dk, dv;
+    int n0, n1;
+    const uint8_t *bits;
+    const int64_t *offs;
+    uint8_t *base;
+    float *S32;
+    double *S64;
+    const float *q, *k, *v, *beta, *g;
+    double *y;
+} job_t;
+
+enum { OP_QUANT = 0, OP_DEQUANT = 1, OP_STEP = 2, OP_F64STEP = 3, OP_F32STEP = 4 };
+
+static void run_row(const job_t *J, int row) {
+    const int dk = J->dk, dv = J->dv;
+    const size_t n = (size_t)dk * dv;
+    const float *g = J->g ? J->g + (J->kda ? (size_t)row * dk : (size_t)row) : NULL;
+    switch (J->op) {
+    case OP_QUANT: {
+        uint8_t *rec = J->base + J->offs[row];
+        int32_t *Q = (int32_t *)malloc(sizeof(int32_t) * n);
+        float rr[1024], cc[1024];
+        sqo_quantize(J->bits[row], dk, dv, J->S32 + (size_t)row * n, Q, rr, cc);
+        sqo_record_pack(J->bits[row], dk, dv, Q, rr, cc, rec);
+        free(Q);
+        break;
+    }
+    case OP_DEQUANT: {
+        const uint8_t *rec = J->base + J->offs[row];
+        int32_t *Q = (int32_t *)malloc(sizeof(int32_t) * n);
+        float rr[1024], cc[1024];
+        sqo_record_unpack(J->bits[row], dk, dv, rec, Q, rr, cc);
+        sqo_dequantize(dk, dv, Q, rr, cc, J->S32 + (size_t)row * n);
+        free(Q);
+        break;
+    }
+    case OP_STEP: {
+        uint8_t *rec = J->base + J->offs[row];
+        const int bits = J->bits[row];
+        int32_t *Q = (int32_t *)malloc(sizeof(int32_t) * n);
+        float rr[1024], cc[1024];
+        sqo_record_unpack(bits, dk, dv, rec, Q, rr, cc);
+        sqo_quant_step_codes(J->kda, bits, dk, dv, Q, rr, cc, J->q + (size_t)row * dk,
+                             J->k + (size_t)row * dk, J->v + (size_t)row * dv, J->beta[row], g,
+                             J->y + (size_t)row * dv);
+        sqo_record_pack(bits, dk, dv, Q, rr, cc, rec);
+        free(Q);
+        break;
+    }
+    case OP_F64STEP:
+    case OP_F32STEP: {
+        double *S = J->op == OP_F64STEP ? J->S64 + (size_t)row * n
+                                        : (double *)malloc(sizeof(double) * n);
+        float *S32 = J->op == OP_F32STEP ? J->S32 + (size_t)row * n : NULL;
+        if (S32)
+            for (size_t e = 0; e < n; ++e) S[e] = (double)S32[e];
+        double alpha[1024], qd[1024], kd[1024], vd[1024];
+        gate_alpha(J->kda, dk, g, alpha);
+        for (int i = 0; i < dk; ++i) {
+            qd[i] = J->q[(size_t)row * dk + i];
+            kd[i] = J->k[(size_t)row * dk + i];
+        }
+        for (int j = 0; j < dv; ++j) vd[j] = J->v[(size_t)row * dv + j];
+        sqo_gated_delta_f64(dk, dv, S, alpha, qd, kd, vd, (double)J->beta[row],
+                            J->y + (size_t)row * dv);
+        if (S32) {
+            for (size_t e = 0; e < n; ++e) S32[e] = (float)S[e];
+            free(S);
+        }
+        break;
+    }
+    }
+}
+
+static void *worker(void *arg) {
+    const job_t *J = (const job_t *)arg;
+    for (int r = J->n0; r < J->n1; ++r) run_row(J, r);
+    return NULL;
+}
+
+static int run_rows(job_t proto, int n_rows, int n_threads) {
+    if (proto.dk <= 0 || proto.dk > 1024 || proto.dv <= 0 || proto.dv > 1024 || n_rows < 0)
+        return -1;
+    if (n_threads < 1) n_threads = 1;
+    if (n_threads > 64) n_threads = 64;
+    if (n_threads > n_rows) n_threads = n_rows > 0 ? n_rows : 1;
+    job_t jobs[64];
+    pthread_t th[64];
+    for (int w = 0; w < n_threads; ++w) {
+        jobs[w] = proto;
+        jobs[w].n0 = (int)((int64_t)n_rows * w / n_threads);
+        jobs[w].n1 = (int)((int64_t)n_rows * (w + 1) / n_threads);
+    }
+    for (int w = 1; w < n_threads; ++w) pthread_create(&th[w], NULL, worker, &jobs[w]);
+    worker(&jobs[0]);
+    for (int w = 1; w < n_threads; ++w) pthread_join(th[w], NULL);
+    return 0;
+}
+
+static int check_bits(int n, const uint8_t *bits) {
+    for (int i = 0; i < n; ++i)
+        if (bits[i] != 4 && bits[i] != 6 && bits[i] != 8) return -1;
+    return 0;
+}
+
+/* Quantize fp32 states S[n, dk, dv] into the records at base + offs[row]. */
+int sqo_records_quantize(int n, int dk, int dv, const uint8_t *bits, const int64_t *offs,
+                         uint8_t *base, const float *S, int n_threads) {
+    if (check_bits(n, bits)) return -1;
+    job_t J = {OP_QUANT, 0, dk, dv, 0, 0, bits, offs, base, (float *)S, NULL,
+               NULL, NULL, NULL, NULL, NULL, NULL};
+    return run_rows(J, n, n_threads);
+}
+
+/* Dequantize the records into S[n, dk, dv]. */
+int sqo_records_dequantize(int n, int dk, int dv, const uint8_t *bits, const int64_t *offs,
+                           const uint8_t *base, float *S, int n_threads) {
+    if (check_bits(n, bits)) return -1;
+    job_t J = {OP_DEQUANT, 0, dk, dv, 0, 0, bits, offs, (uint8_t *)base, S, NULL,
+               NULL, NULL, NULL, NULL, NULL, NULL};
+    return run_rows(J, n, n_threads);
+}
+
+/* One quantized decode step, in place on the records; y[n, dv] in double. */
+int sqo_records_step(int kda, int n, int dk, int dv, const uint8_t *bits, const int64_t *offs,
+                     uint8_t *base, const float *q, const float *k, const float *v,
+                     const float *beta, const float *g, double *y, int n_threads) {
+    if (check_bits(n, bits)) return -1;
+    job_t J = {OP_STEP, kda, dk, dv, 0, 0, bits, offs, base, NULL, NULL, q, k, v, beta, g, y};
+    return run_rows(J, n, n_threads);
+}
+
+/* One unquantized step on FP64 states S[n, dk, dv] (in place). */
+int sqo_f64_step(int kda, int n, int dk, int dv, double *S, const float *q, const float *k,
+                 const float *v, const float *beta, const float *g, double *y, int n_threads) {
+    job_t J = {OP_F64STEP, kda, dk, dv, 0, 0, NULL, NULL, NULL, NULL, S, q, k, v, beta, g, y};
+    return run_rows(J, n, n_threads);
+}
+
+/* One step on fp32-stored states S[n, dk, dv]: widen, FP64 step, round back. */
+int sqo_f32_step(int kda, int n, int dk, int dv, float *S, const float *q, const float *k,
+                 const float *v, const float *beta, const float *g, double *y, int n_threads) {
+    job_t J = {OP_F32STEP, kda, dk, dv, 0, 0, NULL, NULL, NULL, S, NULL, q, k, v, beta, g, y};
+    return run_rows(J, n, n_threads);
+}

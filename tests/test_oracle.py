@@ -1,0 +1,527 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each check below is chosen so that a plausible slip in the oracle (a dropped
+term, a wrong sign, a transposed operand, a wrong tie rule, a wrong scale
+axis, a shifted bit field) fails at least one of them:
+
+* encoding: hand-derived golden rows, an independent big-integer packer,
+  exhaustive round trips;
+* quantizer: hand-derived ties, exact rational brute force on 4x4 states,
+  idempotence, scale/sign equivariance, the max-level property, error bound;
+* recurrence: the transition-matrix form of the step, exact rationals, the
+  delta-rule identities (unit key writes v exactly, basis keys overwrite one
+  row, orthogonal directions only decay), read-out through basis queries;
+* the quantized loop: the error-propagation identity (error now = transition
+  applied to yesterday's error + fresh rounding error), convergence to the
+  unquantized FP64 recurrence as the bit width grows, KDA == GDN when all
+  channel gates are equal, the beta = 0 / gate = 1 identity.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workload as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append([p.strip() for p in line.split("|")])
+    return rows
+
+
+def _rand_state(rng, dk, dv, scale_rows=True, scale_cols=True):
+    """Dense state with outliers along rows and columns (dual-axis geometry)."""
+    S = rng.standard_normal((dk, dv))
+    if scale_rows:
+        S *= np.exp(rng.standard_normal(dk))[:, None]
+    if scale_cols:
+        S *= np.exp(rng.standard_normal(dv))[None, :]
+    return S.astype(np.float32)
+
+
+# ------------------------------------------------------------------ encoding
+def test_pack_golden_rows():
+    for bits, codes, hexbytes in _golden("pack_examples.txt"):
+        bits = int(bits)
+        codes = np.array([int(x) for x in codes.split()], np.int32)
+        want = bytes.fromhex(hexbytes.replace(" ", ""))
+        got = O.pack_row(bits, codes).tobytes()
+        assert got == want, (bits, codes, got.hex(), want.hex())
+        assert np.array_equal(O.unpack_row(bits, np.frombuffer(want, np.uint8), codes.size), codes)
+
+
+def _bigint_pack(bits, codes):
+    acc = 0
+    for j, cde in enumerate(codes):
+        acc |= (int(cde) % (1 << bits)) << (bits * j)
+    nbytes = (len(codes) * bits + 7) // 8
+    return acc.to_bytes(nbytes, "little")
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_pack_matches_bigint_bitstream(bits):
+    rng = np.random.default_rng(bits)
+    q = O.qmax(bits)
+    for n in (8, 16, 64, 128):
+        codes = rng.integers(-q, q + 1, n).astype(np.int32)
+        assert O.pack_row(bits, codes).tobytes() == _bigint_pack(bits, codes)
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_pack_roundtrip_exhaustive(bits):
+    """Every code value at every position of a 24-code row (covers every
+    position inside the 2-code, 4-code and 1-code groups)."""
+    q = O.qmax(bits)
+    rng = np.random.default_rng(100 + bits)
+    n = 24
+    for pos in range(n):
+        base = rng.integers(-q, q + 1, n).astype(np.int32)
+        for val in range(-q, q + 1):
+            base[pos] = val
+            packed = O.pack_row(bits, base)
+            assert np.array_equal(O.unpack_row(bits, packed, n), base)
+
+
+def test_pack_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        O.pack_row(4, np.array([8, 0], np.int32))
+    with pytest.raises(ValueError):
+        O.pack_row(6, np.array([0, 0, 0, -32], np.int32))  # -2^(b-1) is never produced
+
+
+def test_record_bytes_and_compression():
+    # d = 128: codes 8192 / 12288 / 16384 B + 1024 B of fp32 scales
+    assert [O.record_bytes(b, 128, 128) for b in (4, 6, 8)] == [9216, 13312, 17408]
+    assert [O.record_bytes(b, 64, 64) for b in (4, 6, 8)] == [2560, 3584, 4608]
+    fp32 = 128 * 128 * 4
+    ratios = [fp32 / O.record_bytes(b, 128, 128) for b in (4, 6, 8)]
+    assert [round(r, 2) for r in ratios] == [7.11, 4.92, 3.76]
+    # every record is a whole number of 256-byte units (aligned pool records)
+    for b in (4, 6, 8):
+        for d in (64, 128):
+            assert O.record_bytes(b, d, d) % 256 == 0
+
+
+# ------------------------------------------------------------------ quantizer
+def test_quant_golden_ties():
+    for bits, S, codes, r1 in _golden("quant_ties.txt"):
+        bits = int(bits)
+        S = np.array([float(x) for x in S.split()], np.float32).reshape(2, 2)
+        codes = np.array([int(x) for x in codes.split()], np.int32).reshape(2, 2)
+        Q, r, c = O.quantize(bits, S)
+        assert np.array_equal(Q, codes), (S, Q, codes)
+        assert r[1] == np.float32(float(r1))
+        assert np.array_equal(c, np.abs(S).max(axis=0))
+
+
+def _nearest_even(x: Fraction) -> int:
+    f = math.floor(x)
+    d = x - f
+    if d > Fraction(1, 2):
+        return f + 1
+    if d < Fraction(1, 2):
+        return f
+    return f if f % 2 == 0 else f + 1
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_quant_bruteforce_4x4_exact(bits):
+    """Each code is the nearest level to S_ij / (r_i c_j) in exact rational
+    arithmetic, searched over every level; scales follow the closed rule."""
+    q = O.qmax(bits)
+    rng = np.random.default_rng(7 + bits)
+    near_ties = 0
+    for trial in range(200):
+        S = _rand_state(rng, 4, 4)
+        Q, r, c = O.quantize(bits, S)
+        Sf = [[Fraction(float(S[i, j])) for j in range(4)] for i in range(4)]
+        for j in range(4):
+            assert Fraction(float(c[j])) == max(abs(Sf[i][j]) for i in range(4))
+        for i in range(4):
+            m = max(abs(Sf[i][j]) / Fraction(float(c[j])) for j in range(4))
+            assert abs(Fraction(float(r[i])) - m / q) <= m / q * Fraction(3, 2 ** 24)
+            for j in range(4):
+                rc = Fraction(float(r[i])) * Fraction(float(c[j]))
+                best = min(range(-q, q + 1),
+                           key=lambda lv: (abs(Sf[i][j] - lv * rc), lv % 2))
+                x = Sf[i][j] / rc
+                assert best == _nearest_even(x)
+                if abs(x - math.floor(x) - Fraction(1, 2)) < Fraction(1, 10 ** 5):
+                    near_ties += 1
+                    assert abs(int(Q[i, j]) - best) <= 1
+                else:
+                    assert int(Q[i, j]) == best, (trial, i, j, float(x))
+    assert near_ties < 5
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8, 12, 16])
+def test_quant_dequant_idempotent(bits):
+    rng = np.random.default_rng(bits)
+    for d in (8, 64, 128):
+        S = _rand_state(rng, d, d)
+        Q, r, c = O.quantize(bits, S)
+        Q2, r2, c2 = O.quantize(bits, O.dequantize(Q, r, c))
+        assert np.array_equal(Q, Q2)
+        np.testing.assert_allclose(r2, r, rtol=4 * 2.0 ** -23)
+        np.testing.assert_allclose(c2, c, rtol=4 * 2.0 ** -23)
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_quant_every_row_and_column_hits_qmax(bits):
+    rng = np.random.default_rng(11)
+    q = O.qmax(bits)
+    S = _rand_state(rng, 128, 128)
+    Q, r, c = O.quantize(bits, S)
+    assert (np.abs(Q).max(axis=0) == q).all()
+    assert (np.abs(Q).max(axis=1) == q).all()
+    assert np.abs(Q).max() <= q
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_quant_error_bound(bits):
+    rng = np.random.default_rng(12)
+    S = _rand_state(rng, 128, 128)
+    Q, r, c = O.quantize(bits, S)
+    step = r.astype(np.float64)[:, None] * c.astype(np.float64)[None, :]
+    err = np.abs(S.astype(np.float64) - O.dequantize(Q, r, c).astype(np.float64))
+    assert (err <= 0.5 * step * (1 + 1e-5) + 1e-30).all()
+
+
+def test_quant_equivariance():
+    rng = np.random.default_rng(13)
+    S = _rand_state(rng, 64, 64)
+    Q, r, c = O.quantize(6, S)
+    Qn, rn, cn = O.quantize(6, -S)
+    assert np.array_equal(Qn, -Q) and np.array_equal(rn, r) and np.array_equal(cn, c)
+    Qs, rs, cs = O.quantize(6, S * np.float32(2.0 ** 20))
+    assert np.array_equal(Qs, Q) and np.array_equal(rs, r) and np.array_equal(cs, c * 2.0 ** 20)
+    # scaling one column by a power of two moves only that column's scale
+    S2 = S.copy()
+    S2[:, 5] *= 8
+    Q2, r2, c2 = O.quantize(6, S2)
+    assert np.array_equal(Q2, Q) and np.array_equal(r2, r)
+    assert c2[5] == 8 * c[5] and np.array_equal(np.delete(c2, 5), np.delete(c, 5))
+
+
+def test_quant_zero_row_column_and_tiny():
+    S = np.zeros((8, 8), np.float32)
+    Q, r, c = O.quantize(6, S)
+    assert not Q.any() and not r.any() and not c.any()
+    rng = np.random.default_rng(14)
+    S = _rand_state(rng, 8, 8)
+    S[3, :] = 0
+    S[:, 5] = 0
+    S[6, 2] = 1e-39  # subnormal entry in an otherwise normal column
+    Q, r, c = O.quantize(6, S)
+    assert r[3] == 0 and not Q[3].any()
+    assert c[5] == 0 and not Q[:, 5].any()
+    S = np.zeros((4, 4), np.float32)
+    S[1, 1] = 1e-40  # only a subnormal: column max below FLT_MIN -> stored as zero
+    Q, r, c = O.quantize(8, S)
+    assert not Q.any() and c[1] == 0
+
+
+def test_dequant_exact_for_power_of_two_scales():
+    rng = np.random.default_rng(15)
+    Q = rng.integers(-31, 32, (16, 16)).astype(np.int32)
+    r = (2.0 ** rng.integers(-20, 5, 16)).astype(np.float32)
+    c = (2.0 ** rng.integers(-20, 5, 16)).astype(np.float32)
+    want = Q.astype(np.float64) * r[:, None].astype(np.float64) * c[None, :].astype(np.float64)
+    assert np.array_equal(O.dequantize(Q, r, c).astype(np.float64), want)
+    # general scales: within one rounding of each of the two products
+    r = rng.random(16).astype(np.float32)
+    c = rng.random(16).astype(np.float32)
+    want = Q.astype(np.float64) * r[:, None] * c[None, :]
+    np.testing.assert_allclose(O.dequantize(Q, r, c), want, rtol=2.5 * 2.0 ** -24, atol=0)
+
+
+def test_magic_number_rounding_identity():
+    """fl(x + 1.5*2^23) - 1.5*2^23 == round_half_even(x) for |x| < 2^22: the
+    shortcut the GPU epilogue uses.  Dense grid of k/2^16 over [-256, 256],
+    every half-integer, and random fp32 values across the range."""
+    M = np.float32(1.5 * 2 ** 23)
+    xs = [np.arange(-256 * 2 ** 16, 256 * 2 ** 16 + 1, dtype=np.int64).astype(np.float32)
+          / np.float32(2 ** 16),
+          np.arange(-2 ** 12, 2 ** 12, dtype=np.float32) + np.float32(0.5)]
+    rng = np.random.default_rng(16)
+    xs.append((rng.random(2_000_000) * 2 ** 23 - 2 ** 22).astype(np.float32))
+    for x in xs:
+        got = (x + M) - M
+        assert np.array_equal(got, np.rint(x))
+        # low bits of the sum's bit pattern are the two's complement code
+        bitsum = (x + M).view(np.uint32)
+        lo = (bitsum & 0xFF).astype(np.int64)
+        assert np.array_equal(lo, np.rint(x).astype(np.int64) & 0xFF)
+
+
+# ------------------------------------------------------------------ recurrence
+def _inputs(rng, dk, dv, kda=False):
+    q = rng.standard_normal(dk)
+    q /= np.linalg.norm(q)
+    k = rng.standard_normal(dk)
+    k /= np.linalg.norm(k)
+    v = rng.standard_normal(dv)
+    beta = 1 / (1 + math.exp(-rng.standard_normal()))
+    alpha = np.exp(-rng.uniform(0.001, 0.5, dk if kda else 1)) * np.ones(dk)
+    return q, k, v, beta, alpha
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_step_matches_transition_matrix_form(kda):
+    """S' = (I - beta k k^T) D S + beta k v^T and y = S'^T q, as matrices."""
+    rng = np.random.default_rng(20 + kda)
+    for dk, dv in ((4, 4), (16, 32), (64, 64)):
+        S = rng.standard_normal((dk, dv))
+        q, k, v, beta, alpha = _inputs(rng, dk, dv, kda)
+        S1, y = O.gated_delta_f64(S, alpha, q, k, v, beta)
+        A = (np.eye(dk) - beta * np.outer(k, k)) @ np.diag(alpha)
+        want = A @ S + beta * np.outer(k, v)
+        np.testing.assert_allclose(S1, want, rtol=0, atol=1e-13 * np.abs(want).max())
+        np.testing.assert_allclose(y, want.T @ q, rtol=0, atol=1e-13 * np.abs(want).max())
+
+
+def test_step_exact_rational_4x4():
+    """Exact rational evaluation of the transition-matrix form on 4x4 inputs."""
+    rng = np.random.default_rng(22)
+    for _ in range(20):
+        S = rng.standard_normal((4, 4))
+        q, k, v, beta, alpha = _inputs(rng, 4, 4, True)
+        S1, y = O.gated_delta_f64(S, alpha, q, k, v, beta)
+        F = Fraction
+        Sf = [[F(S[i, j]) for j in range(4)] for i in range(4)]
+        kf, qf, vf, af, bf = ([F(x) for x in k], [F(x) for x in q], [F(x) for x in v],
+                              [F(x) for x in alpha], F(beta))
+        A = [[((1 if i == m else 0) - bf * kf[i] * kf[m]) * af[m] for m in range(4)]
+             for i in range(4)]
+        want = [[sum(A[i][m] * Sf[m][j] for m in range(4)) + bf * kf[i] * vf[j]
+                 for j in range(4)] for i in range(4)]
+        yw = [sum(qf[i] * want[i][j] for i in range(4)) for j in range(4)]
+        for i in range(4):
+            for j in range(4):
+                assert abs(F(S1[i, j]) - want[i][j]) <= F(1, 10 ** 14)
+        for j in range(4):
+            assert abs(F(y[j]) - yw[j]) <= F(1, 10 ** 14)
+
+
+def test_delta_rule_identities():
+    rng = np.random.default_rng(23)
+    dk = dv = 64
+    S = rng.standard_normal((dk, dv))
+    q, k, v, beta, _ = _inputs(rng, dk, dv)
+    one = np.ones(dk)
+    # unit key, full write strength, no decay: the key now retrieves v exactly
+    S1, _ = O.gated_delta_f64(S, one, q, k, v, 1.0)
+    np.testing.assert_allclose(S1.T @ k, v, rtol=0, atol=1e-12)
+    # partial strength: read-out along k moves a fraction beta toward v
+    S1, _ = O.gated_delta_f64(S, one, q, k, v, beta)
+    np.testing.assert_allclose(S1.T @ k, (1 - beta) * (S.T @ k) + beta * v, rtol=0, atol=1e-12)
+    # directions orthogonal to k are untouched by the write (only decayed)
+    w = rng.standard_normal(dk)
+    w -= (w @ k) * k
+    a = 0.9 * one
+    S1, _ = O.gated_delta_f64(S, a, q, k, v, beta)
+    np.testing.assert_allclose(S1.T @ w, 0.9 * (S.T @ w), rtol=0, atol=1e-12)
+    # basis key: row m is overwritten by v, every other row unchanged bit for bit
+    m = 17
+    e = np.zeros(dk)
+    e[m] = 1.0
+    S1, y = O.gated_delta_f64(S, one, q, e, v, 1.0)
+    np.testing.assert_allclose(S1[m], v, rtol=0, atol=1e-15)
+    assert np.array_equal(np.delete(S1, m, axis=0), np.delete(S, m, axis=0))
+    # basis query reads one row of the new state
+    S1, y = O.gated_delta_f64(S, a, e, k, v, beta)
+    assert np.array_equal(y, S1[m])
+    # beta = 0: pure decay, D S
+    S1, y = O.gated_delta_f64(S, a, q, k, v, 0.0)
+    assert np.array_equal(S1, S * 0.9)
+
+
+# ------------------------------------------------------------------ quantized loop
+def _seq(rng, T, dk, dv, kda):
+    seq = []
+    for _ in range(T):
+        q, k, v, beta, _ = _inputs(rng, dk, dv, kda)
+        g = -rng.uniform(0.001, 0.5, dk if kda else 1)
+        seq.append((q.astype(np.float32), k.astype(np.float32), v.astype(np.float32),
+                    np.float32(beta), g.astype(np.float32)))
+    return seq
+
+
+def _alpha(kda, dk, g):
+    return np.array([float(np.float32(math.exp(float(g[i if kda else 0])))) for i in range(dk)])
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_error_propagation_identity(kda):
+    """E_t = (I - beta k k^T) D_t E_{t-1} + eps_t, with E the gap between the
+    quantized and the exact trajectories and eps_t the fresh requantization
+    error of step t (the error-propagation proposition, section 3.1)."""
+    rng = np.random.default_rng(30 + kda)
+    dk = dv = 32
+    bits = 6
+    S0 = rng.standard_normal((dk, dv)).astype(np.float32)
+    Q, r, c = O.quantize(bits, S0)
+    Sq = O.dequantize(Q, r, c).astype(np.float64)
+    St = Sq.copy()  # exact trajectory from the same start: E_0 = 0
+    E = np.zeros((dk, dv))
+    for q, k, v, beta, g in _seq(rng, 24, dk, dv, kda):
+        alpha = _alpha(kda, dk, g)
+        Fq, _ = O.gated_delta_f64(Sq, alpha, q, k, v, beta)        # F_t(S^q_{t-1})
+        y = O.quant_step_codes(kda, bits, Q, r, c, q, k, v, beta, g)
+        Sq = O.dequantize(Q, r, c).astype(np.float64)
+        eps = Sq - Fq
+        St, _ = O.gated_delta_f64(St, alpha, q, k, v, beta)
+        k64 = k.astype(np.float64)
+        A = (np.eye(dk) - float(beta) * np.outer(k64, k64)) @ np.diag(alpha)
+        E_new = Sq - St
+        np.testing.assert_allclose(E_new, A @ E + eps, rtol=0,
+                                   atol=1e-12 * max(1.0, np.abs(St).max()))
+        np.testing.assert_allclose(y, Fq.T @ q.astype(np.float64), rtol=0, atol=1e-12)
+        E = E_new
+
+
+def _rel(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_quantized_recurrence_converges_to_fp64(kda):
+    """As bits grow by 4, the quantized trajectory's error falls about 16x
+    until it reaches the fp32 floor; at 16 bits it is far below 1e-3."""
+    rng = np.random.default_rng(40 + kda)
+    dk = dv = 64
+    T = 64
+    seq = _seq(rng, T, dk, dv, kda)
+    S0 = np.zeros((dk, dv))
+    errs = {}
+    for bits in (8, 12, 16, 20, 24):
+        St = S0.copy()
+        Q, r, c = O.quantize(bits, S0.astype(np.float32))
+        worst = 0.0
+        for q, k, v, beta, g in seq:
+            O.quant_step_codes(kda, bits, Q, r, c, q, k, v, beta, g)
+            St, _ = O.gated_delta_f64(St, _alpha(kda, dk, g), q, k, v, beta)
+            worst = max(worst, _rel(O.dequantize(Q, r, c).astype(np.float64), St))
+        errs[bits] = worst
+    for b in (8, 12):
+        assert 8 < errs[b] / errs[b + 4] < 32, errs
+    assert errs[16] < 1e-3 and errs[24] < 2e-6, errs
+
+
+def test_kda_equals_gdn_with_equal_channel_gates():
+    rng = np.random.default_rng(50)
+    dk = dv = 64
+    S0 = _rand_state(rng, dk, dv)
+    for bits in (4, 6, 8):
+        Qa, ra, ca = O.quantize(bits, S0)
+        Qb, rb, cb = Qa.copy(), ra.copy(), ca.copy()
+        for q, k, v, beta, g in _seq(rng, 8, dk, dv, False):
+            ya = O.quant_step_codes(False, bits, Qa, ra, ca, q, k, v, beta, g)
+            yb = O.quant_step_codes(True, bits, Qb, rb, cb, q, k, v, beta,
+                                    np.full(dk, g[0], np.float32))
+            assert np.array_equal(ya, yb)
+        assert np.array_equal(Qa, Qb) and np.array_equal(ra, rb) and np.array_equal(ca, cb)
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_beta0_gate1_keeps_codes(bits):
+    """No write (beta = 0) and no decay (log-gate 0): one step leaves every
+    code unchanged and the scales within a few ulp; y = S~^T q."""
+    rng = np.random.default_rng(60 + bits)
+    dk = dv = 128
+    Q, r, c = O.quantize(bits, _rand_state(rng, dk, dv))
+    Q0, r0, c0 = Q.copy(), r.copy(), c.copy()
+    q, k, v, _, _ = _inputs(rng, dk, dv)
+    y = O.quant_step_codes(False, bits, Q, r, c, q.astype(np.float32), k.astype(np.float32),
+                           v.astype(np.float32), 0.0, np.zeros(1, np.float32))
+    assert np.array_equal(Q, Q0)
+    np.testing.assert_allclose(r, r0, rtol=4 * 2.0 ** -23)
+    np.testing.assert_allclose(c, c0, rtol=4 * 2.0 ** -23)
+    St = O.dequantize(Q0, r0, c0).astype(np.float64)
+    np.testing.assert_allclose(y, St.T @ q.astype(np.float32).astype(np.float64), rtol=0,
+                               atol=1e-12)
+
+
+# ------------------------------------------------------------------ batch drivers
+def test_records_drivers_match_single_head():
+    rng = np.random.default_rng(70)
+    dk = dv = 64
+    n = 6
+    bits = np.array([4, 6, 8, 6, 4, 8], np.uint8)
+    sizes = [O.record_bytes(int(b), dk, dv) for b in bits]
+    # records laid out in reverse order, so row i is not at the i-th position
+    offs = np.zeros(n, np.int64)
+    pos = 0
+    for i in reversed(range(n)):
+        offs[i] = pos
+        pos += sizes[i]
+    base = np.zeros(sum(sizes), np.uint8)
+    S = np.stack([_rand_state(rng, dk, dv) for _ in range(n)])
+    O.records_quantize(base, offs, bits, S, dk, dv)
+    for kda in (False, True):
+        q = rng.standard_normal((n, dk)).astype(np.float32)
+        k = rng.standard_normal((n, dk)).astype(np.float32)
+        v = rng.standard_normal((n, dv)).astype(np.float32)
+        beta = rng.random(n).astype(np.float32)
+        g = -rng.uniform(0.001, 0.5, (n, dk) if kda else n).astype(np.float32)
+        singles = []
+        for i in range(n):
+            Qi, ri, ci = O.record_unpack(int(bits[i]), dk, dv, base[offs[i]:offs[i] + sizes[i]])
+            assert np.array_equal(O.dequantize(Qi, ri, ci),
+                                  O.records_dequantize(base, offs[i:i + 1], bits[i:i + 1],
+                                                       dk, dv)[0])
+            yi = O.quant_step_codes(kda, int(bits[i]), Qi, ri, ci, q[i], k[i], v[i], beta[i],
+                                    g[i] if kda else g[i:i + 1])
+            singles.append((O.record_pack(int(bits[i]), Qi, ri, ci), yi))
+        y = O.records_step(kda, base, offs, bits, dk, dv, q, k, v, beta, g)
+        for i in range(n):
+            assert np.array_equal(base[offs[i]:offs[i] + sizes[i]], singles[i][0])
+            assert np.array_equal(y[i], singles[i][1])
+
+
+def test_f32_step_is_rounded_f64_step():
+    rng = np.random.default_rng(71)
+    n, d = 3, 32
+    S = rng.standard_normal((n, d, d)).astype(np.float32)
+    q = rng.standard_normal((n, d)).astype(np.float32)
+    k = rng.standard_normal((n, d)).astype(np.float32)
+    v = rng.standard_normal((n, d)).astype(np.float32)
+    beta = rng.random(n).astype(np.float32)
+    g = -rng.uniform(0.001, 0.5, n).astype(np.float32)
+    S64 = S.astype(np.float64)
+    y64 = O.f64_step(False, S64, q, k, v, beta, g)
+    S32 = S.copy()
+    y32 = O.f32_step(False, S32, q, k, v, beta, g)
+    assert np.array_equal(S32, S64.astype(np.float32))
+    assert np.array_equal(y32, y64)
+
+
+def test_oracle_thread_count_independent(monkeypatch):
+    wl = W.custom("gdn", 4, 3, 64, [4, 6, 8], dtype="f32")
+    layer = wl.layers[0]
+    x = wl.step_inputs(layer, 0)
+    rng = np.random.default_rng(72)
+    S = np.stack([_rand_state(rng, 64, 64) for _ in range(12)])
+    bits = np.tile(layer.head_bits, 4)
+    sizes = [O.record_bytes(int(b), 64, 64) for b in bits]
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.int64)
+    outs = []
+    for nt in (1, 5):
+        monkeypatch.setattr(O, "n_threads", lambda nt=nt: nt)
+        base = np.zeros(sum(sizes), np.uint8)
+        O.records_quantize(base, offs, bits, S, 64, 64)
+        y = O.records_step(False, base, offs, bits, 64, 64, x["q"], x["k"], x["v"], x["beta"],
+                           x["g"])
+        outs.append((base, y))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
