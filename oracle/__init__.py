@@ -52,6 +52,8 @@ def lib():
         L.sqo_unpack_row.argtypes = [i32, i32, vp, vp]
         L.sqo_quantize.restype = None
         L.sqo_quantize.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+        L.sqo_reconstruct_f64.restype = None
+        L.sqo_reconstruct_f64.argtypes = [i32, i32, vp, vp, vp, vp]
         L.sqo_dequantize.restype = None
         L.sqo_dequantize.argtypes = [i32, i32, vp, vp, vp, vp]
         L.sqo_gated_delta_f64.restype = None
@@ -134,7 +136,19 @@ def quantize(bits: int, S) -> tuple:
     return Q, r, c
 
 
+def reconstruct_f64(Q, r, c) -> np.ndarray:
+    """FP64 reconstruction ((double)Q * r) * c used inside the decode step."""
+    Q = _c(Q, np.int32)
+    r = _c(r, np.float32)
+    c = _c(c, np.float32)
+    dk, dv = Q.shape
+    S = np.empty((dk, dv), np.float64)
+    lib().sqo_reconstruct_f64(dk, dv, _p(Q), _p(r), _p(c), _p(S))
+    return S
+
+
 def dequantize(Q, r, c) -> np.ndarray:
+    """fp32 export of the reconstruction: (float)(((double)Q * r) * c)."""
     Q = _c(Q, np.int32)
     r = _c(r, np.float32)
     c = _c(c, np.float32)

@@ -150,13 +150,26 @@ void sqo_quantize(int bits, int dk, int dv, const float *S, int32_t *Q, float *r
     free(ic);
 }
 
-/* S_ij = ((float)Q_ij * r_i) * c_j, two rounded fp32 products. */
+/*
+ * Reconstruction (hyper.ai "Method" para 4: the state is the product of row
+ * factors, column factors and low-bit integers): S_ij = Q_ij * r_i * c_j,
+ * evaluated in FP64 as ((double)Q_ij * r_i) * c_j.  Q_ij * r_i is exact; the
+ * second product is exact for |Q| <= 31 (at most 53 significant bits) and
+ * rounded once (2^-53 relative) for 8-bit codes.
+ */
+void sqo_reconstruct_f64(int dk, int dv, const int32_t *Q, const float *r, const float *c,
+                         double *S) {
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j)
+            S[(size_t)i * dv + j] = ((double)Q[(size_t)i * dv + j] * (double)r[i]) * (double)c[j];
+}
+
+/* fp32 export of the reconstruction: (float)(((double)Q_ij * r_i) * c_j). */
 void sqo_dequantize(int dk, int dv, const int32_t *Q, const float *r, const float *c, float *S) {
     for (int i = 0; i < dk; ++i)
-        for (int j = 0; j < dv; ++j) {
-            const float t = (float)Q[(size_t)i * dv + j] * r[i];
-            S[(size_t)i * dv + j] = t * c[j];
-        }
+        for (int j = 0; j < dv; ++j)
+            S[(size_t)i * dv + j] =
+                (float)(((double)Q[(size_t)i * dv + j] * (double)r[i]) * (double)c[j]);
 }
 
 /* ------------------------------------------------------------------ */
@@ -204,9 +217,10 @@ static void gate_alpha(int kda, int dk, const float *g, double *alpha) {
 
 /*
  * Quantized step on one head with unpacked codes (any bits 2..24):
- * dequantize -> FP64 gated delta step -> round S' to fp32 -> quantize.
- * y receives the read-out of the unrequantized S' (hyper.ai "Method" para 1:
- * the output is computed before the state is quantized for storage).
+ * FP64 reconstruction -> FP64 gated delta step -> round S' to fp32 ->
+ * pinned fp32 quantizer.  y receives the read-out of the unrequantized S'
+ * (hyper.ai "Method" para 1: the state is updated in floating point and the
+ * output computed, then the updated state is quantized for storage).
  */
 void sqo_quant_step_codes(int kda, int bits, int dk, int dv, int32_t *Q, float *r, float *c,
                           const float *q, const float *k, const float *v, float beta,
@@ -216,8 +230,7 @@ void sqo_quant_step_codes(int kda, int bits, int dk, int dv, int32_t *Q, float *
     double *Sd = (double *)malloc(sizeof(double) * n);
     double *vec = (double *)malloc(sizeof(double) * (size_t)(3 * dk + dv));
     double *alpha = vec, *qd = vec + dk, *kd = vec + 2 * dk, *vd = vec + 3 * dk;
-    sqo_dequantize(dk, dv, Q, r, c, S);
-    for (size_t e = 0; e < n; ++e) Sd[e] = (double)S[e];
+    sqo_reconstruct_f64(dk, dv, Q, r, c, Sd);
     gate_alpha(kda, dk, g, alpha);
     for (int i = 0; i < dk; ++i) {
         qd[i] = q[i];

@@ -239,11 +239,20 @@ def test_dequant_exact_for_power_of_two_scales():
     c = (2.0 ** rng.integers(-20, 5, 16)).astype(np.float32)
     want = Q.astype(np.float64) * r[:, None].astype(np.float64) * c[None, :].astype(np.float64)
     assert np.array_equal(O.dequantize(Q, r, c).astype(np.float64), want)
-    # general scales: within one rounding of each of the two products
+    # general scales: the FP64 reconstruction is the exact rational product for
+    # |Q| <= 31 (4- and 6-bit codes) and the fp32 export is its single rounding
     r = rng.random(16).astype(np.float32)
     c = rng.random(16).astype(np.float32)
-    want = Q.astype(np.float64) * r[:, None] * c[None, :]
-    np.testing.assert_allclose(O.dequantize(Q, r, c), want, rtol=2.5 * 2.0 ** -24, atol=0)
+    S64 = O.reconstruct_f64(Q, r, c)
+    for i in range(16):
+        for j in range(16):
+            exact = Fraction(int(Q[i, j])) * Fraction(float(r[i])) * Fraction(float(c[j]))
+            assert Fraction(float(S64[i, j])) == exact
+    assert np.array_equal(O.dequantize(Q, r, c), S64.astype(np.float32))
+    Q8 = rng.integers(-127, 128, (16, 16)).astype(np.int32)
+    exact = Q8.astype(np.float64) * r[:, None].astype(np.float64)
+    np.testing.assert_allclose(O.reconstruct_f64(Q8, r, c), exact * c[None, :], rtol=2.0 ** -53,
+                               atol=0)
 
 
 def test_magic_number_rounding_identity():
@@ -372,14 +381,14 @@ def test_error_propagation_identity(kda):
     bits = 6
     S0 = rng.standard_normal((dk, dv)).astype(np.float32)
     Q, r, c = O.quantize(bits, S0)
-    Sq = O.dequantize(Q, r, c).astype(np.float64)
+    Sq = O.reconstruct_f64(Q, r, c)
     St = Sq.copy()  # exact trajectory from the same start: E_0 = 0
     E = np.zeros((dk, dv))
     for q, k, v, beta, g in _seq(rng, 24, dk, dv, kda):
         alpha = _alpha(kda, dk, g)
         Fq, _ = O.gated_delta_f64(Sq, alpha, q, k, v, beta)        # F_t(S^q_{t-1})
         y = O.quant_step_codes(kda, bits, Q, r, c, q, k, v, beta, g)
-        Sq = O.dequantize(Q, r, c).astype(np.float64)
+        Sq = O.reconstruct_f64(Q, r, c)
         eps = Sq - Fq
         St, _ = O.gated_delta_f64(St, alpha, q, k, v, beta)
         k64 = k.astype(np.float64)
@@ -412,7 +421,7 @@ def test_quantized_recurrence_converges_to_fp64(kda):
         for q, k, v, beta, g in seq:
             O.quant_step_codes(kda, bits, Q, r, c, q, k, v, beta, g)
             St, _ = O.gated_delta_f64(St, _alpha(kda, dk, g), q, k, v, beta)
-            worst = max(worst, _rel(O.dequantize(Q, r, c).astype(np.float64), St))
+            worst = max(worst, _rel(O.reconstruct_f64(Q, r, c), St))
         errs[bits] = worst
     for b in (8, 12):
         assert 8 < errs[b] / errs[b + 4] < 32, errs
@@ -448,7 +457,7 @@ def test_beta0_gate1_keeps_codes(bits):
     assert np.array_equal(Q, Q0)
     np.testing.assert_allclose(r, r0, rtol=4 * 2.0 ** -23)
     np.testing.assert_allclose(c, c0, rtol=4 * 2.0 ** -23)
-    St = O.dequantize(Q0, r0, c0).astype(np.float64)
+    St = O.reconstruct_f64(Q0, r0, c0)
     np.testing.assert_allclose(y, St.T @ q.astype(np.float32).astype(np.float64), rtol=0,
                                atol=1e-12)
 
