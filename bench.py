@@ -1,0 +1,313 @@
+"""Benchmark of the fused quantized gated Delta-rule decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3a]
+
+A step is one sq_decode_step over the whole batch (dequantize, gate, look-up,
+delta write, read-out, requantize in place) for B = 512 requests x 48 heads,
+d = 128, 6-bit codes with fp32 row / column scales, bf16 inputs, requests
+reached through a seeded permutation of 640 pool slots.  Inputs and the pool
+are resident in HBM before timing starts.
+
+Prints ONE JSON line: state-updates/s (request x head x step), the roofline
+of the decode kernel (algorithmic bytes / average launch time against the
+8 TB/s HBM3E peak), the same step on an fp32 state pool, the mixed 4/8-bit
+variant, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gdn6_B512_H48_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "quantized_gated_delta_amd", "csrc", "sq_kernels.hip")
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algo_bytes_per_step(B, H, d, head_bits, gate, io_bytes=2):
+    """Algorithmic bytes one step must move: packed codes and fp32 scales read
+    and written, q, k, v, beta, g read, y written, one slot index per request."""
+    total = 0
+    for b in head_bits:
+        codes = d * d * int(b) // 8
+        scales = 8 * d
+        io = (3 * d + 1 + (d if gate == "kda" else 1) + d) * io_bytes
+        total += 2 * codes + 2 * scales + io
+    return B * total + 4 * B
+
+
+def f32_bytes_per_step(B, H, d, gate, io_bytes=2):
+    io = (3 * d + 1 + (d if gate == "kda" else 1) + d) * io_bytes
+    return B * H * (2 * 4 * d * d + io) + 4 * B
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c3a")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-variants", action="store_true", help="only the headline kernel")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration for profiles)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: every (request, head) update is independent "
+              "and the path has no collective; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_gated_delta_amd as Q
+    import workload as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calib:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        eprint("copied 3 x 1 GiB")
+        return
+
+    wl = W.make(args.workload)
+    layer = wl.layers[0]
+    B, H, d = wl.B, wl.H, wl.d
+    kda = layer.gate == "kda"
+    io_dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    def make_pool(lay):
+        pool = Q.StatePool(wl.n_slots, H, d, lay.head_bits.tolist(), lay.gate, device=dev)
+        slot = to_dev(lay.slot_of.astype(np.int32))
+        return pool, slot
+
+    # ---- initial state: 128 unquantized fp32 warm-up steps on the GPU, then quantize
+    eprint("warm-up: %d fp32 steps for %d x %d heads" % (W.WARMUP_STEPS, B, H))
+    t0 = time.time()
+    state = torch.zeros((wl.n_slots, H, d, d), dtype=torch.float32, device=dev)
+    slot_l = to_dev(layer.slot_of.astype(np.int32))
+    y = torch.empty((B, H, d), dtype=io_dt, device=dev)
+    for t in range(-W.WARMUP_STEPS, 0):
+        x = {k: to_dev(v) for k, v in wl.step_inputs(layer, t).items()}
+        Q.sq_f32_decode_step(state, wl.n_slots, H, d, d, int(kda), slot_l, B, x["q"], x["k"],
+                             x["v"], x["beta"], x["g"], y)
+    torch.cuda.synchronize()
+    eprint("warm-up done in %.1f s" % (time.time() - t0))
+    pool, slot = make_pool(layer)
+    pool.quant_state(slot, state[slot.long()])
+
+    # ---- resident inputs for the timed steps (4 distinct steps, cycled)
+    steps_in = [{k: to_dev(v) for k, v in wl.step_inputs(layer, t).items()} for t in range(4)]
+    y = torch.empty((B * H, d), dtype=io_dt, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run(pl, sl, n, per_launch=None):
+        for i in range(n):
+            x = steps_in[i % 4]
+            if per_launch is not None:
+                per_launch[i][0].record(stream)
+            pl.decode_step(sl, x["q"], x["k"], x["v"], x["beta"], x["g"], y)
+            if per_launch is not None:
+                per_launch[i][1].record(stream)
+
+    def timed(pl, sl, fn=None):
+        fn = fn or (lambda n, ev=None: run(pl, sl, n, ev))
+        fn(args.warmup)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        fn(args.steps)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        fn(args.steps, ev)
+        torch.cuda.synchronize()
+        launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        return wall / args.steps * 1e3, launch_ms
+
+    eprint("timing the quantized decode step (%s)" % args.workload)
+    ms_step, ms_launch = timed(pool, slot)
+    updates = B * H
+    bytes_step = algo_bytes_per_step(B, H, d, layer.head_bits, layer.gate,
+                                     2 if wl.dtype == "bf16" else 4)
+    achieved = bytes_step / (ms_launch * 1e-3) / 1e9
+    eprint("quantized: %.2f us/step wall, %.2f us/launch, %.1f GB/s (%.1f%% of 8 TB/s)"
+           % (ms_step * 1e3, ms_launch * 1e3, achieved, 100 * achieved / HBM_PEAK_GBS))
+
+    variants = {}
+    if not args.no_variants:
+        # fp32-state comparator on the same inputs
+        def run_f32(n, ev=None):
+            for i in range(n):
+                x = steps_in[i % 4]
+                if ev is not None:
+                    ev[i][0].record(stream)
+                Q.sq_f32_decode_step(state, wl.n_slots, H, d, d, int(kda), slot_l, B, x["q"],
+                                     x["k"], x["v"], x["beta"], x["g"], y)
+                if ev is not None:
+                    ev[i][1].record(stream)
+        f_ms, f_launch = timed(None, None, run_f32)
+        fb = f32_bytes_per_step(B, H, d, layer.gate, 2 if wl.dtype == "bf16" else 4)
+        variants["fp32_state"] = {
+            "updates_per_s": updates / (f_ms * 1e-3), "us_per_step": f_ms * 1e3,
+            "us_per_launch": f_launch * 1e3, "algo_bytes_per_step": fb,
+            "achieved_GBps": fb / (f_launch * 1e-3) / 1e9,
+            "speedup_quantized_vs_fp32": f_ms / ms_step}
+        eprint("fp32 state: %.2f us/step, %.1f GB/s" % (f_ms * 1e3, variants["fp32_state"]["achieved_GBps"]))
+        # the mixed 4/8-bit variant (8-bit for heads whose half-life exceeds 64 steps)
+        if args.workload == "c3a":
+            wb = W.make("c3b")
+            lb = wb.layers[0]
+            pool_b, slot_b = make_pool(lb)
+            stb = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
+            stb.copy_(state[slot_l.long()])
+            pool_b.quant_state(slot_b, stb)
+            del stb
+            b_ms, b_launch = timed(pool_b, slot_b)
+            bb = algo_bytes_per_step(B, H, d, lb.head_bits, lb.gate)
+            variants["mixed_4_8_halflife"] = {
+                "n_8bit_heads": int((lb.head_bits == 8).sum()), "seed": wb.seed,
+                "updates_per_s": updates / (b_ms * 1e-3), "us_per_step": b_ms * 1e3,
+                "us_per_launch": b_launch * 1e3, "algo_bytes_per_step": bb,
+                "achieved_GBps": bb / (b_launch * 1e-3) / 1e9,
+                "hbm_frac": bb / (b_launch * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            eprint("mixed 4/8: %.2f us/step, %.1f GB/s" % (b_ms * 1e3, variants["mixed_4_8_halflife"]["achieved_GBps"]))
+            pool_b.close()
+            # KDA (per-key-channel gate) at the same shape, bits 4/6/8 at 25/50/25 %
+            wk = W.custom("kda", B, H, d, W.mixed_bits(0, 0, H), dtype="bf16",
+                          n_slots=wl.n_slots, permute=True, seed=0, name="kda_mixed")
+            lk = wk.layers[0]
+            pool_k, slot_k = make_pool(lk)
+            stk = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
+            stk.copy_(state[slot_l.long()])
+            pool_k.quant_state(slot_k, stk)
+            del stk
+            kin = [{k: to_dev(v) for k, v in wk.step_inputs(lk, t).items()} for t in range(4)]
+
+            def run_k(n, ev=None):
+                for i in range(n):
+                    x = kin[i % 4]
+                    if ev is not None:
+                        ev[i][0].record(stream)
+                    pool_k.decode_step(slot_k, x["q"], x["k"], x["v"], x["beta"], x["g"], y)
+                    if ev is not None:
+                        ev[i][1].record(stream)
+            k_ms, k_launch = timed(None, None, run_k)
+            kb = algo_bytes_per_step(B, H, d, lk.head_bits, "kda")
+            variants["kda_mixed_4_6_8"] = {
+                "updates_per_s": updates / (k_ms * 1e-3), "us_per_step": k_ms * 1e3,
+                "us_per_launch": k_launch * 1e3, "algo_bytes_per_step": kb,
+                "achieved_GBps": kb / (k_launch * 1e-3) / 1e9,
+                "hbm_frac": kb / (k_launch * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            eprint("kda mixed: %.2f us/step, %.1f GB/s" % (k_ms * 1e3, variants["kda_mixed_4_6_8"]["achieved_GBps"]))
+            pool_k.close()
+    del state
+
+    # ---- CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, layer, args.cpu_seconds)
+        eprint("cpu oracle: %.3g updates/s on %d threads" % (cpu["value"], cpu["cores"]))
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_src_sha256_16") == kernel_hash() and tr.get("workload") == args.workload:
+            traffic = tr.get("bytes_per_launch")
+
+    out = {
+        "metric": "state-updates/s (req x head x step) and achieved HBM GB/s vs peak at B=512",
+        "value": updates / (ms_step * 1e-3),
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded generator; state from 128 fp32 warm-up steps)",
+        "config": {"workload": "gdn_decode_%s" % args.workload, "B": B, "H": H, "d_k": d,
+                   "d_v": d, "bits": sorted(set(int(b) for b in layer.head_bits)),
+                   "pool_slots": wl.n_slots, "io_dtype": wl.dtype, "scales": "fp32",
+                   "gate": layer.gate},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algo_bytes_per_launch": bytes_step, "us_per_launch": ms_launch * 1e3,
+                     "kernel": "decode_kernel<128, GDN, bf16, bf16>"},
+        "cpu_baseline": cpu,
+        "variants": variants,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, layer, seconds):
+    """The oracle, as it stands, on sampled (b, h) rows of the same workload,
+    all host threads; repeated until `seconds` of wall time have passed."""
+    import numpy as np
+
+    import oracle as O
+    import workload as W
+    d, H = wl.d, wl.H
+    nthr = O.n_threads()
+    rng = np.random.default_rng(0)
+    n_rows = 64 * nthr
+    flat = rng.choice(wl.B * H, size=n_rows, replace=False)
+    rows = np.stack([flat // H, flat % H], 1)
+    # initial records: a short FP64 warm-up of the sampled rows, then the pinned quantizer
+    S = np.zeros((n_rows, d, d))
+    for t in range(-8, 0):
+        x = {k: W.to_f32(v) for k, v in wl.step_inputs(layer, t, rows).items()}
+        O.f64_step(layer.gate == "kda", S, x["q"], x["k"], x["v"], x["beta"], x["g"])
+    bits = layer.head_bits[rows[:, 1]]
+    sizes = np.array([d * d * int(b) // 8 + 8 * d for b in bits], np.int64)
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.int64)
+    base = np.zeros(int(sizes.sum()), np.uint8)
+    O.records_quantize(base, offs, bits, S.astype(np.float32), d, d)
+    x = {k: W.to_f32(v) for k, v in wl.step_inputs(layer, 0, rows).items()}
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        O.records_step(layer.gate == "kda", base, offs, bits, d, d, x["q"], x["k"], x["v"],
+                       x["beta"], x["g"])
+        done += n_rows
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": done / el, "unit": "state-updates/s", "cores": nthr, "kind": "oracle",
+            "sample": "%d rows x %d passes of the B=%d H=%d d=%d step (%.1f s wall)"
+                      % (n_rows, done // n_rows, wl.B, H, d, el)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+/*
+ * sq.h -- C ABI of the packed low-bit recurrent-state pool and its fused
+ * gated Delta-rule decode step on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the pages on STEPQuant, arXiv 2609.38169):
+ *  - "Paper Explained: STEPQuant" (ta-paperlens), section "The mechanism:
+ *    rewriting state with the delta rule": per (request, head) a d_k x d_v
+ *    state S is faded by the retention gate, the key's current look-up is
+ *    formed, the beta-scaled difference to v is written along k, and the
+ *    head output is read through q.  GDN has one scalar gate per head, KDA
+ *    one gate per key channel.  Reading of the dropped equation:
+ *        S' = (I - beta k k^T) diag(a) S + beta k v^T,   y = S'^T q,
+ *        a = exp(g)   (g: log-gate, one per head or one per key channel).
+ *  - hyper.ai summary, "Method", first paragraph: the reconstructed state is
+ *    updated in floating point, the output is computed, and the updated
+ *    state is then quantized for storage (symmetric uniform quantization).
+ *  - hyper.ai summary, "Method", Key-Row-Aware Dual-Axis Fitting paragraph:
+ *    the state is stored as row factors x column factors x low-bit integers,
+ *    each scaled entry rounded to the nearest level.  Scale rule used here:
+ *    c_j = max_i |S'_ij|, r_i = max_j |S'_ij / c_j| / qmax, codes
+ *    round-half-even(S'_ij / (c_j r_i)), qmax = 2^(bits-1) - 1.
+ *  - hyper.ai summary, "Method", last paragraph: packed-state kernels sit in
+ *    a per-request recurrent-state pool; a fused kernel reconstructs tiles,
+ *    applies the delta update and reads out the output.  Here the
+ *    requantization and packed write-back are fused into the same kernel.
+ *  - blog.ontle.kr (efficiency paragraph): serving pre-allocates spare
+ *    slots, so requests reach their state through a slot index.
+ *
+ * Memory and ownership
+ *  - Every tensor argument is a DEVICE pointer to contiguous row-major
+ *    memory that the caller owns (e.g. a torch tensor); the library never
+ *    allocates or frees device memory.  Pointers must be 16-byte aligned and
+ *    the pool buffer 256-byte aligned.
+ *  - Host pointers: the descriptor, head_bits, and the layout outputs.
+ *  - An sq_pool is a small host-side handle describing how a caller-owned
+ *    device buffer is laid out; destroying it never touches the buffer.
+ *
+ * Pool layout (little-endian):
+ *   pool[slot] = record(h = 0) | record(h = 1) | ... | record(H - 1)
+ *   slot_stride = sum_h record_bytes(bits_h)
+ *   record      = codes[d_k][d_v * bits / 8] | r[d_k] fp32 | c[d_v] fp32
+ *   Each code row is a little-endian bit stream, code j at bits
+ *   [bits*j, bits*j + bits), b-bit two's complement in [-qmax, qmax]:
+ *   8-bit one code per byte; 4-bit code 2n in the low nibble of byte n;
+ *   6-bit four codes per three bytes.  Record sizes at d = 128:
+ *   9216 / 13312 / 17408 bytes for 4 / 6 / 8 bits (d = 64: 2560/3584/4608),
+ *   all multiples of 256 bytes.
+ *
+ * Execution
+ *  - Compute entry points only validate their arguments on the host and
+ *    enqueue work on the given stream; they return before the work runs.
+ *    Device faults surface at the caller's next synchronisation.
+ *  - Argument errors return a non-zero status synchronously and enqueue
+ *    nothing; sq_last_error() then describes the problem (thread-local).
+ *  - The decode step updates the listed slots in place.  The entries of
+ *    slot_idx must be distinct and in [0, n_slots); slots not listed are
+ *    never read or written.  Overlapping calls on the same slots race.
+ *  - n = 0 is a valid no-op.
+ *  - Supported shapes: d_k = d_v = d in {64, 128}; bits in {4, 6, 8};
+ *    1 <= n_heads <= 64.  Others return SQ_EUNSUPPORTED.
+ *  - NaN or infinite inputs give undefined (but memory-safe) results.
+ */
+#ifndef SQ_H
+#define SQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SQ_OK = 0,
+    SQ_EINVAL = 1,        /* bad argument (null, misaligned, out of range) */
+    SQ_EUNSUPPORTED = 2,  /* shape or bit width this build does not handle */
+    SQ_ENOMEM = 3,        /* buffer too small / host allocation failed */
+    SQ_EHIP = 4           /* a HIP runtime call failed (text in sq_last_error) */
+} sq_status;
+
+typedef enum { SQ_GATE_GDN = 0, SQ_GATE_KDA = 1 } sq_gate;
+
+typedef enum { SQ_F32 = 0, SQ_BF16 = 1 } sq_dtype;
+
+typedef struct {
+    int32_t n_slots;          /* pool capacity in requests (>= 1) */
+    int32_t n_heads;          /* heads per request, 1..64 */
+    int32_t d_k;              /* key dimension (rows of the state) */
+    int32_t d_v;              /* value dimension (columns), must equal d_k */
+    const uint8_t *head_bits; /* host array [n_heads], each 4, 6 or 8; copied */
+    sq_gate gate;             /* GDN: g is [n, H]; KDA: g is [n, H, d_k] */
+} sq_pool_desc;
+
+typedef struct sq_pool sq_pool;
+
+/* Bytes of device memory a pool with this descriptor needs
+ * (n_slots * slot_stride).  Defines the layout above. */
+sq_status sq_pool_bytes(const sq_pool_desc *desc, size_t *bytes);
+
+/* Wrap the caller's device buffer dev_buf (>= sq_pool_bytes, 256-byte
+ * aligned) as a pool.  Host-side only: the buffer's contents are not
+ * touched (initialise slots with sq_quant_state).  *out receives a handle
+ * to release with sq_pool_destroy. */
+sq_status sq_pool_create(const sq_pool_desc *desc, void *dev_buf, size_t bytes, sq_pool **out);
+
+/* Release the host handle.  Never frees or touches dev_buf.  NULL is a no-op. */
+sq_status sq_pool_destroy(sq_pool *pool);
+
+/* Layout of a pool: slot stride in bytes, and per head its record's byte
+ * offset within a slot and its record size.  Output arrays are host arrays
+ * of n_heads entries; any output pointer may be NULL. */
+sq_status sq_pool_layout(const sq_pool *pool, int64_t *slot_stride, int64_t *head_off,
+                         int64_t *record_bytes);
+
+/* Quantize fp32 states S [n, H, d_k, d_v] (device) into the slots
+ * slot_idx[0..n) (device int32) with each head's bit width, using the scale
+ * rule above in fp32 (reciprocal-multiply; one rounding per operation).
+ * Bit-exact with the documented arithmetic. */
+sq_status sq_quant_state(sq_pool *pool, const int32_t *slot_idx, int32_t n, const float *S,
+                         hipStream_t stream);
+
+/* Reconstruct fp32 states S [n, H, d_k, d_v] = (code * r_i) * c_j (two
+ * rounded fp32 products) from the slots slot_idx[0..n). */
+sq_status sq_dequant_state(const sq_pool *pool, const int32_t *slot_idx, int32_t n, float *S,
+                           hipStream_t stream);
+
+/* One fused decode step for n requests (request b lives in slot slot_idx[b]):
+ * for every (b, h): dequantize, decay by a = exp(g), look up v_old = Sd^T k,
+ * u = beta (v - v_old), S' = Sd + k u^T, y = S'^T q (from the unrequantized
+ * S'), then requantize S' to the head's bit width and store it in place.
+ *   q, k: [n, H, d_k]   v: [n, H, d_v]   beta: [n, H]
+ *   g (log-gate): [n, H] for GDN, [n, H, d_k] for KDA
+ *   y: [n, H, d_v] output
+ * in_dtype gives the type of q, k, v, beta, g; y_dtype the type of y. */
+sq_status sq_decode_step(sq_pool *pool, const int32_t *slot_idx, int32_t n, const void *q,
+                         const void *k, const void *v, const void *beta, const void *g,
+                         sq_dtype in_dtype, void *y, sq_dtype y_dtype, hipStream_t stream);
+
+/* The same step on an fp32 state pool state_pool [n_slots, H, d_k, d_v]
+ * (the unquantized serving default), in place on the listed slots.
+ * Same argument conventions as sq_decode_step. */
+sq_status sq_f32_decode_step(float *state_pool, int32_t n_slots, int32_t n_heads, int32_t d_k,
+                             int32_t d_v, sq_gate gate, const int32_t *slot_idx, int32_t n,
+                             const void *q, const void *k, const void *v, const void *beta,
+                             const void *g, sq_dtype in_dtype, void *y, sq_dtype y_dtype,
+                             hipStream_t stream);
+
+/* Debug check: copy slot_idx[0..n) (device) to the host, synchronising the
+ * stream, and verify every entry is in [0, n_slots) and distinct.  Returns
+ * SQ_EINVAL with the first offending index in sq_last_error() otherwise. */
+sq_status sq_check_slots(const sq_pool *pool, const int32_t *slot_idx, int32_t n,
+                         hipStream_t stream);
+
+/* Text describing the last non-OK status returned on this thread. */
+const char *sq_last_error(void);
+
+/* Library version string. */
+const char *sq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQ_H */

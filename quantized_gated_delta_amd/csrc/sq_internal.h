@@ -1,0 +1,49 @@
+// Internal interface between the C-ABI layer (sq_api.cpp) and the HIP
+// kernels (sq_kernels.hip).  Not installed; the public boundary is sq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sqk {
+
+constexpr int kMaxHeads = 64;
+
+// Per-head record placement inside one slot of the pool.
+struct HeadTable {
+    int64_t off[kMaxHeads];  // byte offset of head h's record within a slot
+    uint8_t bits[kMaxHeads]; // 4, 6 or 8
+};
+
+struct PoolView {
+    uint8_t *base;       // device pointer to slot 0
+    int64_t slot_stride; // bytes per slot
+    int32_t n_heads;
+    int32_t d;           // d_k == d_v
+};
+
+// Step inputs; dtype flags: 0 = fp32, 1 = bf16.
+struct StepIO {
+    const int32_t *slot;
+    const void *q, *k, *v, *beta, *g;
+    void *y;
+    int32_t n;
+    int32_t in_bf16, y_bf16;
+    int32_t kda;
+};
+
+// Bytes of one record: d rows of d * bits / 8 code bytes, then r[d], c[d] fp32.
+inline int64_t record_bytes(int bits, int d) {
+    return (int64_t)d * d * bits / 8 + 8 * (int64_t)d;
+}
+
+hipError_t launch_quant_state(const PoolView &pool, const HeadTable &tab, const int32_t *slot,
+                              int32_t n, const float *S, hipStream_t stream);
+hipError_t launch_dequant_state(const PoolView &pool, const HeadTable &tab, const int32_t *slot,
+                                int32_t n, float *S, hipStream_t stream);
+hipError_t launch_decode(const PoolView &pool, const HeadTable &tab, const StepIO &io,
+                         hipStream_t stream);
+hipError_t launch_f32_decode(float *state, int64_t slot_stride_floats, int32_t n_heads, int32_t d,
+                             const StepIO &io, hipStream_t stream);
+
+} // namespace sqk

@@ -1,0 +1,404 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Criteria (stated in the tests below):
+  quant_state / dequant_state    bit-exact
+  one decode step                codes |dQ| <= 1 and dQ != 0 on <= 1e-4 of them,
+                                 scales within 1e-5 relative, y rel-L2 <= 1e-3
+  trajectories                   dequantized state rel-L2 <= 1e-3 at the end,
+                                 y rel-L2 <= 1e-3 at every step
+  spare slots                    bit-identical before and after
+Inputs come from the seeded generator; initial states from the oracle's
+FP64 warm-up.  Where a full-size pool is too large for the oracle, the GPU
+runs the full batch and the oracle checks a seeded sample of (b, h) rows
+whose records and inputs are identical on both sides.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O
+import workload as W
+import harness as Hn
+import quantized_gated_delta_amd as Q
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ----------------------------------------------------------------- plumbing
+def to_dev(a: np.ndarray):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def from_dev(t) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def dev_inputs(x: dict) -> dict:
+    return {k: to_dev(v) for k, v in x.items()}
+
+
+class Side:
+    """One layer on both sides: GPU pool and the oracle's host image."""
+
+    def __init__(self, wl: W.Workload, layer: W.Layer):
+        self.wl, self.layer = wl, layer
+        self.kda = layer.gate == "kda"
+        self.gpu = Q.StatePool(wl.n_slots, wl.H, wl.d, layer.head_bits.tolist(), layer.gate)
+        self.host = Hn.HostPool(wl.n_slots, layer.head_bits, wl.d)
+        assert self.gpu.slot_stride == self.host.stride
+        assert np.array_equal(np.array(self.gpu.head_off), self.host.head_off)
+        self.slot_dev = to_dev(layer.slot_of.astype(np.int32))
+
+    def rows_offsets(self, rows):
+        rows = np.asarray(rows).reshape(-1, 2)
+        return self.host.offsets(self.layer.slot_of[rows[:, 0]], rows[:, 1]), \
+            self.layer.head_bits[rows[:, 1]]
+
+    def init_oracle_rows(self, rows, S=None):
+        """Warm-up (or given) fp32 states for rows -> oracle records -> GPU bytes."""
+        if S is None:
+            S = Hn.oracle_warmup(self.wl, self.layer, rows)
+        offs, bits = self.rows_offsets(rows)
+        O.records_quantize(self.host.bytes, offs, bits, S, self.wl.d, self.wl.d)
+        self.push_rows(rows)
+
+    def push_rows(self, rows):
+        offs, bits = self.rows_offsets(rows)
+        buf = self.gpu.buf
+        for o, b in zip(offs, bits):
+            n = Hn.record_bytes(int(b), self.wl.d)
+            buf[int(o):int(o) + n].copy_(torch.from_numpy(self.host.bytes[o:o + n]))
+
+    def gpu_warmup_all(self):
+        """GPU-side initial pool for rows the oracle does not check: fp32 warm-up
+        with the fp32-state kernel, then sq_quant_state."""
+        wl, layer = self.wl, self.layer
+        B, H, d = wl.B, wl.H, wl.d
+        state = torch.zeros((B, H, d, d), dtype=torch.float32, device=DEV)
+        ident = torch.arange(B, dtype=torch.int32, device=DEV)
+        y = torch.empty((B, H, d), dtype=torch.float32, device=DEV)
+        for t in range(-W.WARMUP_STEPS, 0):
+            x = dev_inputs(wl.step_inputs(layer, t))
+            Q.sq_f32_decode_step(state, B, H, d, d, int(self.kda), ident, B, x["q"], x["k"],
+                                 x["v"], x["beta"], x["g"], y)
+        self.gpu.quant_state(self.slot_dev, state)
+        torch.cuda.synchronize()
+        del state
+
+    def step(self, t, rows_checked):
+        """One step: GPU on the full batch, oracle on rows_checked.
+        Returns (y_gpu [B*H, d] float64 rows for rows_checked, y_oracle)."""
+        wl, layer = self.wl, self.layer
+        x = wl.step_inputs(layer, t)
+        xd = dev_inputs(x)
+        ydt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+        y = torch.empty((wl.B * wl.H, wl.d), dtype=ydt, device=DEV)
+        self.gpu.decode_step(self.slot_dev, xd["q"], xd["k"], xd["v"], xd["beta"], xd["g"], y)
+        rows = np.asarray(rows_checked).reshape(-1, 2)
+        idx = rows[:, 0] * wl.H + rows[:, 1]
+        xs = {k: W.to_f32(v[idx]) for k, v in x.items()}
+        offs, bits = self.rows_offsets(rows)
+        y_ref = O.records_step(self.kda, self.host.bytes, offs, bits, wl.d, wl.d, xs["q"],
+                               xs["k"], xs["v"], xs["beta"], xs["g"])
+        y_gpu = W.to_f32(from_dev(y)).astype(np.float64)[idx]
+        if wl.dtype == "bf16":
+            y_ref = Hn.to_bf16_f32(y_ref)
+        return y_gpu, y_ref
+
+    def gpu_pool(self) -> np.ndarray:
+        torch.cuda.synchronize()
+        return self.gpu.buf.cpu().numpy()
+
+
+def check_records(side: Side, rows, pool_gpu: np.ndarray, label=""):
+    """Codes / scales of the given rows, GPU pool vs oracle image."""
+    d = side.wl.d
+    flips = 0
+    total = 0
+    worst = 0
+    for (b, h) in np.asarray(rows).reshape(-1, 2):
+        bits = int(side.layer.head_bits[h])
+        o = int(side.host.offsets([side.layer.slot_of[b]], [h])[0])
+        n = Hn.record_bytes(bits, d)
+        rg, rr = pool_gpu[o:o + n], side.host.bytes[o:o + n]
+        qg, qr = Hn.unpack_codes(bits, d, rg), Hn.unpack_codes(bits, d, rr)
+        mx, _ = Hn.compare_codes(qg, qr)
+        worst = max(worst, mx)
+        flips += int((qg != qr).sum())
+        total += qg.size
+        sg, sr = Hn.record_scales(bits, d, rg), Hn.record_scales(bits, d, rr)
+        for a, bb in zip(sg, sr):
+            np.testing.assert_allclose(a, bb, rtol=Hn.SCALE_RTOL, atol=0,
+                                       err_msg="%s scales row %d head %d" % (label, b, h))
+    frac = flips / max(1, total)
+    assert worst <= 1, "%s: a code differs by %d" % (label, worst)
+    assert frac <= Hn.CODE_FLIP_FRACTION, "%s: %.3g of codes differ" % (label, frac)
+    return frac
+
+
+def sample_rows(B, H, n, seed=0):
+    rng = np.random.default_rng(1234 + seed)
+    flat = rng.choice(B * H, size=min(n, B * H), replace=False)
+    return np.stack([flat // H, flat % H], axis=1)
+
+
+# ----------------------------------------------------------------- G1
+@pytest.mark.parametrize("d", [64, 128])
+def test_quant_dequant_bit_exact(d):
+    log("G1 quant/dequant d=%d" % d)
+    rng = np.random.default_rng(d)
+    H = 6
+    bits = [4, 6, 8, 8, 6, 4]
+    n_slots, B = 7, 5
+    wl = W.custom("gdn", B, H, d, bits, n_slots=n_slots, permute=True, seed=3)
+    side = Side(wl, wl.layers[0])
+    S = (rng.standard_normal((B, H, d, d)) * np.exp(rng.standard_normal((B, H, d, 1)))
+         * np.exp(rng.standard_normal((B, H, 1, d)))).astype(np.float32)
+    S[0, 0] = 0.0                                 # all-zero state
+    S[1, 1, 5, :] = 0.0                           # zero row
+    S[1, 1, :, 7] = 0.0                           # zero column
+    S[2, 2, 3, 3] = 1e-39                         # subnormal entry
+    S[2, 3] *= np.float32(1e-36)                  # tiny state
+    S[3, 4] *= np.float32(1e30)                   # huge state
+    S[4, 5, :, 9] = 1e-40                         # column of subnormals only
+    S[4, 5, 11, :] *= np.float32(1e-30)           # row far below its columns
+    Sd = to_dev(S)
+    side.gpu.quant_state(side.slot_dev, Sd)
+    rows = Hn.rows_all(B, H)
+    offs, hb = side.rows_offsets(rows)
+    O.records_quantize(side.host.bytes, offs, hb, S.reshape(-1, d, d), d, d)
+    got = side.gpu_pool()
+    for (b, h), o, bb in zip(rows, offs, hb):
+        n = Hn.record_bytes(int(bb), d)
+        assert np.array_equal(got[o:o + n], side.host.bytes[o:o + n]), (b, h)
+    # spare slots never written: the pool buffer is uninitialised there, so
+    # compare dequant only through the listed slots
+    out = side.gpu.dequant_state(side.slot_dev)
+    want = O.records_dequantize(side.host.bytes, offs, hb, d, d)
+    assert np.array_equal(from_dev(out).reshape(-1, d, d), want)
+
+
+# ----------------------------------------------------------------- G2 small shapes
+@pytest.mark.parametrize("case", [
+    ("gdn", 5, 3, 64, [4, 6, 8], "f32", 9),
+    ("kda", 3, 5, 128, [6, 4, 8, 6, 6], "bf16", 4),
+    ("gdn", 4, 4, 128, [8, 6, 4, 6], "bf16", 11),
+    ("kda", 2, 3, 64, [4, 8, 6], "f32", 2),
+])
+def test_decode_step_small_full_compare(case):
+    gate, B, H, d, bits, dtype, n_slots = case
+    log("G2 small %s" % (case,))
+    wl = W.custom(gate, B, H, d, bits, dtype=dtype, n_slots=n_slots, permute=True, seed=5)
+    side = Side(wl, wl.layers[0])
+    # spare slots hold a canary pattern that must survive
+    side.gpu.buf.fill_(0xA5)
+    side.host.bytes[:] = 0xA5
+    rows = Hn.rows_all(B, H)
+    side.init_oracle_rows(rows)
+    for t in range(3):
+        # single-step criteria hold from identical records: start every step
+        # from the oracle's bytes (a legal +-1 flip would otherwise compound)
+        side.push_rows(rows)
+        y_gpu, y_ref = side.step(t, rows)
+        pool = side.gpu_pool()
+        check_records(side, rows, pool, "step %d" % t)
+        assert Hn.rel_l2(y_gpu, y_ref) <= Hn.Y_REL_L2, t
+        # canaries: every byte outside the listed slots is untouched
+        used = np.zeros(pool.size, bool)
+        for s in side.layer.slot_of:
+            used[s * side.host.stride:(s + 1) * side.host.stride] = True
+        assert (pool[~used] == 0xA5).all()
+
+
+def test_decode_zero_state_and_identity():
+    """From an all-zero pool (scales 0), and the beta = 0 / gate = 1 identity."""
+    log("G5 identity")
+    d, H, B = 128, 3, 4
+    wl = W.custom("gdn", B, H, d, [4, 6, 8], dtype="f32", seed=9)
+    side = Side(wl, wl.layers[0])
+    rows = Hn.rows_all(B, H)
+    side.init_oracle_rows(rows, S=np.zeros((B * H, d, d), np.float32))
+    y_gpu, y_ref = side.step(0, rows)
+    check_records(side, rows, side.gpu_pool(), "from zero")
+    assert Hn.rel_l2(y_gpu, y_ref) <= Hn.Y_REL_L2
+    # identity: beta = 0 and log-gate = 0 keep every code
+    before = side.gpu_pool().copy()
+    x = wl.step_inputs(wl.layers[0], 1)
+    x["beta"][:] = 0
+    x["g"][:] = 0
+    xd = dev_inputs(x)
+    y = torch.empty((B * H, d), dtype=torch.float32, device=DEV)
+    side.gpu.decode_step(side.slot_dev, xd["q"], xd["k"], xd["v"], xd["beta"], xd["g"], y)
+    after = side.gpu_pool()
+    for (b, h) in rows:
+        bits = wl.layers[0].head_bits[h]
+        o = int(side.host.offsets([b], [h])[0])
+        n = Hn.record_bytes(int(bits), d)
+        assert np.array_equal(Hn.unpack_codes(int(bits), d, after[o:o + n]),
+                              Hn.unpack_codes(int(bits), d, before[o:o + n]))
+        for a, bb in zip(Hn.record_scales(int(bits), d, after[o:o + n]),
+                         Hn.record_scales(int(bits), d, before[o:o + n])):
+            np.testing.assert_allclose(a, bb, rtol=4 * 2.0 ** -23, atol=0)
+
+
+def test_kda_equal_gates_matches_gdn():
+    log("KDA == GDN")
+    d, H, B = 128, 4, 3
+    wg = W.custom("gdn", B, H, d, [4, 6, 8, 6], dtype="bf16", seed=12)
+    wk = W.custom("kda", B, H, d, [4, 6, 8, 6], dtype="bf16", seed=12)
+    sg, sk = Side(wg, wg.layers[0]), Side(wk, wk.layers[0])
+    rows = Hn.rows_all(B, H)
+    S = Hn.oracle_warmup(wg, wg.layers[0], rows)
+    sg.init_oracle_rows(rows, S)
+    sk.init_oracle_rows(rows, S)
+    x = wg.step_inputs(wg.layers[0], 0)
+    xk = dict(x)
+    xk["g"] = np.repeat(x["g"][:, None], d, axis=1)
+    outs = []
+    for side, xx in ((sg, x), (sk, xk)):
+        xd = dev_inputs(xx)
+        y = torch.empty((B * H, d), dtype=torch.bfloat16, device=DEV)
+        side.gpu.decode_step(side.slot_dev, xd["q"], xd["k"], xd["v"], xd["beta"], xd["g"], y)
+        outs.append((side.gpu_pool(), from_dev(y)))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+# ----------------------------------------------------------------- workloads
+def test_c0_trajectory_64_steps():
+    log("c0 trajectory")
+    wl = W.make("c0")
+    side = Side(wl, wl.layers[0])
+    rows = Hn.rows_all(wl.B, wl.H)
+    side.init_oracle_rows(rows)
+    for t in range(wl.steps):
+        y_gpu, y_ref = side.step(t, rows)
+        assert Hn.rel_l2(y_gpu, y_ref) <= Hn.Y_REL_L2, t
+    pool = side.gpu_pool()
+    offs, hb = side.rows_offsets(rows)
+    s_gpu = O.records_dequantize(pool, offs, hb, wl.d, wl.d)
+    s_ref = O.records_dequantize(side.host.bytes, offs, hb, wl.d, wl.d)
+    assert Hn.rel_l2(s_gpu, s_ref) <= Hn.STATE_REL_L2
+
+
+def test_c1_single_step_full():
+    log("c1 full step")
+    wl = W.make("c1")
+    side = Side(wl, wl.layers[0])
+    rows = Hn.rows_all(wl.B, wl.H)
+    side.init_oracle_rows(rows)
+    y_gpu, y_ref = side.step(0, rows)
+    frac = check_records(side, rows, side.gpu_pool(), "c1")
+    log("c1 code flip fraction %.3g" % frac)
+    assert Hn.rel_l2(y_gpu, y_ref) <= Hn.Y_REL_L2
+
+
+@pytest.mark.parametrize("name,n_rows", [("c1", 48), ("c2", 48)])
+def test_trajectory_256_steps(name, n_rows):
+    log("%s trajectory" % name)
+    wl = W.make(name)
+    side = Side(wl, wl.layers[0])
+    side.gpu_warmup_all()
+    rows = sample_rows(wl.B, wl.H, n_rows, seed=1)
+    side.init_oracle_rows(rows)
+    worst_y = 0.0
+    for t in range(256):
+        y_gpu, y_ref = side.step(t, rows)
+        worst_y = max(worst_y, Hn.rel_l2(y_gpu, y_ref))
+    offs, hb = side.rows_offsets(rows)
+    pool = side.gpu_pool()
+    s_gpu = O.records_dequantize(pool, offs, hb, wl.d, wl.d)
+    s_ref = O.records_dequantize(side.host.bytes, offs, hb, wl.d, wl.d)
+    err = Hn.rel_l2(s_gpu, s_ref)
+    log("%s: worst y rel-L2 %.3g, final state rel-L2 %.3g" % (name, worst_y, err))
+    assert worst_y <= Hn.Y_REL_L2
+    assert err <= Hn.STATE_REL_L2
+
+
+@pytest.mark.parametrize("name", ["c3a", "c3b"])
+def test_c3_full_size_sampled(name):
+    """Full B = 512, H = 48 batch through 640 slots (the benchmark's launch);
+    sampled rows against the oracle; spare slots bit-identical."""
+    log("%s full size" % name)
+    wl = W.make(name)
+    side = Side(wl, wl.layers[0])
+    side.gpu_warmup_all()
+    rows = sample_rows(wl.B, wl.H, 64, seed=3)
+    if name == "c3b":  # make sure every 8-bit head is sampled
+        h8 = np.nonzero(wl.layers[0].head_bits == 8)[0]
+        rows = np.concatenate([rows, np.stack([np.arange(len(h8)), h8], 1)])
+    side.init_oracle_rows(rows)
+    before = side.gpu_pool()
+    spare = np.setdiff1d(np.arange(wl.n_slots), wl.layers[0].slot_of)
+    for t in range(2):
+        side.push_rows(rows)
+        y_gpu, y_ref = side.step(t, rows)
+        assert Hn.rel_l2(y_gpu, y_ref) <= Hn.Y_REL_L2
+        after = side.gpu_pool()
+        check_records(side, rows, after, "%s step %d" % (name, t))
+    st = side.host.stride
+    for s in spare:
+        assert np.array_equal(after[s * st:(s + 1) * st], before[s * st:(s + 1) * st]), s
+
+
+def test_f32_state_kernel_parity():
+    log("f32 kernel")
+    for gate, d, dtype in (("gdn", 128, "bf16"), ("kda", 64, "f32"), ("kda", 128, "bf16")):
+        wl = W.custom(gate, 6, 4, d, [6], dtype=dtype, n_slots=9, permute=True, seed=21)
+        layer = wl.layers[0]
+        rows = Hn.rows_all(wl.B, wl.H)
+        S0 = Hn.oracle_warmup(wl, layer, rows, steps=16)
+        state = torch.zeros((wl.n_slots, wl.H, d, d), dtype=torch.float32, device=DEV)
+        state[torch.from_numpy(layer.slot_of.astype(np.int64)).to(DEV)] = \
+            to_dev(S0.reshape(wl.B, wl.H, d, d))
+        slot = to_dev(layer.slot_of.astype(np.int32))
+        S_ref = S0.copy()
+        for t in range(4):
+            x = wl.step_inputs(layer, t)
+            xd = dev_inputs(x)
+            y = torch.empty((wl.B, wl.H, d), dtype=xd["q"].dtype, device=DEV)
+            Q.sq_f32_decode_step(state, wl.n_slots, wl.H, d, d, int(gate == "kda"), slot, wl.B,
+                                 xd["q"], xd["k"], xd["v"], xd["beta"], xd["g"], y)
+            xf = Hn.inputs_f32(x)
+            y_ref = O.f32_step(gate == "kda", S_ref, xf["q"], xf["k"], xf["v"], xf["beta"],
+                               xf["g"])
+            if dtype == "bf16":
+                y_ref = Hn.to_bf16_f32(y_ref)
+            tol = 1e-5 if dtype == "f32" else 1e-3
+            assert Hn.rel_l2(W.to_f32(from_dev(y)).reshape(-1, d), y_ref) <= tol
+        got = state.cpu().numpy()[layer.slot_of]
+        assert Hn.rel_l2(got.reshape(-1, d, d), S_ref) <= 1e-5
+
+
+# ----------------------------------------------------------------- boundary
+def test_n0_noop_and_slot_check():
+    log("boundary")
+    wl = W.custom("gdn", 4, 2, 64, [6], n_slots=4)
+    side = Side(wl, wl.layers[0])
+    side.gpu.buf.fill_(7)
+    empty = torch.empty(0, dtype=torch.int32, device=DEV)
+    z = torch.empty(16, dtype=torch.bfloat16, device=DEV)
+    Q.sq_decode_step(side.gpu.handle, empty, 0, z, z, z, z, z, z)
+    torch.cuda.synchronize()
+    assert (side.gpu.buf == 7).all()
+    side.gpu.check_slots(side.slot_dev)
+    bad = to_dev(np.array([0, 1, 1, 2], np.int32))
+    with pytest.raises(Q.SQError) as e:
+        side.gpu.check_slots(bad)
+    assert e.value.status == Q.SQ_EINVAL and "repeated" in e.value.text
+    bad = to_dev(np.array([0, 1, 4, 2], np.int32))
+    with pytest.raises(Q.SQError) as e:
+        side.gpu.check_slots(bad)
+    assert "outside" in e.value.text
