@@ -144,8 +144,11 @@ def main():
         torch.cuda.synchronize()
         t_start = time.perf_counter()
         fn(args.steps)
+        t_host = time.perf_counter() - t_start
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
+        eprint("  host enqueue %.1f us/step, wall %.1f us/step" % (t_host / args.steps * 1e6,
+                                                                  wall / args.steps * 1e6))
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
         fn(args.steps, ev)

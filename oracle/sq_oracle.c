@@ -101,10 +101,14 @@ void sqo_unpack_row(int bits, int n, const uint8_t *in, int32_t *codes) {
  * closed scale rule).  All in fp32, one rounding per operation:
  *   c_j  = max_i |S_ij|
  *   ic_j = c_j >= FLT_MIN ? 1/c_j : 0        (else c_j stored as 0)
- *   m_i  = max_j (|S_ij| * ic_j)
+ *   s_ij = S_ij * ic_j                       (rounded to fp32)
+ *   m_i  = max_j |s_ij|
  *   r_i  = m_i / qmax
  *   ir_i = r_i >= FLT_MIN ? 1/r_i : 0        (else r_i stored as 0)
- *   Q_ij = clamp(round_half_even((S_ij * ic_j) * ir_i), -qmax, qmax)
+ *   Q_ij = clamp(round_half_even(s_ij * ir_i), -qmax, qmax)
+ * The last product is taken exactly (in FP64, where the product of two fp32
+ * values is exact), so each code is the level nearest to the scaled entry
+ * s_ij / r_i.
  */
 void sqo_quantize(int bits, int dk, int dv, const float *S, int32_t *Q, float *r, float *c) {
     const float qmax = (float)sqo_qmax(bits);
@@ -140,8 +144,8 @@ void sqo_quantize(int bits, int dk, int dv, const float *S, int32_t *Q, float *r
         r[i] = ri;
         for (int j = 0; j < dv; ++j) {
             const float s = S[(size_t)i * dv + j] * ic[j];
-            const float x = s * iri;
-            float qv = nearbyintf(x); /* default rounding mode: half to even */
+            const double x = (double)s * (double)iri; /* exact */
+            double qv = nearbyint(x); /* default rounding mode: half to even */
             if (qv > qmax) qv = qmax;
             if (qv < -qmax) qv = -qmax;
             Q[(size_t)i * dv + j] = (int32_t)qv;

@@ -70,12 +70,19 @@ constexpr int kQuadXor1 = 0xB1;    // quad_perm [1, 0, 3, 2]
 constexpr int kQuadXor2 = 0x4E;    // quad_perm [2, 3, 0, 1]
 constexpr int kHalfMirror = 0x141; // row_half_mirror: lane i <-> 7 - i within 8
 
-// Max over the CG adjacent lanes of a band (CG = 4 or 8).
-template <int CG> __device__ __forceinline__ float band_max(float v) {
-    v = fmaxf(v, dpp<kQuadXor1>(v));
-    v = fmaxf(v, dpp<kQuadXor2>(v));
-    if constexpr (CG == 8) v = fmaxf(v, dpp<kHalfMirror>(v));
-    return v;
+// Max of non-negative floats over the CG adjacent lanes of a band (CG = 4
+// or 8).  For non-negative IEEE values the order of the bit patterns as
+// unsigned integers is the numeric order, so an integer max (which folds the
+// DPP exchange into one instruction) gives the float max exactly.
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CG> __device__ __forceinline__ float band_max(float vf) {
+    uint32_t v = __float_as_uint(vf);
+    v = max(v, dpp_u<kQuadXor1>(v));
+    v = max(v, dpp_u<kQuadXor2>(v));
+    if constexpr (CG == 8) v = max(v, dpp_u<kHalfMirror>(v));
+    return __uint_as_float(v);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -127,47 +134,102 @@ template <int BITS> __device__ __forceinline__ int code_at(const Seg<BITS> &s, i
     return (int32_t)(f << (32 - BITS)) >> (32 - BITS);
 }
 
-template <int BITS> __device__ __forceinline__ Seg<BITS> pack_seg(const int *code) {
-    Seg<BITS> s;
-#pragma unroll
-    for (int i = 0; i < Seg<BITS>::NWORDS; ++i) s.w[i] = 0;
-#pragma unroll
-    for (int n = 0; n < 16; ++n) {
-        const int bit = BITS * n, wd = bit >> 5, off = bit & 31;
-        const uint32_t f = (uint32_t)code[n] & ((1u << BITS) - 1u);
-        s.w[wd] |= f << off;
-        if (off + BITS > 32) s.w[wd + 1] |= f >> (32 - off);
-    }
-    return s;
+// Code of a scaled entry: round half to even of the exact product s * ir,
+// by one fused multiply-add with the magic number 1.5 * 2^23: for
+// |s * ir| < 2^22, fl(s * ir + 1.5 * 2^23) = 1.5 * 2^23 + rint(s * ir)
+// (a single rounding at unit spacing), whose low bits are the code in two's
+// complement.  Returns that bit pattern (code in the low BITS bits).
+__device__ __forceinline__ uint32_t code_bits(float s, float ir) {
+    return __float_as_uint(__builtin_fmaf(s, ir, 12582912.0f));
 }
 
-template <int BITS> __device__ __forceinline__ int to_code(float x) {
-    constexpr float QMAX = (float)((1 << (BITS - 1)) - 1);
-    const float rq = fminf(fmaxf(__builtin_rintf(x), -QMAX), QMAX);
-    return (int)rq;
+// Pack 16 codes (low BITS bits of f[n], garbage above) into a row segment
+// with funnel shifts: alignbit(f, acc, s) = (acc >> s) | (f << (32 - s))
+// appends the s low bits of f at the top of acc; everything above them in f
+// falls out of the word.  A code split across two words is appended with the
+// bits that fit, then appended whole to the next word, whose accumulated
+// shift (32 + bits already written) drops the part written before.
+template <int BITS> __device__ __forceinline__ Seg<BITS> pack_stream(const uint32_t (&f)[16]) {
+    Seg<BITS> s;
+    uint32_t acc = 0;
+    int fill = 0, word = 0;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+        if (fill + BITS <= 32) {
+            acc = __builtin_amdgcn_alignbit(f[n], acc, BITS);
+            fill += BITS;
+            if (fill == 32) {
+                s.w[word++] = acc;
+                fill = 0;
+            }
+        } else {
+            const int part = 32 - fill;
+            acc = __builtin_amdgcn_alignbit(f[n], acc, part);
+            s.w[word++] = acc;
+            acc = __builtin_amdgcn_alignbit(f[n], acc, BITS);
+            fill = BITS - part;
+        }
+    }
+    return s;
 }
 
 // ---------------------------------------------------------------- quantizer
 // Pinned fp32 arithmetic, one rounding per operation (no contraction):
 //   c_j = max_i |S_ij|; ic_j = c_j >= FLT_MIN ? 1/c_j : 0 (else c_j := 0)
-//   m_i = max_j |S_ij| ic_j; r_i = m_i / qmax; ir_i = r_i >= FLT_MIN ? 1/r_i : 0
-//   code = clamp(rint((S_ij ic_j) ir_i))
-// Column part: lane j < D folds the band partials of column j.
+//   s_ij = S_ij ic_j (rounded); m_i = max_j |s_ij|; r_i = m_i / qmax;
+//   ir_i = r_i >= FLT_MIN ? 1/r_i : 0;  code = clamp(rint(s_ij * ir_i)),
+//   the last product exact (not rounded before rint)
+// LDS layouts.  A band's 16-column group is written by one lane as 16-byte
+// chunks; eight consecutive lanes write the same chunk index at the same
+// time, and the 32 x 4-byte LDS banks repeat every 128 bytes.  The chunk
+// index is therefore XOR-swizzled with the writer's lane & 7 so that the
+// eight lanes land on eight different 16-byte bank groups.
+//   fp32 plane [NB][D]:  float4 chunk c4 of lane t stored at c4 ^ ((t >> 1) & 3)
+//   FP64 plane [NB][D]:  double2 chunk c2 of lane t stored at c2 ^ (t & 7)
+//   per-column vectors read by column group cg: element n at n ^ cg (double2),
+//   or float4 chunk c4 at c4 ^ ((cg >> 1) & 3) (floats)
+template <int D> __device__ __forceinline__ int plane_idx(int band, int cg, int n) {
+    const int key = ((band * Geo<D>::CG + cg) >> 1) & 3;
+    return band * D + 16 * cg + (((n >> 2) ^ key) << 2) + (n & 3);
+}
+template <int D> __device__ __forceinline__ int part_idx(int band, int cg, int n) {
+    const int key = (band * Geo<D>::CG + cg) & 7;
+    return band * D + 16 * cg + (((n >> 1) ^ key) << 1) + (n & 1);
+}
+__device__ __forceinline__ int colvec2_idx(int j) { return (j & ~15) | ((j & 15) ^ ((j >> 4) & 7)); }
+__device__ __forceinline__ int colvec4_idx(int j) {
+    const int cg = j >> 4, n = j & 15;
+    return 16 * cg + (((n >> 2) ^ ((cg >> 1) & 3)) << 2) + (n & 3);
+}
+
+// Column part: every lane writes its 16 column partials; lane j < D then
+// folds column j over the bands.
 template <int D>
 __device__ __forceinline__ void write_band_partials(float *plane, const float (&v)[16]) {
     using G = Geo<D>;
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
-    float4 *dst = reinterpret_cast<float4 *>(plane + band * D + 16 * cg);
 #pragma unroll
     for (int n4 = 0; n4 < 4; ++n4)
-        dst[n4] = make_float4(v[4 * n4], v[4 * n4 + 1], v[4 * n4 + 2], v[4 * n4 + 3]);
+        *reinterpret_cast<float4 *>(plane + plane_idx<D>(band, cg, 4 * n4)) =
+            make_float4(v[4 * n4], v[4 * n4 + 1], v[4 * n4 + 2], v[4 * n4 + 3]);
 }
 
+// Max over the band partials of column j (non-negative: integer max, exact).
 template <int D> __device__ __forceinline__ float column_max(const float *plane, int j) {
-    float c = 0.0f;
+    uint32_t c = 0;
 #pragma unroll 8
-    for (int b = 0; b < Geo<D>::NB; ++b) c = fmaxf(c, plane[b * D + j]);
-    return c;
+    for (int b = 0; b < Geo<D>::NB; ++b)
+        c = max(c, __float_as_uint(plane[plane_idx<D>(b, j >> 4, j & 15)]));
+    return __uint_as_float(c);
+}
+
+// The 16 per-column floats of column group cg from a colvec4-swizzled vector.
+__device__ __forceinline__ void load_colvec16(const float *vec, int cg, float (&v)[16]) {
+#pragma unroll
+    for (int n4 = 0; n4 < 4; ++n4) {
+        const float4 f = *reinterpret_cast<const float4 *>(vec + colvec4_idx(16 * cg + 4 * n4));
+        v[4 * n4] = f.x; v[4 * n4 + 1] = f.y; v[4 * n4 + 2] = f.z; v[4 * n4 + 3] = f.w;
+    }
 }
 
 // Column scale of column j from its max: stores c_j, returns 1/c_j (or 0).
@@ -188,9 +250,15 @@ __device__ __forceinline__ void load16(const float *src, float (&v)[16]) {
     }
 }
 
-// Row part: row maxima (DPP over the band's lanes), row scales, codes, store.
+// Row part.  x holds S' on entry.  s = S' ic is formed once: |s| is the
+// pinned |S'| ic of the row maximum and s * ir is the pinned scaled entry.
+// The row maxima are reduced over the band's lanes with DPP; lane cg < 4 of
+// a band then computes the two correctly rounded divisions of row cg, and
+// the results are broadcast back with ds_swizzle.  Codes: round half to even
+// of the exact product s * ir (code_bits); |s * ir| <= qmax (1 + 2 eps), so
+// the clamp to [-qmax, qmax] can never act and is omitted.
 template <int D, int BITS>
-__device__ __forceinline__ void quantize_rows_store(const float (&x)[4][16], const float (&ic)[16],
+__device__ __forceinline__ void quantize_rows_store(float (&x)[4][16], const float (&ic)[16],
                                                     uint8_t *rec) {
 #pragma clang fp contract(off)
     using G = Geo<D>;
@@ -198,29 +266,45 @@ __device__ __forceinline__ void quantize_rows_store(const float (&x)[4][16], con
     constexpr float QMAX = (float)((1 << (BITS - 1)) - 1);
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     float *rp = reinterpret_cast<float *>(rec + D * RB);
+    float rm[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        rm[m] = 0.0f;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            x[m][n] = x[m][n] * ic[n];
+            rm[m] = fmaxf(rm[m], fabsf(x[m][n]));
+        }
+        rm[m] = band_max<G::CG>(rm[m]);
+    }
+    // lane cg (< 4) of the band owns row band + NB * cg
+    const float sel01 = (cg & 1) ? rm[1] : rm[0];
+    const float sel23 = (cg & 1) ? rm[3] : rm[2];
+    const float mrow = (cg & 2) ? sel23 : sel01;
+    float r = mrow / QMAX;
+    float ir;
+    if (r >= FLT_MIN) {
+        ir = 1.0f / r;
+    } else {
+        r = 0.0f;
+        ir = 0.0f;
+    }
+    if (cg < 4) rp[band + G::NB * cg] = r;
+    float irm[4];
+    // broadcast lane (band base + m) to the band: ds_swizzle bit mode,
+    // lane' = (lane & and_mask) | or_mask within 32 lanes
+    constexpr int AND_MASK = 0x1F & ~(G::CG - 1);
+    irm[0] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ir), AND_MASK | (0 << 5)));
+    irm[1] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ir), AND_MASK | (1 << 5)));
+    irm[2] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ir), AND_MASK | (2 << 5)));
+    irm[3] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ir), AND_MASK | (3 << 5)));
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int row = band + G::NB * m;
-        float rm = 0.0f;
+        uint32_t f[16];
 #pragma unroll
-        for (int n = 0; n < 16; ++n) rm = fmaxf(rm, fabsf(x[m][n]) * ic[n]);
-        rm = band_max<G::CG>(rm);
-        float r = rm / QMAX;
-        float ir;
-        if (r >= FLT_MIN) {
-            ir = 1.0f / r;
-        } else {
-            r = 0.0f;
-            ir = 0.0f;
-        }
-        if (cg == 0) rp[row] = r;
-        int code[16];
-#pragma unroll
-        for (int n = 0; n < 16; ++n) {
-            const float sv = x[m][n] * ic[n];
-            code[n] = to_code<BITS>(sv * ir);
-        }
-        store_seg<BITS>(rec + row * RB + cg * (2 * BITS), pack_seg<BITS>(code));
+        for (int n = 0; n < 16; ++n) f[n] = code_bits(x[m][n], irm[m]);
+        store_seg<BITS>(rec + row * RB + cg * (2 * BITS), pack_stream<BITS>(f));
     }
 }
 
@@ -240,10 +324,10 @@ __device__ __forceinline__ void quant_tile(uint8_t *rec, const float *S, float *
         cm[n] = fmaxf(fmaxf(fabsf(x[0][n]), fabsf(x[1][n])), fmaxf(fabsf(x[2][n]), fabsf(x[3][n])));
     write_band_partials<D>(plane, cm);
     __syncthreads();
-    if (t < D) lds_ic[t] = column_scale(column_max<D>(plane, t), cp + t);
+    if (t < D) lds_ic[colvec4_idx(t)] = column_scale(column_max<D>(plane, t), cp + t);
     __syncthreads();
     float ic[16];
-    load16<D>(lds_ic + 16 * cg, ic);
+    load_colvec16(lds_ic, cg, ic);
     quantize_rows_store<D, BITS>(x, ic, rec);
 }
 
@@ -320,11 +404,70 @@ __global__ __launch_bounds__(Geo<D>::NT) void dequant_state_kernel(PoolView pool
 // u[D] doubles, 1/c'[D] floats and one k.q partial per wave.
 template <int D> struct DecodeLds {
     static constexpr int PART_F = 2 * Geo<D>::NB * D; // floats in the partials region
-    static constexpr int TOTAL = PART_F + 2 * D + D + 4;
+    static constexpr int TOTAL = PART_F + 4 * D + D + 8; // + {c_j, u_j} FP64 pairs, 1/c'_j, misc
 };
 
+// Lane t of a band of CG lanes reads lane (band base + m) with ds_swizzle
+// (bit mode: lane' = (lane & and_mask) | or_mask, within 32 lanes).
+template <int CG, int M> __device__ __forceinline__ float band_bcast(float v) {
+    constexpr int AND_MASK = 0x1F & ~(CG - 1);
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), AND_MASK | (M << 5)));
+}
+
+// Retention factor a = exp(g) rounded once to fp32 (through FP64 exp).
+__device__ __forceinline__ float gate_factor(float g) { return (float)exp((double)g); }
+
+// What one lane reads of one tile.
+struct TileIn {
+    uint32_t w[4][4];    // the lane's 4 row segments (BITS / 2 dwords used)
+    float r[4];          // row scales of the lane's rows
+    float k[4], q[4];    // k, q at the lane's rows
+    float g;             // KDA: log-gate of row band + NB (cg & 3); GDN: the head's
+    float cj, vj, beta;  // column lane j = t < D: c_j, v_j; beta of the (b, h) row
+    uint8_t *rec;        // the tile's record
+};
+
+template <int D, int BITS, bool KDA, typename TI>
+__device__ __forceinline__ void load_tile(TileIn &in, int tile, uint8_t *rec, const StepIO &io) {
+    using G = Geo<D>;
+    constexpr int RB = D * BITS / 8;
+    const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
+    in.rec = rec;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const Seg<BITS> sg = load_seg<BITS>(rec + (band + G::NB * m) * RB + cg * (2 * BITS));
+#pragma unroll
+        for (int i = 0; i < Seg<BITS>::NWORDS; ++i) in.w[m][i] = sg.w[i];
+    }
+    const float *rp = reinterpret_cast<const float *>(rec + D * RB);
+    const int64_t row_io = tile;
+    const TI *k = reinterpret_cast<const TI *>(io.k) + row_io * D;
+    const TI *q = reinterpret_cast<const TI *>(io.q) + row_io * D;
+    const TI *g = reinterpret_cast<const TI *>(io.g);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int row = band + G::NB * m;
+        in.r[m] = rp[row];
+        in.k[m] = ld<TI>(k, row);
+        in.q[m] = ld<TI>(q, row);
+    }
+    in.g = KDA ? ld<TI>(g, row_io * D + band + G::NB * (cg & 3)) : ld<TI>(g, row_io);
+    in.beta = ld<TI>(reinterpret_cast<const TI *>(io.beta), row_io);
+    if (t < D) {
+        in.cj = rp[D + t];
+        in.vj = ld<TI>(reinterpret_cast<const TI *>(io.v) + row_io * D, t);
+    }
+}
+
+template <int BITS> __device__ __forceinline__ Seg<BITS> seg_of(const TileIn &in, int m) {
+    Seg<BITS> s;
+#pragma unroll
+    for (int i = 0; i < Seg<BITS>::NWORDS; ++i) s.w[i] = in.w[m][i];
+    return s;
+}
+
 template <int D, int BITS, bool KDA, typename TI, typename TO>
-__device__ __forceinline__ void decode_tile(uint8_t *rec, int64_t row_io, const StepIO &io,
+__device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const StepIO &io,
                                             float *lds) {
     using G = Geo<D>;
     constexpr int RB = D * BITS / 8;
@@ -332,108 +475,139 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec, int64_t row_io, const 
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     double *part64 = reinterpret_cast<double *>(lds);
     float *plane_max = lds, *plane_y = lds + PLANE;
-    double *lds_u = reinterpret_cast<double *>(lds + DecodeLds<D>::PART_F);
-    float *lds_ic = lds + DecodeLds<D>::PART_F + 2 * D;
-    float *lds_kq = lds_ic + D;
+    double2 *lds_cu = reinterpret_cast<double2 *>(lds + DecodeLds<D>::PART_F); // {c_j, u_j}
+    float *lds_ic = lds + DecodeLds<D>::PART_F + 4 * D;
+    float *lds_misc = lds_ic + D; // [0]: GDN gate factor
+    TileIn cur;
+    load_tile<D, BITS, KDA, TI>(cur, tile, rec_in, io);
+    uint8_t *rec = cur.rec;
+    float *cp = reinterpret_cast<float *>(rec + D * RB) + D;
+    const int64_t row_io = tile;
 
-    const TI *q = reinterpret_cast<const TI *>(io.q) + row_io * D;
-    const TI *k = reinterpret_cast<const TI *>(io.k) + row_io * D;
-    const TI *v = reinterpret_cast<const TI *>(io.v) + row_io * D;
-    const TI *g = reinterpret_cast<const TI *>(io.g);
-    float *rp = reinterpret_cast<float *>(rec + D * RB);
-    float *cp = rp + D;
-
-    // ---- loads: codes, scales, inputs
     Seg<BITS> seg[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) seg[m] = load_seg<BITS>(rec + (band + G::NB * m) * RB + cg * (2 * BITS));
-    float c[16];
-    load16<D>(cp + 16 * cg, c);
-    double ar[4], kar[4];
-    float kf[4], qf[4], kq_part = 0.0f;
-    const float a_head = KDA ? 0.0f : (float)exp((double)ld<TI>(g, row_io));
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int row = band + G::NB * m;
-        const float a = KDA ? (float)exp((double)ld<TI>(g, row_io * D + row)) : a_head;
-        kf[m] = ld<TI>(k, row);
-        qf[m] = ld<TI>(q, row);
-        ar[m] = (double)a * (double)rp[row];   // a_i r_i, exact in FP64
-        kar[m] = (double)kf[m] * ar[m];        // k_i a_i r_i
-        kq_part += kf[m] * qf[m];
+    for (int m = 0; m < 4; ++m) seg[m] = seg_of<BITS>(cur, m);
+    // ---- retention factors: GDN one per head (one lane, shared through LDS
+    //      after the first barrier); KDA one per key row, computed by lane
+    //      cg & 3 of each band for row band + NB (cg & 3) and broadcast.
+    float am[4];
+    if constexpr (KDA) {
+        const float a = gate_factor(cur.g);
+        am[0] = band_bcast<G::CG, 0>(a);
+        am[1] = band_bcast<G::CG, 1>(a);
+        am[2] = band_bcast<G::CG, 2>(a);
+        am[3] = band_bcast<G::CG, 3>(a);
+    } else {
+        if (t == 0) lds_misc[0] = gate_factor(cur.g);
     }
-    // ---- look-up: band partials of sum_i (k_i a_i r_i) code_ij, FP64
+    // ---- look-up: band partials of sum_i k_i (a_i) r_i code_ij in FP64
+    //      (GDN: the head's factor a multiplies the folded column sum)
     {
-        double acc[16];
+        double kar[4];
 #pragma unroll
-        for (int n = 0; n < 16; ++n) acc[n] = 0.0;
+        for (int m = 0; m < 4; ++m) {
+            kar[m] = (double)cur.k[m] * (double)cur.r[m];
+            if constexpr (KDA) kar[m] *= (double)am[m];
+        }
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int n2 = 0; n2 < 8; ++n2) {
+            double acc0 = 0.0, acc1 = 0.0;
 #pragma unroll
-            for (int n = 0; n < 16; ++n) acc[n] = fma(kar[m], (double)code_at<BITS>(seg[m], n), acc[n]);
-        double2 *dst = reinterpret_cast<double2 *>(part64 + band * D + 16 * cg);
-#pragma unroll
-        for (int n2 = 0; n2 < 8; ++n2) dst[n2] = make_double2(acc[2 * n2], acc[2 * n2 + 1]);
+            for (int m = 0; m < 4; ++m) {
+                acc0 = fma(kar[m], (double)code_at<BITS>(seg[m], 2 * n2), acc0);
+                acc1 = fma(kar[m], (double)code_at<BITS>(seg[m], 2 * n2 + 1), acc1);
+            }
+            *reinterpret_cast<double2 *>(part64 + part_idx<D>(band, cg, 2 * n2)) =
+                make_double2(acc0, acc1);
+        }
     }
-    kq_part = wave_sum(cg == 0 ? kq_part : 0.0f);
-    if ((t & 63) == 0) lds_kq[t >> 6] = kq_part;
     __syncthreads();
+    if constexpr (!KDA) {
+        const float a = lds_misc[0];
+        am[0] = am[1] = am[2] = am[3] = a;
+    }
     if (t < D) {
         double P = 0.0;
 #pragma unroll 8
-        for (int b = 0; b < G::NB; ++b) P += part64[b * D + t];
-        const double beta = (double)ld<TI>(reinterpret_cast<const TI *>(io.beta), row_io);
-        lds_u[t] = beta * ((double)ld<TI>(v, t) - P * (double)cp[t]);
+        for (int b = 0; b < G::NB; ++b) P += part64[part_idx<D>(b, t >> 4, t & 15)];
+        if constexpr (!KDA) P *= (double)am[0];
+        const double cj = (double)cur.cj;
+        lds_cu[colvec2_idx(t)] = make_double2(cj, (double)cur.beta * ((double)cur.vj - P * cj));
     }
+#ifndef SQ_KEEP_F64_CODES
+    // keep the packed codes, not their FP64 values, live across the barrier
+    // (unpacking again costs two VALU per code; holding FP64 codes would cost
+    // 128 VGPRs and halve the waves per SIMD)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < Seg<BITS>::NWORDS; ++i) asm volatile("" : "+v"(seg[m].w[i]));
+#endif
     __syncthreads();
     // ---- decay + delta write in FP64, rounded once to fp32; read-out and
     //      column maxima partials in fp32
     float x[4][16];
     {
-        float cm[16], yp[16];
+        double ar[4];
 #pragma unroll
-        for (int n = 0; n < 16; ++n) {
-            const double cn = (double)c[n];
-            const double un = lds_u[16 * cg + n];
-            cm[n] = 0.0f;
-            yp[n] = 0.0f;
+        for (int m = 0; m < 4; ++m) ar[m] = (double)am[m] * (double)cur.r[m]; // exact
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const double s = fma((double)code_at<BITS>(seg[m], n), ar[m] * cn, (double)kf[m] * un);
-                const float sf = (float)s;
-                x[m][n] = sf;
-                yp[n] = fmaf(qf[m], sf, yp[n]);
-                cm[n] = fmaxf(cm[n], fabsf(sf));
+        for (int n4 = 0; n4 < 4; ++n4) {
+            float cm[4], yp[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = 4 * n4 + i;
+                const double2 cu = lds_cu[colvec2_idx(16 * cg + n)];
+                const double cn = cu.x, un = cu.y;
+                cm[i] = 0.0f;
+                yp[i] = 0.0f;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const double sv = fma((double)code_at<BITS>(seg[m], n), ar[m] * cn,
+                                          (double)cur.k[m] * un);
+                    const float sf = (float)sv;
+                    x[m][n] = sf;
+                    yp[i] = fmaf(cur.q[m], sf, yp[i]);
+                    cm[i] = fmaxf(cm[i], fabsf(sf));
+                }
             }
+            const int pi = plane_idx<D>(band, cg, 4 * n4);
+            *reinterpret_cast<float4 *>(plane_max + pi) = make_float4(cm[0], cm[1], cm[2], cm[3]);
+            *reinterpret_cast<float4 *>(plane_y + pi) = make_float4(yp[0], yp[1], yp[2], yp[3]);
         }
-        write_band_partials<D>(plane_max, cm);
-        write_band_partials<D>(plane_y, yp);
     }
     __syncthreads();
     if (t < D) {
         float yv = 0.0f;
 #pragma unroll 8
-        for (int b = 0; b < G::NB; ++b) yv += plane_y[b * D + t];
+        for (int b = 0; b < G::NB; ++b) yv += plane_y[plane_idx<D>(b, t >> 4, t & 15)];
         st<TO>(reinterpret_cast<TO *>(io.y) + row_io * D, t, yv);
-        lds_ic[t] = column_scale(column_max<D>(plane_max, t), cp + t);
+        lds_ic[colvec4_idx(t)] = column_scale(column_max<D>(plane_max, t), cp + t);
     }
     __syncthreads();
     float ic[16];
-    load16<D>(lds_ic + 16 * cg, ic);
+    load_colvec16(lds_ic, cg, ic);
     quantize_rows_store<D, BITS>(x, ic, rec);
 }
 
+#ifndef SQ_DECODE_WAVES_PER_EU
+#define SQ_DECODE_WAVES_PER_EU 4
+#endif
+// One workgroup per (request, head) tile; four resident per CU (VGPRs and
+// LDS both sized for four 4-wave workgroups), which hides the barriers and
+// reduction phases of one tile behind the others.
 template <int D, bool KDA, typename TI, typename TO>
-__global__ __launch_bounds__(Geo<D>::NT) void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
+__global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(SQ_DECODE_WAVES_PER_EU)))
+void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
     __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D>::TOTAL];
+    const int tile = blockIdx.x;
     const int H = pool.n_heads;
-    const int b = blockIdx.x / H, h = blockIdx.x - b * H;
+    const int b = tile / H, h = tile - b * H;
     uint8_t *rec = pool.base + (int64_t)io.slot[b] * pool.slot_stride + tab.off[h];
-    const int64_t row_io = blockIdx.x; // (b, h) row of the input / output tensors
     switch (tab.bits[h]) {
-    case 4: decode_tile<D, 4, KDA, TI, TO>(rec, row_io, io, lds); break;
-    case 6: decode_tile<D, 6, KDA, TI, TO>(rec, row_io, io, lds); break;
-    default: decode_tile<D, 8, KDA, TI, TO>(rec, row_io, io, lds); break;
+    case 4: decode_tile<D, 4, KDA, TI, TO>(rec, tile, io, lds); break;
+    case 6: decode_tile<D, 6, KDA, TI, TO>(rec, tile, io, lds); break;
+    default: decode_tile<D, 8, KDA, TI, TO>(rec, tile, io, lds); break;
     }
 }
 
