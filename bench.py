@@ -63,6 +63,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-variants", action="store_true", help="only the headline kernel")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    ap.add_argument("--prewarm", type=float, default=0.3,
+                    help="seconds of untimed steps before the warm-up steps")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for profiles)")
     args = ap.parse_args()
@@ -140,6 +142,12 @@ def main():
 
     def timed(pl, sl, fn=None):
         fn = fn or (lambda n, ev=None: run(pl, sl, n, ev))
+        # bring the clocks to their loaded steady state first (untimed), then
+        # the W warm-up steps, then exactly K timed steps
+        t_end = time.perf_counter() + args.prewarm
+        while time.perf_counter() < t_end:
+            fn(10)
+            torch.cuda.synchronize()
         fn(args.warmup)
         torch.cuda.synchronize()
         t_start = time.perf_counter()

@@ -1,0 +1,167 @@
+"""The C-ABI library on the host: symbols, layout and argument validation.
+
+No test here launches work: every call either is host-only (pool descriptor,
+layout) or is rejected by validation before any HIP call is made, so the
+suite runs without a GPU.
+"""
+import ctypes
+import threading
+
+import pytest
+
+import bench
+import quantized_gated_delta_amd as Q
+from quantized_gated_delta_amd import sq as S
+
+FAKE_DEV = 0x7F0000000000   # 256-byte aligned, never dereferenced on the host
+
+
+def test_library_exports_every_declared_symbol():
+    names = Q.header_symbols()
+    for must in ("sq_pool_bytes", "sq_pool_create", "sq_pool_destroy", "sq_pool_layout",
+                 "sq_quant_state", "sq_decode_step", "sq_dequant_state", "sq_f32_decode_step",
+                 "sq_check_slots", "sq_last_error", "sq_version"):
+        assert must in names
+    lib = Q.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert "gfx950" in Q.version()
+
+
+def _layout(bits, d):
+    offs, pos = [], 0
+    for b in bits:
+        offs.append(pos)
+        pos += d * d * b // 8 + 8 * d
+    return pos, offs
+
+
+@pytest.mark.parametrize("d,bits", [(128, [6] * 48), (128, [4, 6, 8, 6]), (64, [8, 4, 6])])
+def test_pool_bytes_and_layout(d, bits):
+    stride, offs = _layout(bits, d)
+    assert Q.sq_pool_bytes(640, len(bits), d, d, bits, Q.SQ_GATE_GDN) == 640 * stride
+    h = Q.sq_pool_create(640, len(bits), d, d, bits, Q.SQ_GATE_KDA, FAKE_DEV, 640 * stride)
+    try:
+        st, ho, rb = Q.sq_pool_layout(h, len(bits))
+        assert st == stride and ho == offs
+        assert rb == [d * d * b // 8 + 8 * d for b in bits]
+        assert all(o % 256 == 0 for o in ho) and st % 256 == 0
+    finally:
+        Q.sq_pool_destroy(h)
+
+
+def _expect(status, fn, *args, text=None):
+    with pytest.raises(Q.SQError) as e:
+        fn(*args)
+    assert e.value.status == status, (e.value.status, e.value.text)
+    if text:
+        assert text in e.value.text, e.value.text
+    return e.value
+
+
+def test_descriptor_validation():
+    _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_bytes, 4, 2, 128, 128, [6, 3], 0, text="head_bits[1]")
+    _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_bytes, 4, 1, 96, 96, [6], 0, text="64 or 128")
+    _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_bytes, 4, 1, 128, 64, [6], 0, text="d_k must equal")
+    _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_bytes, 4, 65, 128, 128, [6] * 65, 0, text="n_heads")
+    _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_bytes, 4, 0, 128, 128, [6], 0, text="n_heads")
+    _expect(Q.SQ_EINVAL, Q.sq_pool_bytes, 0, 1, 128, 128, [6], 0, text="n_slots")
+    _expect(Q.SQ_EINVAL, Q.sq_pool_bytes, 4, 1, 128, 128, [6], 7, text="gate")
+    L = Q.lib()
+    assert L.sq_pool_bytes(None, ctypes.byref(ctypes.c_size_t())) == Q.SQ_EINVAL
+    d = S._Desc(4, 1, 128, 128, None, 0)
+    assert L.sq_pool_bytes(ctypes.byref(d), ctypes.byref(ctypes.c_size_t())) == Q.SQ_EINVAL
+    assert "head_bits is NULL" in Q.sq_last_error()
+
+
+def test_create_validation():
+    need = Q.sq_pool_bytes(8, 2, 64, 64, [6, 6], 0)
+    _expect(Q.SQ_ENOMEM, Q.sq_pool_create, 8, 2, 64, 64, [6, 6], 0, FAKE_DEV, need - 1)
+    _expect(Q.SQ_EINVAL, Q.sq_pool_create, 8, 2, 64, 64, [6, 6], 0, FAKE_DEV + 64, need,
+            text="256-byte")
+    _expect(Q.SQ_EINVAL, Q.sq_pool_create, 8, 2, 64, 64, [6, 6], 0, 0, need, text="dev_buf")
+    assert Q.lib().sq_pool_destroy(None) == Q.SQ_OK
+
+
+@pytest.fixture
+def pool():
+    h = Q.sq_pool_create(8, 2, 128, 128, [6, 4], 0, FAKE_DEV,
+                         Q.sq_pool_bytes(8, 2, 128, 128, [6, 4], 0))
+    yield h
+    Q.sq_pool_destroy(h)
+
+
+def test_step_validation_without_launch(pool):
+    P = FAKE_DEV + 4096
+    ok = dict(q=P, k=P, v=P, beta=P, g=P, y=P)
+    # n = 0 is a no-op: returns before any HIP call
+    Q.sq_decode_step(pool, None, 0, in_dtype=1, y_dtype=1, stream=0, **ok)
+    Q.sq_quant_state(pool, None, 0, None, stream=0)
+    Q.sq_dequant_state(pool, None, 0, None, stream=0)
+    _expect(Q.SQ_EINVAL, Q.sq_decode_step, pool, P, -1, P, P, P, P, P, P, 1, 1, 0, text="n must")
+    _expect(Q.SQ_EINVAL, Q.sq_decode_step, pool, P, 9, P, P, P, P, P, P, 1, 1, 0,
+            text="exceeds n_slots")
+    _expect(Q.SQ_EINVAL, Q.sq_decode_step, pool, None, 2, P, P, P, P, P, P, 1, 1, 0,
+            text="slot_idx is NULL")
+    _expect(Q.SQ_EINVAL, Q.sq_decode_step, pool, P, 2, None, P, P, P, P, P, 1, 1, 0,
+            text="q is NULL")
+    _expect(Q.SQ_EINVAL, Q.sq_decode_step, pool, P, 2, P, P + 2, P, P, P, P, 1, 1, 0,
+            text="k is not 16-byte")
+    _expect(Q.SQ_EINVAL, Q.sq_decode_step, pool, P, 2, P, P, P, P, P, P, 5, 1, 0,
+            text="in_dtype")
+    _expect(Q.SQ_EINVAL, Q.sq_decode_step, pool, P, 2, P, P, P, P, P, P, 1, 9, 0,
+            text="y_dtype")
+    _expect(Q.SQ_EINVAL, Q.sq_decode_step, pool, P + 1, 2, P, P, P, P, P, P, 1, 1, 0,
+            text="slot_idx is not 4-byte")
+    _expect(Q.SQ_EINVAL, Q.sq_quant_state, pool, P, 2, None, 0, text="S is NULL")
+    _expect(Q.SQ_EINVAL, Q.sq_dequant_state, pool, P, 2, P + 8, 0, text="S is not 16-byte")
+    _expect(Q.SQ_EINVAL, Q.sq_decode_step, None, P, 2, P, P, P, P, P, P, 1, 1, 0,
+            text="pool is NULL")
+
+
+def test_f32_step_validation_without_launch():
+    P = FAKE_DEV
+    Q.sq_f32_decode_step(P, 4, 2, 128, 128, 0, None, 0, P, P, P, P, P, P, 1, 1, 0)
+    _expect(Q.SQ_EUNSUPPORTED, Q.sq_f32_decode_step, P, 4, 2, 96, 96, 0, P, 1,
+            P, P, P, P, P, P, 1, 1, 0)
+    _expect(Q.SQ_EINVAL, Q.sq_f32_decode_step, P, 4, 2, 128, 128, 3, P, 1,
+            P, P, P, P, P, P, 1, 1, 0, text="gate")
+    _expect(Q.SQ_EINVAL, Q.sq_f32_decode_step, P, 4, 2, 128, 128, 0, P, 5,
+            P, P, P, P, P, P, 1, 1, 0, text="exceeds")
+    _expect(Q.SQ_EINVAL, Q.sq_f32_decode_step, P, 4, 2, 128, 128, 0, None, 2,
+            P, P, P, P, P, P, 1, 1, 0, text="slot_idx")
+    _expect(Q.SQ_EINVAL, Q.sq_f32_decode_step, P + 4, 4, 2, 128, 128, 0, P, 2,
+            P, P, P, P, P, P, 1, 1, 0, text="state_pool")
+
+
+def test_last_error_is_thread_local():
+    _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_bytes, 4, 1, 96, 96, [6], 0)
+    seen = []
+
+    def other():
+        Q.sq_pool_bytes(4, 1, 128, 128, [6], 0)
+        seen.append(Q.sq_last_error())
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen == [""]
+    assert "64 or 128" in Q.sq_last_error()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(S, "_lib", None)
+    monkeypatch.setattr(S, "LIB_PATH", str(tmp_path / "libsq.so"))
+    with pytest.raises(ImportError):
+        S.lib()
+
+
+def test_bench_byte_model():
+    # per (request, head) update at d = 128, bf16 I/O: codes and scales read
+    # and written, q k v beta g read, y written; plus 4 B slot index per request
+    assert bench.algo_bytes_per_step(1, 1, 128, [6], "gdn") == 27652 + 4
+    assert bench.algo_bytes_per_step(1, 1, 128, [4], "gdn") == 19460 + 4
+    assert bench.algo_bytes_per_step(1, 1, 128, [8], "gdn") == 35844 + 4
+    assert bench.algo_bytes_per_step(1, 1, 128, [6], "kda") == 27652 + 254 + 4
+    assert bench.algo_bytes_per_step(512, 48, 128, [6] * 48, "gdn") == 679577600
+    assert bench.f32_bytes_per_step(1, 1, 128, "gdn") == 132100 + 4
