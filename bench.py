@@ -67,6 +67,10 @@ def main():
                     help="seconds of untimed steps before the warm-up steps")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for profiles)")
+    ap.add_argument("--trajectory", action="store_true",
+                    help="only the c4 trajectory: GDN + KDA layers, per-step y error of the "
+                         "quantized step against the fp32-state step")
+    ap.add_argument("--traj-steps", type=int, default=1024)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -93,6 +97,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         eprint("copied 3 x 1 GiB")
+        return
+
+    if args.trajectory:
+        trajectory(args, dev)
         return
 
     wl = W.make(args.workload)
@@ -279,6 +287,65 @@ def main():
         "cpu_baseline": cpu,
         "variants": variants,
     }
+    print(json.dumps(out), flush=True)
+
+
+def trajectory(args, dev):
+    """c4: two layers (GDN, KDA), B = 1024, H = 32, bits 4/6/8 at 25/50/25 %.
+    Both the packed pool and an fp32 state pool start from the same fp32
+    warm-up state and see identical bf16 inputs; y of the quantized step is
+    compared with y of the fp32-state step at every step (relative L2 over
+    the whole [B, H, d] output)."""
+    import numpy as np
+    import torch
+
+    import quantized_gated_delta_amd as Q
+    import workload as W
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    wl = W.make("c4", steps=args.traj_steps)
+    B, H, d, T = wl.B, wl.H, wl.d, args.traj_steps
+    ident = torch.arange(B, dtype=torch.int32, device=dev)
+    layers = []
+    for layer in wl.layers:
+        kda = layer.gate == "kda"
+        state = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
+        yw = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+        for t in range(-W.WARMUP_STEPS, 0):
+            x = {k: to_dev(v) for k, v in wl.step_inputs(layer, t).items()}
+            Q.sq_f32_decode_step(state, B, H, d, d, int(kda), ident, B, x["q"], x["k"], x["v"],
+                                 x["beta"], x["g"], yw)
+        pool = Q.StatePool(B, H, d, layer.head_bits.tolist(), layer.gate, device=dev)
+        pool.quant_state(ident, state)
+        layers.append((layer, kda, state, pool))
+    torch.cuda.synchronize()
+    errs = {l.index: [] for l, _, _, _ in layers}
+    yq = torch.empty((B * H, d), dtype=torch.bfloat16, device=dev)
+    yf = torch.empty((B * H, d), dtype=torch.bfloat16, device=dev)
+    t0 = time.time()
+    for t in range(T):
+        for layer, kda, state, pool in layers:
+            x = {k: to_dev(v) for k, v in wl.step_inputs(layer, t).items()}
+            pool.decode_step(ident, x["q"], x["k"], x["v"], x["beta"], x["g"], yq)
+            Q.sq_f32_decode_step(state, B, H, d, d, int(kda), ident, B, x["q"], x["k"], x["v"],
+                                 x["beta"], x["g"], yf)
+            a = yq.float()
+            b = yf.float()
+            errs[layer.index].append(float(torch.linalg.vector_norm(a - b)
+                                           / torch.linalg.vector_norm(b)))
+        if t in (0, 15, 63, 255, T - 1):
+            eprint("step %d: %s (%.0f s)" % (t + 1, {k: round(v[-1], 4) for k, v in errs.items()},
+                                            time.time() - t0))
+    out = {"workload": "c4: GDN + KDA layers, B=1024, H=32, d=128, bits 4/6/8, bf16, %d steps" % T,
+           "y_rel_l2_vs_fp32_state": {}}
+    for layer, _, _, _ in layers:
+        e = np.array(errs[layer.index])
+        marks = {str(s): float(e[s - 1]) for s in (1, 16, 64, 256, T) if s <= T}
+        out["y_rel_l2_vs_fp32_state"][layer.gate] = {
+            "bits": {str(b): int((layer.head_bits == b).sum()) for b in (4, 6, 8)},
+            "at_step": marks, "mean": float(e.mean()), "max": float(e.max())}
     print(json.dumps(out), flush=True)
 
 

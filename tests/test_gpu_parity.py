@@ -402,3 +402,63 @@ def test_n0_noop_and_slot_check():
     with pytest.raises(Q.SQError) as e:
         side.gpu.check_slots(bad)
     assert "outside" in e.value.text
+
+
+# ----------------------------------------------------------------- c4
+def test_c4_two_layers_vs_fp32_state():
+    """GDN and KDA layers (B = 1024, H = 32, bits 4/6/8): the quantized step
+    and the fp32-state step on identical inputs from the same warm-up state;
+    sampled rows of both kernels against the oracle; y error of the quantized
+    step against the fp32-state step tracked per step."""
+    T = 24
+    wl = W.make("c4", steps=T)
+    for layer in wl.layers:
+        log("c4 layer %d (%s)" % (layer.index, layer.gate))
+        kda = layer.gate == "kda"
+        B, H, d = wl.B, wl.H, wl.d
+        side = Side(wl, layer)
+        rows = sample_rows(B, H, 16, seed=10 + layer.index)
+        # fp32 warm-up on the GPU for every row, oracle warm-up for the sampled rows
+        state = torch.zeros((B, H, d, d), dtype=torch.float32, device=DEV)
+        ident = torch.arange(B, dtype=torch.int32, device=DEV)
+        yw = torch.empty((B, H, d), dtype=torch.bfloat16, device=DEV)
+        for t in range(-W.WARMUP_STEPS, 0):
+            x = dev_inputs(wl.step_inputs(layer, t))
+            Q.sq_f32_decode_step(state, B, H, d, d, int(kda), ident, B, x["q"], x["k"], x["v"],
+                                 x["beta"], x["g"], yw)
+        S_or = Hn.oracle_warmup(wl, layer, rows)
+        ridx = torch.from_numpy(rows[:, 0].astype(np.int64)).to(DEV)
+        hidx = torch.from_numpy(rows[:, 1].astype(np.int64)).to(DEV)
+        state[ridx, hidx] = to_dev(S_or)
+        side.gpu.quant_state(side.slot_dev, state)
+        side.init_oracle_rows(rows, S_or)
+        S_ref32 = S_or.copy()
+        errs = []
+        for t in range(T):
+            x = wl.step_inputs(layer, t)
+            xd = dev_inputs(x)
+            yq = torch.empty((B * H, d), dtype=torch.bfloat16, device=DEV)
+            yf = torch.empty((B, H, d), dtype=torch.bfloat16, device=DEV)
+            side.gpu.decode_step(side.slot_dev, xd["q"], xd["k"], xd["v"], xd["beta"], xd["g"], yq)
+            Q.sq_f32_decode_step(state, B, H, d, d, int(kda), ident, B, xd["q"], xd["k"], xd["v"],
+                                 xd["beta"], xd["g"], yf)
+            yq_h = W.to_f32(from_dev(yq)).astype(np.float64)
+            yf_h = W.to_f32(from_dev(yf)).reshape(B * H, d).astype(np.float64)
+            errs.append(Hn.rel_l2(yq_h, yf_h))
+            idx = rows[:, 0] * H + rows[:, 1]
+            xs = {k: W.to_f32(v[idx]) for k, v in x.items()}
+            offs, bits = side.rows_offsets(rows)
+            y_ref = O.records_step(kda, side.host.bytes, offs, bits, d, d, xs["q"], xs["k"],
+                                   xs["v"], xs["beta"], xs["g"])
+            assert Hn.rel_l2(yq_h[idx], Hn.to_bf16_f32(y_ref)) <= Hn.Y_REL_L2
+            y32 = O.f32_step(kda, S_ref32, xs["q"], xs["k"], xs["v"], xs["beta"], xs["g"])
+            assert Hn.rel_l2(yf_h[idx], Hn.to_bf16_f32(y32)) <= Hn.Y_REL_L2
+        pool = side.gpu_pool()
+        check_records(side, rows, pool, "c4 layer %d" % layer.index)
+        got32 = state[ridx, hidx].cpu().numpy()
+        assert Hn.rel_l2(got32, S_ref32) <= 1e-4
+        log("c4 layer %d: y error vs fp32 state, step 1 %.3g, step %d %.3g, max %.3g"
+            % (layer.index, errs[0], T, errs[-1], max(errs)))
+        assert np.isfinite(errs).all() and max(errs) < 0.5
+        side.gpu.close()
+        del state
