@@ -75,7 +75,9 @@ constexpr int kHalfMirror = 0x141; // row_half_mirror: lane i <-> 7 - i within 8
 // unsigned integers is the numeric order, so an integer max (which folds the
 // DPP exchange into one instruction) gives the float max exactly.
 template <int CTRL> __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+    // old = 0 is the identity of the unsigned max, so the exchange folds into
+    // the max instruction as a DPP source
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 template <int CG> __device__ __forceinline__ float band_max(float vf) {
     uint32_t v = __float_as_uint(vf);
