@@ -45,6 +45,12 @@
  *   6-bit four codes per three bytes.  Record sizes at d = 128:
  *   9216 / 13312 / 17408 bytes for 4 / 6 / 8 bits (d = 64: 2560/3584/4608),
  *   all multiples of 256 bytes.
+ *   bits = 16 marks an FP16 pivot head (hyper.ai summary, "Method", second
+ *   paragraph: the highest-risk state units stay in FP16 as sparse
+ *   pivots): its record is the state itself as IEEE binary16, row-major
+ *   [d_k][d_v], 2 d_k d_v bytes, no scales; the decode step updates it in
+ *   FP64 from the widened values, rounds S' to fp32 and then to binary16
+ *   (nearest even; values beyond the binary16 range become infinite).
  *
  * Execution
  *  - Compute entry points only validate their arguments on the host and
@@ -56,7 +62,7 @@
  *    slot_idx must be distinct and in [0, n_slots); slots not listed are
  *    never read or written.  Overlapping calls on the same slots race.
  *  - n = 0 is a valid no-op.
- *  - Supported shapes: d_k = d_v = d in {64, 128}; bits in {4, 6, 8};
+ *  - Supported shapes: d_k = d_v = d in {64, 128}; bits in {4, 6, 8, 16};
  *    1 <= n_heads <= 64.  Others return SQ_EUNSUPPORTED.
  *  - NaN or infinite inputs give undefined (but memory-safe) results.
  */
@@ -89,7 +95,7 @@ typedef struct {
     int32_t n_heads;          /* heads per request, 1..64 */
     int32_t d_k;              /* key dimension (rows of the state) */
     int32_t d_v;              /* value dimension (columns), must equal d_k */
-    const uint8_t *head_bits; /* host array [n_heads], each 4, 6 or 8; copied */
+    const uint8_t *head_bits; /* host array [n_heads], each 4, 6, 8 or 16; copied */
     sq_gate gate;             /* GDN: g is [n, H]; KDA: g is [n, H, d_k] */
 } sq_pool_desc;
 

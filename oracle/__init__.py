@@ -44,6 +44,10 @@ def lib():
         L.sqo_qmax.argtypes = [i32]
         L.sqo_row_bytes.restype = i64
         L.sqo_row_bytes.argtypes = [i32, i32]
+        L.sqo_f16_to_f32.restype = ctypes.c_float
+        L.sqo_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.sqo_f32_to_f16.restype = ctypes.c_uint16
+        L.sqo_f32_to_f16.argtypes = [ctypes.c_float]
         L.sqo_record_bytes.restype = i64
         L.sqo_record_bytes.argtypes = [i32, i32, i32]
         L.sqo_pack_row.restype = i32
@@ -107,6 +111,15 @@ def row_bytes(bits: int, dv: int) -> int:
 
 def record_bytes(bits: int, dk: int, dv: int) -> int:
     return lib().sqo_record_bytes(bits, dk, dv)
+
+
+def f32_to_f16(x: float) -> int:
+    """Nearest binary16 (ties to even), as raw bits."""
+    return lib().sqo_f32_to_f16(float(x))
+
+
+def f16_to_f32(h: int) -> float:
+    return lib().sqo_f16_to_f32(int(h))
 
 
 def pack_row(bits: int, codes) -> np.ndarray:

@@ -59,8 +59,76 @@ int sqo_qmax(int bits) { return (1 << (bits - 1)) - 1; }
 
 int64_t sqo_row_bytes(int bits, int dv) { return ((int64_t)dv * bits + 7) / 8; }
 
+/* bits = 16 marks an FP16 pivot record (hyper.ai "Method" paragraph 2: the
+ * highest-risk units are kept in FP16 as sparse pivots): the state itself as
+ * IEEE binary16, row-major, no scales. */
 int64_t sqo_record_bytes(int bits, int dk, int dv) {
+    if (bits == 16) return 2 * (int64_t)dk * dv;
     return (int64_t)dk * sqo_row_bytes(bits, dv) + 4 * (int64_t)dk + 4 * (int64_t)dv;
+}
+
+/* ------------------------------------------------------------------ */
+/* IEEE binary16 <-> binary32, from the format's definition             */
+/* ------------------------------------------------------------------ */
+/* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits;
+ * exponent 0 holds zero and subnormals (fraction * 2^-24), 31 inf / NaN. */
+float sqo_f16_to_f32(uint16_t h) {
+    const uint32_t sign = (uint32_t)(h >> 15) << 31;
+    const int e = (h >> 10) & 31, f = h & 1023;
+    float mag;
+    if (e == 0)
+        mag = ldexpf((float)f, -24);
+    else if (e == 31)
+        mag = f ? NAN : INFINITY;
+    else
+        mag = ldexpf((float)(1024 + f), e - 25);
+    uint32_t u;
+    memcpy(&u, &mag, 4);
+    u |= sign;
+    memcpy(&mag, &u, 4);
+    return mag;
+}
+
+/* Round a float to the nearest binary16, ties to even (overflow to inf). */
+uint16_t sqo_f32_to_f16(float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return sign | 0x7E00u;          /* NaN */
+    /* exact rational value |x| = m * 2^(e - 150) */
+    const int e = (int)(a >> 23);
+    const uint32_t m = e ? ((a & 0x7FFFFFu) | 0x800000u) : (a & 0x7FFFFFu);
+    const int ee = e ? e : 1;
+    /* target spacing: 2^(E - 25) for a normal half of biased exponent E
+     * (value in [2^(E-15), 2^(E-14))), 2^-24 for subnormals */
+    int E = ee - 127 + 15;                               /* half biased exponent */
+    if (e == 0 || E < 1) E = 1;                          /* subnormal spacing 2^-24 */
+    const int shift = (E - 25) - (ee - 150);             /* m * 2^-shift in half units */
+    uint32_t q;
+    if (shift <= 0) {
+        q = m << (-shift);
+    } else if (shift > 31) {
+        q = 0;
+    } else {
+        q = m >> shift;
+        const uint32_t rem = m & ((1u << shift) - 1u), half = 1u << (shift - 1);
+        if (rem > half || (rem == half && (q & 1u))) ++q;
+    }
+    /* q counts units of 2^(E - 25); q in [1024, 2048] for normals at E */
+    uint32_t bitsv;
+    if (E == 1 && q < 1024) {
+        bitsv = q;                                       /* subnormal (or zero) */
+    } else {
+        int EE = E;
+        if (q >= 2048) {                                 /* rounding carried */
+            q >>= 1;
+            ++EE;
+        }
+        if (EE >= 31) return sign | 0x7C00u;             /* overflow */
+        bitsv = ((uint32_t)EE << 10) | (q - 1024);
+    }
+    return sign | (uint16_t)bitsv;
 }
 
 /* Pack n codes of one row.  Returns 0, or -1 if a code is out of range. */
@@ -271,6 +339,27 @@ int sqo_record_pack(int bits, int dk, int dv, const int32_t *Q, const float *r, 
     return 0;
 }
 
+/* FP16 pivot record: one step.  FP64 step on the exactly widened state, S'
+ * rounded once to fp32 (as for the quantized records), then to binary16. */
+static void f16_record_step(int kda, int dk, int dv, uint8_t *rec, const float *q,
+                            const float *k, const float *v, float beta, const float *g,
+                            double *y) {
+    const size_t n = (size_t)dk * dv;
+    uint16_t *h = (uint16_t *)rec;
+    double *S = (double *)malloc(sizeof(double) * n);
+    double alpha[1024], qd[1024], kd[1024], vd[1024];
+    for (size_t e = 0; e < n; ++e) S[e] = (double)sqo_f16_to_f32(h[e]);
+    gate_alpha(kda, dk, g, alpha);
+    for (int i = 0; i < dk; ++i) {
+        qd[i] = q[i];
+        kd[i] = k[i];
+    }
+    for (int j = 0; j < dv; ++j) vd[j] = v[j];
+    sqo_gated_delta_f64(dk, dv, S, alpha, qd, kd, vd, (double)beta, y);
+    for (size_t e = 0; e < n; ++e) h[e] = sqo_f32_to_f16((float)S[e]);
+    free(S);
+}
+
 /* ------------------------------------------------------------------ */
 /* Row-parallel drivers                                                */
 /* ------------------------------------------------------------------ */
@@ -301,6 +390,11 @@ static void run_row(const job_t *J, int row) {
     switch (J->op) {
     case OP_QUANT: {
         uint8_t *rec = J->base + J->offs[row];
+        if (J->bits[row] == 16) {
+            const float *S = J->S32 + (size_t)row * n;
+            for (size_t e = 0; e < n; ++e) ((uint16_t *)rec)[e] = sqo_f32_to_f16(S[e]);
+            break;
+        }
         int32_t *Q = (int32_t *)malloc(sizeof(int32_t) * n);
         float rr[1024], cc[1024];
         sqo_quantize(J->bits[row], dk, dv, J->S32 + (size_t)row * n, Q, rr, cc);
@@ -310,6 +404,11 @@ static void run_row(const job_t *J, int row) {
     }
     case OP_DEQUANT: {
         const uint8_t *rec = J->base + J->offs[row];
+        if (J->bits[row] == 16) {
+            float *S = J->S32 + (size_t)row * n;
+            for (size_t e = 0; e < n; ++e) S[e] = sqo_f16_to_f32(((const uint16_t *)rec)[e]);
+            break;
+        }
         int32_t *Q = (int32_t *)malloc(sizeof(int32_t) * n);
         float rr[1024], cc[1024];
         sqo_record_unpack(J->bits[row], dk, dv, rec, Q, rr, cc);
@@ -320,6 +419,11 @@ static void run_row(const job_t *J, int row) {
     case OP_STEP: {
         uint8_t *rec = J->base + J->offs[row];
         const int bits = J->bits[row];
+        if (bits == 16) {
+            f16_record_step(J->kda, dk, dv, rec, J->q + (size_t)row * dk, J->k + (size_t)row * dk,
+                            J->v + (size_t)row * dv, J->beta[row], g, J->y + (size_t)row * dv);
+            break;
+        }
         int32_t *Q = (int32_t *)malloc(sizeof(int32_t) * n);
         float rr[1024], cc[1024];
         sqo_record_unpack(bits, dk, dv, rec, Q, rr, cc);
@@ -382,9 +486,10 @@ static int run_rows(job_t proto, int n_rows, int n_threads) {
 
 static int check_bits(int n, const uint8_t *bits) {
     for (int i = 0; i < n; ++i)
-        if (bits[i] != 4 && bits[i] != 6 && bits[i] != 8) return -1;
+        if (bits[i] != 4 && bits[i] != 6 && bits[i] != 8 && bits[i] != 16) return -1;
     return 0;
 }
+
 
 /* Quantize fp32 states S[n, dk, dv] into the records at base + offs[row]. */
 int sqo_records_quantize(int n, int dk, int dv, const uint8_t *bits, const int64_t *offs,

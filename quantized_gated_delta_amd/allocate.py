@@ -1,0 +1,120 @@
+"""Lifetime-aware bit allocation with FP16 pivots (offline, once per model).
+
+Source: hyper.ai summary of STEPQuant, "Method" paragraph 2, and blog.ontle.kr
+(the lifetime-allocation paragraphs).  For each recurrent-state unit (here a
+head) the method estimates the reconstruction distortion at each candidate
+bit width and the mean log retention; the error retention after j updates is
+approximated as exponential, which gives a lifetime weight; under an average
+bit budget it picks widths that minimise the lifetime-weighted distortion,
+and keeps the highest-risk units in FP16 as sparse pivots.  This runs
+offline: the decode step only reads the resulting per-head bit table.
+
+Readings (the pages give the recipe in words, no formulas):
+  retention   rho_h = exp(mean log-gate of head h over the calibration steps
+              and, for KDA, its key channels)
+  lifetime    w_h = sum_j rho_h^(2 j) = 1 / (1 - rho_h^2): squared error
+              decays by rho^2 per step, so a unit of fresh squared error adds
+              up to w_h over its life
+  distortion  D_h(b) = mean over calibration states of
+              ||S - DQ_b(S)||^2 / ||S||^2 with the pool's own quantizer
+              (measured with the GPU quant / dequant kernels)
+  objective   minimise sum_h w_h D_h(b_h) subject to mean_h b_h <= budget over
+              the non-pivot heads, b_h in the candidate widths (greedy on the
+              largest objective decrease per extra bit)
+  pivots      the n_pivots heads with the largest w_h D_h(b_min) are stored
+              as FP16 (bits = 16) outside the nominal budget
+"""
+from __future__ import annotations
+
+import math
+from typing import Sequence
+
+import numpy as np
+
+
+def lifetime_weights(mean_log_retention) -> np.ndarray:
+    """w = 1 / (1 - rho^2) with rho = exp(mean log retention) (< 1)."""
+    mlr = np.minimum(np.asarray(mean_log_retention, np.float64), -1e-9)
+    return 1.0 / -np.expm1(2.0 * mlr)
+
+
+def mean_log_retention(log_gates) -> np.ndarray:
+    """Per head: mean of the log-gates over steps (and key channels for KDA).
+    log_gates: [T, H] (GDN) or [T, H, d_k] (KDA), any float dtype."""
+    g = np.asarray(log_gates, np.float64)
+    axes = (0,) if g.ndim == 2 else (0, 2)
+    return g.mean(axis=axes)
+
+
+def allocate_bits(distortion: np.ndarray, weights: np.ndarray, avg_bits: float,
+                  candidates: Sequence[int] = (4, 6, 8), n_pivots: int = 0,
+                  pivot_bits: int = 16) -> np.ndarray:
+    """distortion: [H, len(candidates)] (non-increasing in the width);
+    weights: [H].  Returns the width per head (pivots get pivot_bits)."""
+    D = np.asarray(distortion, np.float64)
+    w = np.asarray(weights, np.float64)
+    cand = list(candidates)
+    H = D.shape[0]
+    if D.shape != (H, len(cand)) or w.shape != (H,):
+        raise ValueError("distortion must be [H, n_candidates] and weights [H]")
+    if sorted(cand) != cand:
+        raise ValueError("candidates must be increasing")
+    bits = np.full(H, cand[0], np.int64)
+    risk = w * D[:, 0]
+    pivots = np.argsort(-risk, kind="stable")[:n_pivots] if n_pivots > 0 else np.array([], int)
+    free = np.setdiff1d(np.arange(H), pivots)
+    level = np.zeros(H, np.int64)
+    budget = avg_bits * len(free) - cand[0] * len(free)
+    if budget < -1e-9:
+        raise ValueError("budget below the smallest width")
+    while True:
+        best, best_gain = -1, 0.0
+        for h in free:
+            l = level[h]
+            if l + 1 >= len(cand):
+                continue
+            extra = cand[l + 1] - cand[l]
+            if extra > budget + 1e-9:
+                continue
+            gain = w[h] * (D[h, l] - D[h, l + 1]) / extra
+            if gain > best_gain:
+                best, best_gain = h, gain
+        if best < 0:
+            break
+        budget -= cand[level[best] + 1] - cand[level[best]]
+        level[best] += 1
+    bits[free] = [cand[l] for l in level[free]]
+    bits[pivots] = pivot_bits
+    return bits.astype(np.uint8)
+
+
+def measure_distortion(states, candidates: Sequence[int] = (4, 6, 8)) -> np.ndarray:
+    """D[h, b]: mean over requests of ||S - DQ_b(S)||^2 / ||S||^2 for fp32
+    device states [N, H, d, d], through the pool's quant / dequant kernels."""
+    import torch
+
+    from .sq import StatePool
+
+    N, H, d, _ = states.shape
+    slot = torch.arange(N, dtype=torch.int32, device=states.device)
+    out = np.zeros((H, len(candidates)))
+    energy = states.double().pow(2).sum(dim=(2, 3)).clamp_min(1e-300)
+    for i, b in enumerate(candidates):
+        pool = StatePool(N, H, d, [b] * H, "gdn", device=states.device)
+        pool.quant_state(slot, states)
+        back = pool.dequant_state(slot)
+        err = (back.double() - states.double()).pow(2).sum(dim=(2, 3))
+        out[:, i] = (err / energy).mean(dim=0).cpu().numpy()
+        pool.close()
+    return out
+
+
+def calibrate(states, log_gates, avg_bits: float = 6.0, candidates=(4, 6, 8),
+              n_pivots: int = 0) -> dict:
+    """Bits per head from calibration states [N, H, d, d] (device, fp32) and
+    the log-gates seen over the calibration steps."""
+    D = measure_distortion(states, candidates)
+    w = lifetime_weights(mean_log_retention(log_gates))
+    bits = allocate_bits(D, w, avg_bits, candidates, n_pivots)
+    return {"bits": bits, "distortion": D, "weights": w,
+            "half_life_steps": math.log(2) / -np.log(np.sqrt(1 - 1 / w))}

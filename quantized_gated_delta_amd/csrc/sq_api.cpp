@@ -56,8 +56,8 @@ sq_status check_desc(const sq_pool_desc *d) {
     if (!d->head_bits) return fail(SQ_EINVAL, "head_bits is NULL");
     for (int h = 0; h < d->n_heads; ++h) {
         const int b = d->head_bits[h];
-        if (b != 4 && b != 6 && b != 8)
-            return fail(SQ_EUNSUPPORTED, "head_bits[%d] = %d, must be 4, 6 or 8", h, b);
+        if (b != 4 && b != 6 && b != 8 && b != 16)
+            return fail(SQ_EUNSUPPORTED, "head_bits[%d] = %d, must be 4, 6, 8 or 16", h, b);
     }
     return SQ_OK;
 }

@@ -12,7 +12,7 @@ constexpr int kMaxHeads = 64;
 // Per-head record placement inside one slot of the pool.
 struct HeadTable {
     int64_t off[kMaxHeads];  // byte offset of head h's record within a slot
-    uint8_t bits[kMaxHeads]; // 4, 6 or 8
+    uint8_t bits[kMaxHeads]; // 4, 6, 8, or 16 (FP16 pivot)
 };
 
 struct PoolView {
@@ -32,8 +32,10 @@ struct StepIO {
     int32_t kda;
 };
 
-// Bytes of one record: d rows of d * bits / 8 code bytes, then r[d], c[d] fp32.
+// Bytes of one record: d rows of d * bits / 8 code bytes, then r[d], c[d]
+// fp32; bits = 16 is an FP16 pivot record (the state as binary16, no scales).
 inline int64_t record_bytes(int bits, int d) {
+    if (bits == 16) return 2 * (int64_t)d * d;
     return (int64_t)d * d * bits / 8 + 8 * (int64_t)d;
 }
 

@@ -333,6 +333,66 @@ __device__ __forceinline__ void quant_tile(uint8_t *rec, const float *S, float *
     quantize_rows_store<D, BITS>(x, ic, rec);
 }
 
+// ---------------------------------------------------------------- FP16 pivot records
+// bits = 16: the record is the state itself as IEEE binary16, row-major, no
+// scales (the highest-risk heads kept in FP16 as pivots).  Conversions are
+// round-to-nearest-even (v_cvt_f16_f32) and exact widening (v_cvt_f32_f16).
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+    const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ float half_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)w); }
+__device__ __forceinline__ float half_hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ float half_at(const uint32_t (&w)[8], int n) {
+    return (n & 1) ? half_hi(w[n >> 1]) : half_lo(w[n >> 1]);
+}
+
+template <int D>
+__device__ __forceinline__ void load_half16(const uint8_t *rec, int row, int cg, uint32_t (&w)[8]) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(rec + 2 * (row * D + 16 * cg));
+    const uint4 a = p[0], b = p[1];
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+template <int D>
+__device__ __forceinline__ void store_half16(uint8_t *rec, int row, int cg, const float (&v)[16]) {
+    uint4 *p = reinterpret_cast<uint4 *>(rec + 2 * (row * D + 16 * cg));
+    p[0] = make_uint4(pack_half2(v[0], v[1]), pack_half2(v[2], v[3]), pack_half2(v[4], v[5]),
+                      pack_half2(v[6], v[7]));
+    p[1] = make_uint4(pack_half2(v[8], v[9]), pack_half2(v[10], v[11]), pack_half2(v[12], v[13]),
+                      pack_half2(v[14], v[15]));
+}
+
+template <int D> __device__ __forceinline__ void quant_tile_f16(uint8_t *rec, const float *S) {
+    using G = Geo<D>;
+    const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        float v[16];
+        load16<D>(S + (band + G::NB * m) * D + 16 * cg, v);
+        store_half16<D>(rec, band + G::NB * m, cg, v);
+    }
+}
+
+template <int D> __device__ __forceinline__ void dequant_tile_f16(const uint8_t *rec, float *S) {
+    using G = Geo<D>;
+    const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int row = band + G::NB * m;
+        uint32_t w[8];
+        load_half16<D>(rec, row, cg, w);
+        float4 *dst = reinterpret_cast<float4 *>(S + row * D + 16 * cg);
+#pragma unroll
+        for (int n4 = 0; n4 < 4; ++n4)
+            dst[n4] = make_float4(half_at(w, 4 * n4), half_at(w, 4 * n4 + 1), half_at(w, 4 * n4 + 2),
+                                  half_at(w, 4 * n4 + 3));
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(Geo<D>::NT) void quant_state_kernel(PoolView pool, HeadTable tab,
                                                                  const int32_t *slot,
@@ -345,6 +405,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void quant_state_kernel(PoolView pool, 
     switch (tab.bits[h]) {
     case 4: quant_tile<D, 4>(rec, src, lds); break;
     case 6: quant_tile<D, 6>(rec, src, lds); break;
+    case 16: quant_tile_f16<D>(rec, src); break;
     default: quant_tile<D, 8>(rec, src, lds); break;
     }
 }
@@ -396,6 +457,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void dequant_state_kernel(PoolView pool
     switch (tab.bits[h]) {
     case 4: dequant_tile<D, 4>(rec, dst); break;
     case 6: dequant_tile<D, 6>(rec, dst); break;
+    case 16: dequant_tile_f16<D>(rec, dst); break;
     default: dequant_tile<D, 8>(rec, dst); break;
     }
 }
@@ -592,6 +654,125 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     quantize_rows_store<D, BITS>(x, ic, rec);
 }
 
+// FP16 pivot record: the same FP64 look-up and update on the exactly
+// widened state, S' rounded once to fp32 (read-out) and then to binary16.
+template <int D, bool KDA, typename TI, typename TO>
+__device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const StepIO &io,
+                                                float *lds) {
+    using G = Geo<D>;
+    constexpr int PLANE = G::NB * D;
+    const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
+    double *part64 = reinterpret_cast<double *>(lds);
+    float *plane_y = lds + PLANE;
+    double2 *lds_cu = reinterpret_cast<double2 *>(lds + DecodeLds<D>::PART_F);
+    float *lds_misc = lds + DecodeLds<D>::PART_F + 5 * D;
+    const int64_t row_io = tile;
+    const TI *k = reinterpret_cast<const TI *>(io.k) + row_io * D;
+    const TI *q = reinterpret_cast<const TI *>(io.q) + row_io * D;
+    const TI *g = reinterpret_cast<const TI *>(io.g);
+
+    float kf[4], qf[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int row = band + G::NB * m;
+        kf[m] = ld<TI>(k, row);
+        qf[m] = ld<TI>(q, row);
+    }
+    const float beta = ld<TI>(reinterpret_cast<const TI *>(io.beta), row_io);
+    float vj = 0.0f;
+    if (t < D) vj = ld<TI>(reinterpret_cast<const TI *>(io.v) + row_io * D, t);
+    float am[4];
+    if constexpr (KDA) {
+        const float a = gate_factor(ld<TI>(g, row_io * D + band + G::NB * (cg & 3)));
+        am[0] = band_bcast<G::CG, 0>(a);
+        am[1] = band_bcast<G::CG, 1>(a);
+        am[2] = band_bcast<G::CG, 2>(a);
+        am[3] = band_bcast<G::CG, 3>(a);
+    } else {
+        if (t == 0) lds_misc[0] = gate_factor(ld<TI>(g, row_io));
+    }
+    {
+        uint32_t w[4][8];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) load_half16<D>(rec, band + G::NB * m, cg, w[m]);
+        double ka[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) ka[m] = KDA ? (double)kf[m] * (double)am[m] : (double)kf[m];
+#pragma unroll
+        for (int n2 = 0; n2 < 8; ++n2) {
+            double acc0 = 0.0, acc1 = 0.0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                acc0 = fma(ka[m], (double)half_lo(w[m][n2]), acc0);
+                acc1 = fma(ka[m], (double)half_hi(w[m][n2]), acc1);
+            }
+            *reinterpret_cast<double2 *>(part64 + part_idx<D>(band, cg, 2 * n2)) =
+                make_double2(acc0, acc1);
+        }
+    }
+    __syncthreads();
+    if constexpr (!KDA) {
+        const float a = lds_misc[0];
+        am[0] = am[1] = am[2] = am[3] = a;
+    }
+    if (t < D) {
+        double P = 0.0;
+#pragma unroll 8
+        for (int b = 0; b < G::NB; ++b) P += part64[part_idx<D>(b, t >> 4, t & 15)];
+        if constexpr (!KDA) P *= (double)am[0];
+        lds_cu[colvec2_idx(t)] = make_double2(1.0, (double)beta * ((double)vj - P));
+    }
+    __syncthreads();
+    {
+        // each lane reads and writes only its own 4 x 16 elements, so the row
+        // segments are loaded again here (after the barriers) rather than
+        // held in registers across them
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const double a = (double)am[m], kk = (double)kf[m];
+            uint32_t wm[8];
+            load_half16<D>(rec, band + G::NB * m, cg, wm);
+            float o[16];
+#pragma unroll
+            for (int n = 0; n < 16; ++n) {
+                const double un = lds_cu[colvec2_idx(16 * cg + n)].y;
+                o[n] = (float)fma(a, (double)half_at(wm, n), kk * un);
+                // S' is rounded to fp32 first and binary16 second; the empty
+                // asm keeps the compiler from merging the two roundings into
+                // one double -> half conversion (which differs on near-ties)
+                asm volatile("" : "+v"(o[n]));
+            }
+            store_half16<D>(rec, band + G::NB * m, cg, o);
+            float ypart[16];
+#pragma unroll
+            for (int n = 0; n < 16; ++n) ypart[n] = qf[m] * o[n];
+            if (m == 0) {
+#pragma unroll
+                for (int n4 = 0; n4 < 4; ++n4)
+                    *reinterpret_cast<float4 *>(plane_y + plane_idx<D>(band, cg, 4 * n4)) =
+                        make_float4(ypart[4 * n4], ypart[4 * n4 + 1], ypart[4 * n4 + 2],
+                                    ypart[4 * n4 + 3]);
+            } else {
+#pragma unroll
+                for (int n4 = 0; n4 < 4; ++n4) {
+                    float4 *pp = reinterpret_cast<float4 *>(plane_y + plane_idx<D>(band, cg, 4 * n4));
+                    float4 f = *pp;
+                    f.x += ypart[4 * n4]; f.y += ypart[4 * n4 + 1];
+                    f.z += ypart[4 * n4 + 2]; f.w += ypart[4 * n4 + 3];
+                    *pp = f;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (t < D) {
+        float yv = 0.0f;
+#pragma unroll 8
+        for (int b = 0; b < G::NB; ++b) yv += plane_y[plane_idx<D>(b, t >> 4, t & 15)];
+        st<TO>(reinterpret_cast<TO *>(io.y) + row_io * D, t, yv);
+    }
+}
+
 #ifndef SQ_DECODE_WAVES_PER_EU
 #define SQ_DECODE_WAVES_PER_EU 4
 #endif
@@ -609,6 +790,7 @@ void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
     switch (tab.bits[h]) {
     case 4: decode_tile<D, 4, KDA, TI, TO>(rec, tile, io, lds); break;
     case 6: decode_tile<D, 6, KDA, TI, TO>(rec, tile, io, lds); break;
+    case 16: decode_tile_f16<D, KDA, TI, TO>(rec, tile, io, lds); break;
     default: decode_tile<D, 8, KDA, TI, TO>(rec, tile, io, lds); break;
     }
 }

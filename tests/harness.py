@@ -13,6 +13,8 @@ import workload as W
 
 # ----------------------------------------------------------------- format
 def record_bytes(bits: int, d: int) -> int:
+    if bits == 16:  # FP16 pivot record: the state as binary16, no scales
+        return 2 * d * d
     return d * d * bits // 8 + 8 * d
 
 
@@ -26,7 +28,10 @@ def layout(head_bits, d):
 
 
 def unpack_codes(bits: int, d: int, rec: np.ndarray) -> np.ndarray:
-    """Codes [d, d] of one record, decoded with numpy bit arithmetic."""
+    """Codes [d, d] of one record, decoded with numpy bit arithmetic (for an
+    FP16 pivot record: the binary16 bit patterns)."""
+    if bits == 16:
+        return rec[: 2 * d * d].view(np.uint16).reshape(d, d).astype(np.int32)
     rb = d * bits // 8
     raw = rec[: d * rb].reshape(d, rb)
     if bits == 8:
@@ -44,6 +49,8 @@ def unpack_codes(bits: int, d: int, rec: np.ndarray) -> np.ndarray:
 
 
 def record_scales(bits: int, d: int, rec: np.ndarray):
+    if bits == 16:
+        return ()
     rb = d * bits // 8
     sc = rec[d * rb: d * rb + 8 * d].view(np.float32)
     return sc[:d].copy(), sc[d:].copy()

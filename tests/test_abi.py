@@ -28,15 +28,21 @@ def test_library_exports_every_declared_symbol():
     assert "gfx950" in Q.version()
 
 
+def _rec(b, d):
+    # FP16 pivot records hold the binary16 state and no scales
+    return 2 * d * d if b == 16 else d * d * b // 8 + 8 * d
+
+
 def _layout(bits, d):
     offs, pos = [], 0
     for b in bits:
         offs.append(pos)
-        pos += d * d * b // 8 + 8 * d
+        pos += _rec(b, d)
     return pos, offs
 
 
-@pytest.mark.parametrize("d,bits", [(128, [6] * 48), (128, [4, 6, 8, 6]), (64, [8, 4, 6])])
+@pytest.mark.parametrize("d,bits", [(128, [6] * 48), (128, [4, 6, 8, 6]), (64, [8, 4, 6]),
+                                    (128, [16, 6, 4]), (64, [4, 16, 8, 16])])
 def test_pool_bytes_and_layout(d, bits):
     stride, offs = _layout(bits, d)
     assert Q.sq_pool_bytes(640, len(bits), d, d, bits, Q.SQ_GATE_GDN) == 640 * stride
@@ -44,7 +50,7 @@ def test_pool_bytes_and_layout(d, bits):
     try:
         st, ho, rb = Q.sq_pool_layout(h, len(bits))
         assert st == stride and ho == offs
-        assert rb == [d * d * b // 8 + 8 * d for b in bits]
+        assert rb == [_rec(b, d) for b in bits]
         assert all(o % 256 == 0 for o in ho) and st % 256 == 0
     finally:
         Q.sq_pool_destroy(h)
@@ -61,6 +67,8 @@ def _expect(status, fn, *args, text=None):
 
 def test_descriptor_validation():
     _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_bytes, 4, 2, 128, 128, [6, 3], 0, text="head_bits[1]")
+    _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_bytes, 4, 2, 128, 128, [16, 12], 0, text="head_bits[1]")
+    _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_bytes, 4, 1, 128, 128, [32], 0, text="head_bits[0]")
     _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_bytes, 4, 1, 96, 96, [6], 0, text="64 or 128")
     _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_bytes, 4, 1, 128, 64, [6], 0, text="d_k must equal")
     _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_bytes, 4, 65, 128, 128, [6] * 65, 0, text="n_heads")

@@ -1,0 +1,73 @@
+"""Lifetime-aware bit allocation with FP16 pivots (host logic, no GPU)."""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+from quantized_gated_delta_amd import allocate as A
+
+
+def test_lifetime_weights_closed_form():
+    rho = np.array([0.5, 0.9, 0.99])
+    w = A.lifetime_weights(np.log(rho))
+    assert np.allclose(w, 1 / (1 - rho ** 2))
+    assert np.all(np.diff(w) > 0)
+    # a geometric series of squared retention: sum_j rho^(2j)
+    assert math.isclose(w[1], sum(0.81 ** j for j in range(4000)), rel_tol=1e-9)
+
+
+def test_mean_log_retention_axes():
+    g = -np.arange(2 * 3 * 4, dtype=np.float64).reshape(2, 3, 4)
+    assert np.allclose(A.mean_log_retention(g), g.mean(axis=(0, 2)))
+    assert np.allclose(A.mean_log_retention(g[:, :, 0]), g[:, :, 0].mean(axis=0))
+
+
+def _objective(D, w, bits, cand):
+    idx = [cand.index(b) for b in bits]
+    return float(sum(w[h] * D[h, i] for h, i in enumerate(idx)))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_greedy_matches_brute_force(seed):
+    """With distortion falling geometrically in the width (convex), the
+    greedy allocation equals the exhaustive optimum under the budget."""
+    rng = np.random.default_rng(seed)
+    H, cand = 6, [4, 6, 8]
+    base = np.exp(rng.normal(0, 1, H))
+    D = np.stack([base * 4.0 ** (-(b - 4) / 2 * rng.uniform(0.8, 1.2)) for b in cand], 1)
+    w = A.lifetime_weights(-rng.uniform(0.001, 0.5, H))
+    avg = rng.choice([4.0, 5.0, 6.0, 7.0, 8.0])
+    bits = A.allocate_bits(D, w, avg, cand)
+    assert bits.mean() <= avg + 1e-9
+    best = min((_objective(D, w, c, cand), c) for c in itertools.product(cand, repeat=H)
+               if np.mean(c) <= avg + 1e-9)
+    assert math.isclose(_objective(D, w, bits.tolist(), cand), best[0], rel_tol=1e-12)
+
+
+def test_longer_lifetime_gets_at_least_as_many_bits():
+    D = np.tile([1.0, 0.25, 0.0625], (8, 1))
+    w = A.lifetime_weights(-np.linspace(0.5, 0.002, 8))   # increasing lifetime
+    bits = A.allocate_bits(D, w, 6.0)
+    assert np.all(np.diff(bits.astype(int)) >= 0)
+    assert bits.mean() <= 6.0
+
+
+def test_pivots_are_the_highest_risk_heads():
+    rng = np.random.default_rng(3)
+    H = 10
+    D = np.stack([np.exp(rng.normal(0, 1, H)) * s for s in (1, 0.25, 0.0625)], 1)
+    w = A.lifetime_weights(-rng.uniform(0.001, 0.5, H))
+    bits = A.allocate_bits(D, w, 6.0, n_pivots=2)
+    risk = w * D[:, 0]
+    assert set(np.nonzero(bits == 16)[0]) == set(np.argsort(-risk)[:2])
+    assert bits[bits != 16].mean() <= 6.0
+
+
+def test_budget_edges():
+    D = np.tile([1.0, 0.5, 0.25], (4, 1))
+    w = np.ones(4)
+    assert (A.allocate_bits(D, w, 4.0) == 4).all()
+    assert (A.allocate_bits(D, w, 8.0) == 8).all()
+    with pytest.raises(ValueError):
+        A.allocate_bits(D, w, 3.0)

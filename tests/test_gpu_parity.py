@@ -135,6 +135,9 @@ def check_records(side: Side, rows, pool_gpu: np.ndarray, label=""):
         n = Hn.record_bytes(bits, d)
         rg, rr = pool_gpu[o:o + n], side.host.bytes[o:o + n]
         qg, qr = Hn.unpack_codes(bits, d, rg), Hn.unpack_codes(bits, d, rr)
+        if bits == 16:  # FP16 pivot: the binary16 values must match exactly
+            assert np.array_equal(qg, qr), "%s: fp16 record differs, row %d head %d" % (label, b, h)
+            continue
         mx, _ = Hn.compare_codes(qg, qr)
         worst = max(worst, mx)
         flips += int((qg != qr).sum())
@@ -161,7 +164,7 @@ def test_quant_dequant_bit_exact(d):
     log("G1 quant/dequant d=%d" % d)
     rng = np.random.default_rng(d)
     H = 6
-    bits = [4, 6, 8, 8, 6, 4]
+    bits = [4, 6, 8, 16, 6, 4]
     n_slots, B = 7, 5
     wl = W.custom("gdn", B, H, d, bits, n_slots=n_slots, permute=True, seed=3)
     side = Side(wl, wl.layers[0])
@@ -175,6 +178,8 @@ def test_quant_dequant_bit_exact(d):
     S[3, 4] *= np.float32(1e30)                   # huge state
     S[4, 5, :, 9] = 1e-40                         # column of subnormals only
     S[4, 5, 11, :] *= np.float32(1e-30)           # row far below its columns
+    S[1, 3] *= np.float32(1e-6)                   # FP16 pivot head: subnormal halves
+    S[0, 3] *= np.float32(3e4)                    # FP16 pivot head: overflow to inf
     Sd = to_dev(S)
     side.gpu.quant_state(side.slot_dev, Sd)
     rows = Hn.rows_all(B, H)
@@ -195,6 +200,8 @@ def test_quant_dequant_bit_exact(d):
 @pytest.mark.parametrize("case", [
     ("gdn", 5, 3, 64, [4, 6, 8], "f32", 9),
     ("kda", 3, 5, 128, [6, 4, 8, 6, 6], "bf16", 4),
+    ("gdn", 4, 4, 128, [16, 6, 4, 8], "bf16", 6),
+    ("kda", 3, 3, 64, [8, 16, 4], "f32", 3),
     ("gdn", 4, 4, 128, [8, 6, 4, 6], "bf16", 11),
     ("kda", 2, 3, 64, [4, 8, 6], "f32", 2),
 ])

@@ -534,3 +534,51 @@ def test_oracle_thread_count_independent(monkeypatch):
                            x["g"])
         outs.append((base, y))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+# ------------------------------------------------------------------ FP16 pivot records
+def test_f16_conversions_match_numpy():
+    """binary16 <-> binary32 against numpy's float16 (an independent
+    implementation): every half value, and floats at and around every half
+    value, halfway points, overflow and subnormal boundaries."""
+    h = np.arange(65536, dtype=np.uint16)
+    ref = h.view(np.float16).astype(np.float32)
+    got = np.array([O.f16_to_f32(int(x)) for x in h], np.float32)
+    same = (ref.view(np.uint32) == got.view(np.uint32)) | (np.isnan(ref) & np.isnan(got))
+    assert same.all()
+    fin = ref[np.isfinite(ref)].astype(np.float64)
+    rng = np.random.default_rng(80)
+    xs = np.concatenate([
+        (rng.standard_normal(50000) * np.exp(rng.uniform(-20, 12, 50000))),
+        fin, fin * (1 + 2.0 ** -11), fin * (1 - 2.0 ** -12), fin * (1 + 2.0 ** -12),
+        [65504, 65519.99, 65520, 65536, 1e9, 2.0 ** -25, 2.0 ** -24, 3 * 2.0 ** -25,
+         2.0 ** -14 * (1 - 2.0 ** -11), 1e-45, 0.0, -0.0]]).astype(np.float32)
+    with np.errstate(over="ignore"):
+        want = xs.astype(np.float16).view(np.uint16)
+    got = np.array([O.f32_to_f16(float(x)) for x in xs], np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_f16_record_step():
+    """A pivot record holds the state in binary16; one step is the FP64 step
+    on the widened state, rounded once to fp32 and then to binary16."""
+    rng = np.random.default_rng(81)
+    d = 32
+    S = (rng.standard_normal((d, d)) * 3).astype(np.float32)
+    rec = np.zeros(O.record_bytes(16, d, d), np.uint8)
+    assert rec.size == 2 * d * d
+    O.records_quantize(rec, np.array([0], np.int64), np.array([16], np.uint8), S[None], d, d)
+    assert np.array_equal(rec.view(np.uint16), S.astype(np.float16).view(np.uint16).ravel())
+    S16 = O.records_dequantize(rec, np.array([0]), np.array([16], np.uint8), d, d)[0]
+    assert np.array_equal(S16, S.astype(np.float16).astype(np.float32))
+    q, k, v, beta, _ = _inputs(rng, d, d)
+    g = np.array([-0.1], np.float32)
+    y = O.records_step(False, rec, np.array([0], np.int64), np.array([16], np.uint8), d, d,
+                       q[None].astype(np.float32), k[None].astype(np.float32),
+                       v[None].astype(np.float32), np.array([beta], np.float32), g)
+    alpha = np.full(d, float(np.float32(math.exp(-0.1))))
+    want, yw = O.gated_delta_f64(S16.astype(np.float64), alpha, q.astype(np.float32),
+                                 k.astype(np.float32), v.astype(np.float32), np.float32(beta))
+    assert np.array_equal(rec.view(np.uint16),
+                          want.astype(np.float32).astype(np.float16).view(np.uint16).ravel())
+    assert np.array_equal(y[0], yw)
