@@ -71,6 +71,12 @@ def main():
                     help="only the c4 trajectory: GDN + KDA layers, per-step y error of the "
                          "quantized step against the fp32-state step")
     ap.add_argument("--traj-steps", type=int, default=1024)
+    ap.add_argument("--allocate", action="store_true",
+                    help="with --trajectory: also run uniform-6 and lifetime-aware pools")
+    ap.add_argument("--pivots", type=int, default=2,
+                    help="FP16 pivot heads per layer for the --allocate comparison")
+    ap.add_argument("--calib", type=int, default=256,
+                    help="requests whose warm-up states calibrate the allocation")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -295,12 +301,20 @@ def trajectory(args, dev):
     Both the packed pool and an fp32 state pool start from the same fp32
     warm-up state and see identical bf16 inputs; y of the quantized step is
     compared with y of the fp32-state step at every step (relative L2 over
-    the whole [B, H, d] output)."""
+    the whole [B, H, d] output).
+
+    With --allocate the same trajectory also runs, side by side, pools whose
+    per-head widths come from other rules at the same 6-bit average: uniform
+    6 bits, the lifetime-aware allocation (calibrated on the warm-up states
+    of the first --calib requests and the warm-up log-gates), and that
+    allocation plus --pivots FP16 pivot heads outside the budget, and the
+    same with the pivots' 16 bits counted inside the 6-bit average."""
     import numpy as np
     import torch
 
     import quantized_gated_delta_amd as Q
     import workload as W
+    from quantized_gated_delta_amd import allocate as A
 
     def to_dev(a):
         return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -313,39 +327,71 @@ def trajectory(args, dev):
         kda = layer.gate == "kda"
         state = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
         yw = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+        gsum = []
         for t in range(-W.WARMUP_STEPS, 0):
-            x = {k: to_dev(v) for k, v in wl.step_inputs(layer, t).items()}
+            xh = wl.step_inputs(layer, t)
+            gsum.append(W.to_f32(xh["g"]).reshape((B, H, d) if kda else (B, H)).mean(axis=0))
+            x = {k: to_dev(v) for k, v in xh.items()}
             Q.sq_f32_decode_step(state, B, H, d, d, int(kda), ident, B, x["q"], x["k"], x["v"],
                                  x["beta"], x["g"], yw)
-        pool = Q.StatePool(B, H, d, layer.head_bits.tolist(), layer.gate, device=dev)
-        pool.quant_state(ident, state)
-        layers.append((layer, kda, state, pool))
+        schemes = {"fixed_c4_mix": layer.head_bits.astype(np.uint8)}
+        cal = None
+        if args.allocate:
+            cal = A.calibrate(state[:args.calib], np.stack(gsum), avg_bits=6.0, n_pivots=0)
+            schemes["uniform_6"] = np.full(H, 6, np.uint8)
+            schemes["lifetime_6"] = cal["bits"]
+            schemes["lifetime_6+%d_fp16_pivots" % args.pivots] = A.allocate_bits(
+                cal["distortion"], cal["weights"], 6.0, n_pivots=args.pivots)
+            schemes["lifetime_6_incl_%d_fp16_pivots" % args.pivots] = A.allocate_bits(
+                cal["distortion"], cal["weights"], 6.0, n_pivots=args.pivots,
+                pivots_in_budget=True)
+        pools = {}
+        for name, hb in schemes.items():
+            pool = Q.StatePool(B, H, d, [int(b) for b in hb], layer.gate, device=dev)
+            pool.quant_state(ident, state)
+            pools[name] = pool
+        layers.append((layer, kda, state, pools, schemes, cal))
     torch.cuda.synchronize()
-    errs = {l.index: [] for l, _, _, _ in layers}
+    errs = {(l.index, n): [] for l, _, _, pools, _, _ in layers for n in pools}
     yq = torch.empty((B * H, d), dtype=torch.bfloat16, device=dev)
     yf = torch.empty((B * H, d), dtype=torch.bfloat16, device=dev)
     t0 = time.time()
     for t in range(T):
-        for layer, kda, state, pool in layers:
+        for layer, kda, state, pools, _, _ in layers:
             x = {k: to_dev(v) for k, v in wl.step_inputs(layer, t).items()}
-            pool.decode_step(ident, x["q"], x["k"], x["v"], x["beta"], x["g"], yq)
             Q.sq_f32_decode_step(state, B, H, d, d, int(kda), ident, B, x["q"], x["k"], x["v"],
                                  x["beta"], x["g"], yf)
-            a = yq.float()
             b = yf.float()
-            errs[layer.index].append(float(torch.linalg.vector_norm(a - b)
-                                           / torch.linalg.vector_norm(b)))
-        if t in (0, 15, 63, 255, T - 1):
-            eprint("step %d: %s (%.0f s)" % (t + 1, {k: round(v[-1], 4) for k, v in errs.items()},
+            nb = torch.linalg.vector_norm(b)
+            for name, pool in pools.items():
+                pool.decode_step(ident, x["q"], x["k"], x["v"], x["beta"], x["g"], yq)
+                errs[(layer.index, name)].append(
+                    float(torch.linalg.vector_norm(yq.float() - b) / nb))
+        if t in (0, 15, 63, 255, T - 1) or (t + 1) % 64 == 0:
+            eprint("step %d: %s (%.0f s)" % (t + 1, {"%d/%s" % k: round(v[-1], 4)
+                                                     for k, v in errs.items()},
                                             time.time() - t0))
-    out = {"workload": "c4: GDN + KDA layers, B=1024, H=32, d=128, bits 4/6/8, bf16, %d steps" % T,
+    out = {"workload": "c4: GDN + KDA layers, B=1024, H=32, d=128, bf16, %d steps" % T,
            "y_rel_l2_vs_fp32_state": {}}
-    for layer, _, _, _ in layers:
-        e = np.array(errs[layer.index])
-        marks = {str(s): float(e[s - 1]) for s in (1, 16, 64, 256, T) if s <= T}
-        out["y_rel_l2_vs_fp32_state"][layer.gate] = {
-            "bits": {str(b): int((layer.head_bits == b).sum()) for b in (4, 6, 8)},
-            "at_step": marks, "mean": float(e.mean()), "max": float(e.max())}
+    for layer, _, _, pools, schemes, cal in layers:
+        per = {}
+        for name, pool in pools.items():
+            hb = schemes[name]
+            e = np.array(errs[(layer.index, name)])
+            marks = {str(s): float(e[s - 1]) for s in (1, 16, 64, 256, T) if s <= T}
+            per[name] = {"bits": {str(b): int((hb == b).sum()) for b in (4, 6, 8, 16)
+                                  if (hb == b).any()},
+                         "slot_bytes": int(pool.slot_stride),
+                         "at_step": marks, "mean": float(e.mean()), "max": float(e.max())}
+        entry = per if args.allocate else per["fixed_c4_mix"]
+        if cal is not None:
+            entry = {"schemes": per,
+                     "calibration": {"requests": int(args.calib),
+                                     "half_life_steps": [round(float(x), 2)
+                                                         for x in cal["half_life_steps"]],
+                                     "nmse_4_6_8": [[float("%.3g" % v) for v in row]
+                                                    for row in cal["distortion"]]}}
+        out["y_rel_l2_vs_fp32_state"][layer.gate] = entry
     print(json.dumps(out), flush=True)
 
 

@@ -10,11 +10,13 @@ and keeps the highest-risk units in FP16 as sparse pivots.  This runs
 offline: the decode step only reads the resulting per-head bit table.
 
 Readings (the pages give the recipe in words, no formulas):
-  retention   rho_h = exp(mean log-gate of head h over the calibration steps
-              and, for KDA, its key channels)
-  lifetime    w_h = sum_j rho_h^(2 j) = 1 / (1 - rho_h^2): squared error
-              decays by rho^2 per step, so a unit of fresh squared error adds
-              up to w_h over its life
+  retention   rho = exp(mean log-gate over the calibration steps), per head
+              for GDN and per key row (channel) of each head for KDA, whose
+              decay acts row by row
+  lifetime    w = sum_j rho^(2 j) = 1 / (1 - rho^2): squared error decays by
+              rho^2 per step, so a unit of fresh squared error adds up to w
+              over its life; a KDA head's weight is the mean of its rows'
+              weights (its distortion is spread over the rows)
   distortion  D_h(b) = mean over calibration states of
               ||S - DQ_b(S)||^2 / ||S||^2 with the pool's own quantizer
               (measured with the GPU quant / dequant kernels)
@@ -38,6 +40,14 @@ def lifetime_weights(mean_log_retention) -> np.ndarray:
     return 1.0 / -np.expm1(2.0 * mlr)
 
 
+def head_lifetime_weights(log_gates) -> np.ndarray:
+    """Per head lifetime weight from log-gates [T, H] (GDN) or [T, H, d_k]
+    (KDA): the mean over key rows of each row's 1 / (1 - rho^2)."""
+    g = np.asarray(log_gates, np.float64)
+    w = lifetime_weights(g.mean(axis=0))
+    return w if w.ndim == 1 else w.mean(axis=1)
+
+
 def mean_log_retention(log_gates) -> np.ndarray:
     """Per head: mean of the log-gates over steps (and key channels for KDA).
     log_gates: [T, H] (GDN) or [T, H, d_k] (KDA), any float dtype."""
@@ -48,9 +58,11 @@ def mean_log_retention(log_gates) -> np.ndarray:
 
 def allocate_bits(distortion: np.ndarray, weights: np.ndarray, avg_bits: float,
                   candidates: Sequence[int] = (4, 6, 8), n_pivots: int = 0,
-                  pivot_bits: int = 16) -> np.ndarray:
+                  pivot_bits: int = 16, pivots_in_budget: bool = False) -> np.ndarray:
     """distortion: [H, len(candidates)] (non-increasing in the width);
-    weights: [H].  Returns the width per head (pivots get pivot_bits)."""
+    weights: [H].  Returns the width per head (pivots get pivot_bits).
+    The average is over the non-pivot heads, or over all heads with the
+    pivots' bits counted when pivots_in_budget."""
     D = np.asarray(distortion, np.float64)
     w = np.asarray(weights, np.float64)
     cand = list(candidates)
@@ -64,7 +76,8 @@ def allocate_bits(distortion: np.ndarray, weights: np.ndarray, avg_bits: float,
     pivots = np.argsort(-risk, kind="stable")[:n_pivots] if n_pivots > 0 else np.array([], int)
     free = np.setdiff1d(np.arange(H), pivots)
     level = np.zeros(H, np.int64)
-    budget = avg_bits * len(free) - cand[0] * len(free)
+    total = avg_bits * H - pivot_bits * len(pivots) if pivots_in_budget else avg_bits * len(free)
+    budget = total - cand[0] * len(free)
     if budget < -1e-9:
         raise ValueError("budget below the smallest width")
     while True:
@@ -114,7 +127,7 @@ def calibrate(states, log_gates, avg_bits: float = 6.0, candidates=(4, 6, 8),
     """Bits per head from calibration states [N, H, d, d] (device, fp32) and
     the log-gates seen over the calibration steps."""
     D = measure_distortion(states, candidates)
-    w = lifetime_weights(mean_log_retention(log_gates))
+    w = head_lifetime_weights(log_gates)
     bits = allocate_bits(D, w, avg_bits, candidates, n_pivots)
     return {"bits": bits, "distortion": D, "weights": w,
             "half_life_steps": math.log(2) / -np.log(np.sqrt(1 - 1 / w))}

@@ -23,6 +23,21 @@ def test_mean_log_retention_axes():
     assert np.allclose(A.mean_log_retention(g[:, :, 0]), g[:, :, 0].mean(axis=0))
 
 
+def test_head_lifetime_weights_gdn_and_kda():
+    rng = np.random.default_rng(7)
+    g = -rng.uniform(0.01, 1.0, (5, 3))                    # GDN [T, H]
+    rho = np.exp(g.mean(axis=0))
+    assert np.allclose(A.head_lifetime_weights(g), 1 / (1 - rho ** 2))
+    # KDA: one slow row dominates a head whose mean log-gate is fast
+    gk = np.full((4, 2, 8), -2.0)
+    gk[:, 1, 0] = -0.01
+    w = A.head_lifetime_weights(gk)
+    slow = 1 / (1 - np.exp(-0.02))
+    fast = 1 / (1 - np.exp(-4.0))
+    assert np.isclose(w[0], fast) and np.isclose(w[1], (slow + 7 * fast) / 8)
+    assert w[1] > A.lifetime_weights(A.mean_log_retention(gk))[1] * 5
+
+
 def _objective(D, w, bits, cand):
     idx = [cand.index(b) for b in bits]
     return float(sum(w[h] * D[h, i] for h, i in enumerate(idx)))
@@ -62,6 +77,15 @@ def test_pivots_are_the_highest_risk_heads():
     risk = w * D[:, 0]
     assert set(np.nonzero(bits == 16)[0]) == set(np.argsort(-risk)[:2])
     assert bits[bits != 16].mean() <= 6.0
+
+
+def test_pivots_inside_the_budget():
+    D = np.tile([1.0, 0.25, 0.0625], (8, 1))
+    w = np.arange(1.0, 9.0)
+    bits = A.allocate_bits(D, w, 6.0, n_pivots=1, pivots_in_budget=True)
+    assert bits[7] == 16
+    assert bits.astype(int).sum() <= 6 * 8
+    assert bits[:7].astype(int).sum() == 6 * 8 - 16
 
 
 def test_budget_edges():
