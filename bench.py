@@ -207,6 +207,8 @@ def main():
             "achieved_GBps": fb / (f_launch * 1e-3) / 1e9,
             "speedup_quantized_vs_fp32": f_ms / ms_step}
         eprint("fp32 state: %.2f us/step, %.1f GB/s" % (f_ms * 1e3, variants["fp32_state"]["achieved_GBps"]))
+        variants["split_epilogue"] = split_epilogue(pool, slot, steps_in, y, timed, ms_step,
+                                                    stream, dev, B, H, d, io_dt)
         # the mixed 4/8-bit variant (8-bit for heads whose half-life exceeds 64 steps)
         if args.workload == "c3a":
             wb = W.make("c3b")
@@ -294,6 +296,103 @@ def main():
         "variants": variants,
     }
     print(json.dumps(out), flush=True)
+
+
+def split_epilogue(pool, slot, steps_in, y, timed, fused_ms, stream, dev, B, H, d, io_dt):
+    """The pages' split design: the update kernel writes S' (fp32) and y, and
+    the requantization (sq_quant_state of S') runs on a second stream.
+    One layer: the next step's update of the same slots waits for the
+    epilogue.  Two layers (two pools of this shape): the epilogue of one
+    layer overlaps the update of the other.  Compared with the fused step."""
+    import torch
+
+    import quantized_gated_delta_amd as Q
+    epi = torch.cuda.Stream()
+    S_a = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    upd_done = [torch.cuda.Event(), torch.cuda.Event()]
+    epi_done = [torch.cuda.Event(), torch.cuda.Event()]
+
+    def split_one(pl, x, yy, S, i):
+        stream.wait_event(epi_done[i])
+        pl.decode_update(slot, x["q"], x["k"], x["v"], x["beta"], x["g"], yy, S)
+        upd_done[i].record(stream)
+        epi.wait_event(upd_done[i])
+        pl.quant_state(slot, S, stream=epi)
+        epi_done[i].record(epi)
+
+    def run_split(n, ev=None):
+        for i in range(n):
+            if ev is not None:
+                ev[i][0].record(stream)
+            split_one(pool, steps_in[i % 4], y, S_a, 0)
+            stream.wait_event(epi_done[0])
+            if ev is not None:
+                ev[i][1].record(stream)
+
+    def run_update_only(n, ev=None):
+        for i in range(n):
+            x = steps_in[i % 4]
+            if ev is not None:
+                ev[i][0].record(stream)
+            pool.decode_update(slot, x["q"], x["k"], x["v"], x["beta"], x["g"], y, S_a)
+            if ev is not None:
+                ev[i][1].record(stream)
+
+    def run_quant_only(n, ev=None):
+        for i in range(n):
+            if ev is not None:
+                ev[i][0].record(stream)
+            pool.quant_state(slot, S_a)
+            if ev is not None:
+                ev[i][1].record(stream)
+
+    s1_ms, _ = timed(None, None, run_split)
+    _, upd_launch = timed(None, None, run_update_only)
+    _, q_launch = timed(None, None, run_quant_only)
+    eprint("split, one layer: %.2f us/step (update %.1f + requantize %.1f us per launch); "
+           "fused %.2f" % (s1_ms * 1e3, upd_launch * 1e3, q_launch * 1e3, fused_ms * 1e3))
+
+    pool2 = Q.StatePool(pool.n_slots, H, d, pool.head_bits,
+                        "kda" if pool.gate == Q.SQ_GATE_KDA else "gdn", device=dev)
+    pool2.buf.copy_(pool.buf)
+    S_b = torch.empty_like(S_a)
+    y2 = torch.empty_like(y)
+
+    # (wall time per step is the figure here; the per-step events only mark
+    # the main stream)
+    def run_fused2(n, ev=None):
+        for i in range(n):
+            x = steps_in[i % 4]
+            if ev is not None:
+                ev[i][0].record(stream)
+            pool.decode_step(slot, x["q"], x["k"], x["v"], x["beta"], x["g"], y)
+            pool2.decode_step(slot, x["q"], x["k"], x["v"], x["beta"], x["g"], y2)
+            if ev is not None:
+                ev[i][1].record(stream)
+
+    def run_split2(n, ev=None):
+        for i in range(n):
+            x = steps_in[i % 4]
+            if ev is not None:
+                ev[i][0].record(stream)
+            split_one(pool, x, y, S_a, 0)
+            split_one(pool2, x, y2, S_b, 1)
+            if ev is not None:
+                ev[i][1].record(stream)
+        stream.wait_event(epi_done[0])
+        stream.wait_event(epi_done[1])
+
+    f2_ms, _ = timed(None, None, run_fused2)
+    s2_ms, _ = timed(None, None, run_split2)
+    eprint("two layers: fused %.2f us/step, split with overlapped epilogues %.2f us/step"
+           % (f2_ms * 1e3, s2_ms * 1e3))
+    pool2.close()
+    return {"one_layer_us_per_step": s1_ms * 1e3, "fused_one_layer_us_per_step": fused_ms * 1e3,
+            "update_kernel_us_per_launch": upd_launch * 1e3,
+            "requantize_kernel_us_per_launch": q_launch * 1e3,
+            "two_layers_fused_us_per_step": f2_ms * 1e3,
+            "two_layers_split_overlapped_us_per_step": s2_ms * 1e3,
+            "workspace_bytes_per_layer": B * H * d * d * 4}
 
 
 def trajectory(args, dev):

@@ -144,6 +144,22 @@ sq_status sq_decode_step(sq_pool *pool, const int32_t *slot_idx, int32_t n, cons
                          const void *k, const void *v, const void *beta, const void *g,
                          sq_dtype in_dtype, void *y, sq_dtype y_dtype, hipStream_t stream);
 
+/* First half of the split step (hyper.ai summary, "Method", last paragraph,
+ * and blog.ontle.kr: once the head output exists, scale fitting and packed
+ * write-back run on a separate stream).  Does what sq_decode_step does up to
+ * and including the read-out: y is written, and S' rounded to fp32 is written
+ * to S_out [n, H, d_k, d_v] (device, 16-byte aligned, request order like y);
+ * the pool is only read.  Calling sq_quant_state(pool, slot_idx, n, S_out, s2)
+ * afterwards (s2 may be another stream, ordered after this one by the caller,
+ * e.g. with an event) stores exactly the records sq_decode_step would have
+ * stored.  Until that call the listed slots still hold the previous state.
+ * Same argument conventions and errors as sq_decode_step; S_out NULL or
+ * misaligned gives SQ_EINVAL. */
+sq_status sq_decode_update(const sq_pool *pool, const int32_t *slot_idx, int32_t n, const void *q,
+                           const void *k, const void *v, const void *beta, const void *g,
+                           sq_dtype in_dtype, void *y, sq_dtype y_dtype, float *S_out,
+                           hipStream_t stream);
+
 /* The same step on an fp32 state pool state_pool [n_slots, H, d_k, d_v]
  * (the unquantized serving default), in place on the listed slots.
  * Same argument conventions as sq_decode_step. */

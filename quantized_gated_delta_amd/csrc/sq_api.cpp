@@ -202,8 +202,30 @@ sq_status sq_decode_step(sq_pool *pool, const int32_t *slot_idx, int32_t n, cons
     io.in_bf16 = in_dtype == SQ_BF16;
     io.y_bf16 = y_dtype == SQ_BF16;
     io.kda = pool->desc.gate == SQ_GATE_KDA;
+    io.s_out = nullptr;
     const hipError_t e = sqk::launch_decode(pool->view, pool->tab, io, stream);
     return e == hipSuccess ? SQ_OK : hip_fail(e, "decode_step launch");
+}
+
+sq_status sq_decode_update(const sq_pool *pool, const int32_t *slot_idx, int32_t n, const void *q,
+                           const void *k, const void *v, const void *beta, const void *g,
+                           sq_dtype in_dtype, void *y, sq_dtype y_dtype, float *S_out,
+                           hipStream_t stream) {
+    sq_status st = check_rows(pool, slot_idx, n);
+    if (st) return st;
+    if (n == 0) return SQ_OK;
+    if ((st = check_step_io(q, k, v, beta, g, in_dtype, y, y_dtype))) return st;
+    if ((st = check_io("S_out", S_out, true))) return st;
+    sqk::StepIO io;
+    io.slot = slot_idx;
+    io.q = q; io.k = k; io.v = v; io.beta = beta; io.g = g; io.y = y;
+    io.n = n;
+    io.in_bf16 = in_dtype == SQ_BF16;
+    io.y_bf16 = y_dtype == SQ_BF16;
+    io.kda = pool->desc.gate == SQ_GATE_KDA;
+    io.s_out = S_out;
+    const hipError_t e = sqk::launch_decode_update(pool->view, pool->tab, io, stream);
+    return e == hipSuccess ? SQ_OK : hip_fail(e, "decode_update launch");
 }
 
 sq_status sq_f32_decode_step(float *state_pool, int32_t n_slots, int32_t n_heads, int32_t d_k,

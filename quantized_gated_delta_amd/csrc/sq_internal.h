@@ -30,6 +30,7 @@ struct StepIO {
     int32_t n;
     int32_t in_bf16, y_bf16;
     int32_t kda;
+    float *s_out;   // split step only: S' as fp32 [n, H, d, d]
 };
 
 // Bytes of one record: d rows of d * bits / 8 code bytes, then r[d], c[d]
@@ -45,6 +46,9 @@ hipError_t launch_dequant_state(const PoolView &pool, const HeadTable &tab, cons
                                 int32_t n, float *S, hipStream_t stream);
 hipError_t launch_decode(const PoolView &pool, const HeadTable &tab, const StepIO &io,
                          hipStream_t stream);
+// The decode step without its requantization: S' (fp32) goes to io.s_out.
+hipError_t launch_decode_update(const PoolView &pool, const HeadTable &tab, const StepIO &io,
+                                hipStream_t stream);
 hipError_t launch_f32_decode(float *state, int64_t slot_stride_floats, int32_t n_heads, int32_t d,
                              const StepIO &io, hipStream_t stream);
 

@@ -530,7 +530,9 @@ template <int BITS> __device__ __forceinline__ Seg<BITS> seg_of(const TileIn &in
     return s;
 }
 
-template <int D, int BITS, bool KDA, typename TI, typename TO>
+// SPLIT: write S' (fp32) to io.s_out instead of requantizing; the record
+// is only read.  The requantization then runs as its own launch.
+template <int D, int BITS, bool KDA, bool SPLIT, typename TI, typename TO>
 __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const StepIO &io,
                                             float *lds) {
     using G = Geo<D>;
@@ -611,6 +613,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     // ---- decay + delta write in FP64, rounded once to fp32; read-out and
     //      column maxima partials in fp32
     float x[4][16];
+    float *s_out = SPLIT ? io.s_out + (int64_t)tile * D * D : nullptr;
     {
         double ar[4];
 #pragma unroll
@@ -636,8 +639,21 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
                 }
             }
             const int pi = plane_idx<D>(band, cg, 4 * n4);
-            *reinterpret_cast<float4 *>(plane_max + pi) = make_float4(cm[0], cm[1], cm[2], cm[3]);
+            if constexpr (!SPLIT)
+                *reinterpret_cast<float4 *>(plane_max + pi) = make_float4(cm[0], cm[1], cm[2], cm[3]);
             *reinterpret_cast<float4 *>(plane_y + pi) = make_float4(yp[0], yp[1], yp[2], yp[3]);
+        }
+    }
+    if constexpr (SPLIT) {
+        // each lane's 64 contiguous bytes of a row back to back (interleaving
+        // the rows per 16-byte chunk measured 1.8x slower on MI355X)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            float4 *dst = reinterpret_cast<float4 *>(s_out + (band + G::NB * m) * D + 16 * cg);
+#pragma unroll
+            for (int n4 = 0; n4 < 4; ++n4)
+                dst[n4] = make_float4(x[m][4 * n4], x[m][4 * n4 + 1], x[m][4 * n4 + 2],
+                                      x[m][4 * n4 + 3]);
         }
     }
     __syncthreads();
@@ -646,8 +662,9 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
 #pragma unroll 8
         for (int b = 0; b < G::NB; ++b) yv += plane_y[plane_idx<D>(b, t >> 4, t & 15)];
         st<TO>(reinterpret_cast<TO *>(io.y) + row_io * D, t, yv);
-        lds_ic[colvec4_idx(t)] = column_scale(column_max<D>(plane_max, t), cp + t);
+        if constexpr (!SPLIT) lds_ic[colvec4_idx(t)] = column_scale(column_max<D>(plane_max, t), cp + t);
     }
+    if constexpr (SPLIT) return;
     __syncthreads();
     float ic[16];
     load_colvec16(lds_ic, cg, ic);
@@ -656,7 +673,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
 
 // FP16 pivot record: the same FP64 look-up and update on the exactly
 // widened state, S' rounded once to fp32 (read-out) and then to binary16.
-template <int D, bool KDA, typename TI, typename TO>
+template <int D, bool KDA, bool SPLIT, typename TI, typename TO>
 __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const StepIO &io,
                                                 float *lds) {
     using G = Geo<D>;
@@ -742,7 +759,15 @@ __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const St
                 // one double -> half conversion (which differs on near-ties)
                 asm volatile("" : "+v"(o[n]));
             }
-            store_half16<D>(rec, band + G::NB * m, cg, o);
+            if constexpr (SPLIT) {
+                float4 *dst = reinterpret_cast<float4 *>(io.s_out + (int64_t)tile * D * D +
+                                                         (band + G::NB * m) * D + 16 * cg);
+#pragma unroll
+                for (int n4 = 0; n4 < 4; ++n4)
+                    dst[n4] = make_float4(o[4 * n4], o[4 * n4 + 1], o[4 * n4 + 2], o[4 * n4 + 3]);
+            } else {
+                store_half16<D>(rec, band + G::NB * m, cg, o);
+            }
             float ypart[16];
 #pragma unroll
             for (int n = 0; n < 16; ++n) ypart[n] = qf[m] * o[n];
@@ -779,7 +804,7 @@ __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const St
 // One workgroup per (request, head) tile; four resident per CU (VGPRs and
 // LDS both sized for four 4-wave workgroups), which hides the barriers and
 // reduction phases of one tile behind the others.
-template <int D, bool KDA, typename TI, typename TO>
+template <int D, bool KDA, bool SPLIT, typename TI, typename TO>
 __global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(SQ_DECODE_WAVES_PER_EU)))
 void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
     __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D>::TOTAL];
@@ -788,10 +813,10 @@ void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
     const int b = tile / H, h = tile - b * H;
     uint8_t *rec = pool.base + (int64_t)io.slot[b] * pool.slot_stride + tab.off[h];
     switch (tab.bits[h]) {
-    case 4: decode_tile<D, 4, KDA, TI, TO>(rec, tile, io, lds); break;
-    case 6: decode_tile<D, 6, KDA, TI, TO>(rec, tile, io, lds); break;
-    case 16: decode_tile_f16<D, KDA, TI, TO>(rec, tile, io, lds); break;
-    default: decode_tile<D, 8, KDA, TI, TO>(rec, tile, io, lds); break;
+    case 4: decode_tile<D, 4, KDA, SPLIT, TI, TO>(rec, tile, io, lds); break;
+    case 6: decode_tile<D, 6, KDA, SPLIT, TI, TO>(rec, tile, io, lds); break;
+    case 16: decode_tile_f16<D, KDA, SPLIT, TI, TO>(rec, tile, io, lds); break;
+    default: decode_tile<D, 8, KDA, SPLIT, TI, TO>(rec, tile, io, lds); break;
     }
 }
 
@@ -896,19 +921,30 @@ __global__ __launch_bounds__(Geo<D>::NT) void f32_decode_kernel(float *state, in
 }
 
 // ---------------------------------------------------------------- dispatch
-template <int D, bool KDA>
+template <int D, bool KDA, bool SPLIT>
 hipError_t decode_dispatch(const PoolView &pool, const HeadTable &tab, const StepIO &io,
                            hipStream_t s) {
     const dim3 grid((unsigned)io.n * (unsigned)pool.n_heads), block(Geo<D>::NT);
     if (!io.in_bf16 && !io.y_bf16)
-        hipLaunchKernelGGL((decode_kernel<D, KDA, float, float>), grid, block, 0, s, pool, tab, io);
+        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, float, float>), grid, block, 0, s, pool, tab, io);
     else if (!io.in_bf16 && io.y_bf16)
-        hipLaunchKernelGGL((decode_kernel<D, KDA, float, uint16_t>), grid, block, 0, s, pool, tab, io);
+        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, float, uint16_t>), grid, block, 0, s, pool, tab, io);
     else if (io.in_bf16 && !io.y_bf16)
-        hipLaunchKernelGGL((decode_kernel<D, KDA, uint16_t, float>), grid, block, 0, s, pool, tab, io);
+        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, uint16_t, float>), grid, block, 0, s, pool, tab, io);
     else
-        hipLaunchKernelGGL((decode_kernel<D, KDA, uint16_t, uint16_t>), grid, block, 0, s, pool, tab, io);
+        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, uint16_t, uint16_t>), grid, block, 0, s, pool, tab,
+                           io);
     return hipGetLastError();
+}
+
+template <bool SPLIT>
+hipError_t decode_gate_dispatch(const PoolView &pool, const HeadTable &tab, const StepIO &io,
+                                hipStream_t stream) {
+    if (pool.d == 128)
+        return io.kda ? decode_dispatch<128, true, SPLIT>(pool, tab, io, stream)
+                      : decode_dispatch<128, false, SPLIT>(pool, tab, io, stream);
+    return io.kda ? decode_dispatch<64, true, SPLIT>(pool, tab, io, stream)
+                  : decode_dispatch<64, false, SPLIT>(pool, tab, io, stream);
 }
 
 template <int D, bool KDA>
@@ -949,11 +985,12 @@ hipError_t launch_dequant_state(const PoolView &pool, const HeadTable &tab, cons
 
 hipError_t launch_decode(const PoolView &pool, const HeadTable &tab, const StepIO &io,
                          hipStream_t stream) {
-    if (pool.d == 128)
-        return io.kda ? decode_dispatch<128, true>(pool, tab, io, stream)
-                      : decode_dispatch<128, false>(pool, tab, io, stream);
-    return io.kda ? decode_dispatch<64, true>(pool, tab, io, stream)
-                  : decode_dispatch<64, false>(pool, tab, io, stream);
+    return decode_gate_dispatch<false>(pool, tab, io, stream);
+}
+
+hipError_t launch_decode_update(const PoolView &pool, const HeadTable &tab, const StepIO &io,
+                                hipStream_t stream) {
+    return decode_gate_dispatch<true>(pool, tab, io, stream);
 }
 
 hipError_t launch_f32_decode(float *state, int64_t slot_stride_floats, int32_t n_heads, int32_t d,

@@ -67,6 +67,9 @@ def lib():
         L.sq_decode_step.restype = st
         L.sq_decode_step.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, ctypes.c_int, vp,
                                      ctypes.c_int, vp]
+        L.sq_decode_update.restype = st
+        L.sq_decode_update.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, ctypes.c_int, vp,
+                                       ctypes.c_int, vp, vp]
         L.sq_f32_decode_step.restype = st
         L.sq_f32_decode_step.argtypes = [vp, i32, i32, i32, i32, ctypes.c_int, vp, i32, vp, vp,
                                          vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp]
@@ -182,6 +185,15 @@ def sq_decode_step(handle, slot_idx, n: int, q, k, v, beta, g, y, in_dtype=None,
                                 _stream(stream)), "sq_decode_step")
 
 
+def sq_decode_update(handle, slot_idx, n: int, q, k, v, beta, g, y, S_out, in_dtype=None,
+                     y_dtype=None, stream=None) -> None:
+    in_dtype = _dtype_code(q) if in_dtype is None else in_dtype
+    y_dtype = _dtype_code(y) if y_dtype is None else y_dtype
+    _check(lib().sq_decode_update(handle, _ptr(slot_idx), int(n), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(beta), _ptr(g), in_dtype, _ptr(y), y_dtype, _ptr(S_out),
+                                  _stream(stream)), "sq_decode_update")
+
+
 def sq_f32_decode_step(state, n_slots, n_heads, d_k, d_v, gate, slot_idx, n, q, k, v, beta, g,
                        y, in_dtype=None, y_dtype=None, stream=None) -> None:
     in_dtype = _dtype_code(q) if in_dtype is None else in_dtype
@@ -230,6 +242,12 @@ class StatePool:
     def decode_step(self, slot_idx, q, k, v, beta, g, y, stream=None):
         sq_decode_step(self.handle, slot_idx, slot_idx.numel(), q, k, v, beta, g, y,
                        stream=stream)
+
+    def decode_update(self, slot_idx, q, k, v, beta, g, y, S_out, stream=None):
+        """Split step, first half: y and S' (fp32) out, pool unchanged; store
+        with quant_state(slot_idx, S_out) afterwards."""
+        sq_decode_update(self.handle, slot_idx, slot_idx.numel(), q, k, v, beta, g, y, S_out,
+                         stream=stream)
 
     def check_slots(self, slot_idx, stream=None):
         sq_check_slots(self.handle, slot_idx, slot_idx.numel(), stream)

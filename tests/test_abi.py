@@ -19,7 +19,8 @@ FAKE_DEV = 0x7F0000000000   # 256-byte aligned, never dereferenced on the host
 def test_library_exports_every_declared_symbol():
     names = Q.header_symbols()
     for must in ("sq_pool_bytes", "sq_pool_create", "sq_pool_destroy", "sq_pool_layout",
-                 "sq_quant_state", "sq_decode_step", "sq_dequant_state", "sq_f32_decode_step",
+                 "sq_quant_state", "sq_decode_step", "sq_decode_update", "sq_dequant_state",
+                 "sq_f32_decode_step",
                  "sq_check_slots", "sq_last_error", "sq_version"):
         assert must in names
     lib = Q.lib()
@@ -125,6 +126,18 @@ def test_step_validation_without_launch(pool):
     _expect(Q.SQ_EINVAL, Q.sq_dequant_state, pool, P, 2, P + 8, 0, text="S is not 16-byte")
     _expect(Q.SQ_EINVAL, Q.sq_decode_step, None, P, 2, P, P, P, P, P, P, 1, 1, 0,
             text="pool is NULL")
+
+
+def test_split_update_validation_without_launch(pool):
+    P = FAKE_DEV + 4096
+    io = (P, P, P, P, P, P)
+    Q.sq_decode_update(pool, None, 0, *io, None, in_dtype=1, y_dtype=1, stream=0)
+    _expect(Q.SQ_EINVAL, Q.sq_decode_update, pool, P, 2, *io, None, 1, 1, 0, text="S_out is NULL")
+    _expect(Q.SQ_EINVAL, Q.sq_decode_update, pool, P, 2, *io, P + 4, 1, 1, 0,
+            text="S_out is not 16-byte")
+    _expect(Q.SQ_EINVAL, Q.sq_decode_update, pool, P, 9, *io, P, 1, 1, 0, text="exceeds n_slots")
+    _expect(Q.SQ_EINVAL, Q.sq_decode_update, pool, P, 2, P, P, P, P, P, None, P, 1, 1, 0,
+            text="y is NULL")
 
 
 def test_f32_step_validation_without_launch():

@@ -230,6 +230,47 @@ def test_decode_step_small_full_compare(case):
         assert (pool[~used] == 0xA5).all()
 
 
+@pytest.mark.parametrize("case", [
+    ("gdn", 4, 5, 128, [6, 16, 4, 8, 6], "bf16", 6),
+    ("kda", 3, 3, 64, [8, 16, 4], "f32", 4),
+])
+def test_split_update_then_quant_matches_fused(case):
+    """The split step (sq_decode_update, then sq_quant_state of S' on a second
+    stream ordered by an event) stores byte-identical records and y to the
+    fused sq_decode_step, whose records match the oracle's."""
+    gate, B, H, d, bits, dtype, n_slots = case
+    log("split %s" % (case,))
+    wl = W.custom(gate, B, H, d, bits, dtype=dtype, n_slots=n_slots, permute=True, seed=8)
+    side = Side(wl, wl.layers[0])
+    side.gpu.buf.fill_(0xA5)
+    side.host.bytes[:] = 0xA5
+    rows = Hn.rows_all(B, H)
+    side.init_oracle_rows(rows)
+    split = Q.StatePool(wl.n_slots, H, d, bits, gate)
+    S_out = torch.full((B, H, d, d), float("nan"), dtype=torch.float32, device=DEV)
+    epi = torch.cuda.Stream()
+    ydt = torch.float32 if dtype == "f32" else torch.bfloat16
+    for t in range(3):
+        side.push_rows(rows)                         # both start from the oracle's bytes
+        split.buf.copy_(side.gpu.buf)
+        y_gpu, y_ref = side.step(t, rows)            # fused step + oracle
+        x = dev_inputs(wl.step_inputs(wl.layers[0], t))
+        y_s = torch.empty((B * H, d), dtype=ydt, device=DEV)
+        split.decode_update(side.slot_dev, x["q"], x["k"], x["v"], x["beta"], x["g"], y_s, S_out)
+        done = torch.cuda.Event()
+        done.record()
+        with torch.cuda.stream(epi):
+            epi.wait_event(done)
+            split.quant_state(side.slot_dev, S_out)
+        torch.cuda.current_stream().wait_stream(epi)
+        torch.cuda.synchronize()
+        assert torch.equal(split.buf, side.gpu.buf), "step %d: split records differ" % t
+        y_f = W.to_f32(from_dev(y_s)).astype(np.float64)
+        assert np.array_equal(y_f, y_gpu), "step %d: split y differs" % t
+        check_records(side, rows, side.gpu_pool(), "step %d" % t)
+        assert Hn.rel_l2(y_gpu, y_ref) <= Hn.Y_REL_L2, t
+
+
 def test_decode_zero_state_and_identity():
     """From an all-zero pool (scales 0), and the beta = 0 / gate = 1 identity."""
     log("G5 identity")
