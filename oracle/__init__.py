@@ -56,6 +56,8 @@ def lib():
         L.sqo_unpack_row.argtypes = [i32, i32, vp, vp]
         L.sqo_quantize.restype = None
         L.sqo_quantize.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+        L.sqo_quantize_kra.restype = None
+        L.sqo_quantize_kra.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
         L.sqo_reconstruct_f64.restype = None
         L.sqo_reconstruct_f64.argtypes = [i32, i32, vp, vp, vp, vp]
         L.sqo_dequantize.restype = None
@@ -64,18 +66,18 @@ def lib():
         L.sqo_gated_delta_f64.argtypes = [i32, i32, vp, vp, vp, vp, vp, ctypes.c_double, vp]
         L.sqo_quant_step_codes.restype = None
         L.sqo_quant_step_codes.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32,
-                                           vp, vp]
+                                           vp, vp, vp]
         L.sqo_record_unpack.restype = i32
         L.sqo_record_unpack.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.sqo_record_pack.restype = i32
         L.sqo_record_pack.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.sqo_records_quantize.restype = i32
-        L.sqo_records_quantize.argtypes = [i32, i32, i32, vp, vp, vp, vp, i32]
+        L.sqo_records_quantize.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, i32]
         L.sqo_records_dequantize.restype = i32
         L.sqo_records_dequantize.argtypes = [i32, i32, i32, vp, vp, vp, vp, i32]
         L.sqo_records_step.restype = i32
         L.sqo_records_step.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
-                                       vp, i32]
+                                       vp, vp, i32]
         L.sqo_f64_step.restype = i32
         L.sqo_f64_step.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32]
         L.sqo_f32_step.restype = i32
@@ -149,6 +151,20 @@ def quantize(bits: int, S) -> tuple:
     return Q, r, c
 
 
+def quantize_kra(bits: int, S, imp) -> tuple:
+    """Key-row-aware dual-axis fit with row-impact scores imp [dk] (> 0):
+    returns (Q int32, r f32 [dk], c f32 [dv])."""
+    S = _c(S, np.float32)
+    imp = _c(imp, np.float32)
+    dk, dv = S.shape
+    assert imp.shape == (dk,)
+    Q = np.empty((dk, dv), np.int32)
+    r = np.empty(dk, np.float32)
+    c = np.empty(dv, np.float32)
+    lib().sqo_quantize_kra(bits, dk, dv, _p(S), _p(imp), _p(Q), _p(r), _p(c))
+    return Q, r, c
+
+
 def reconstruct_f64(Q, r, c) -> np.ndarray:
     """FP64 reconstruction ((double)Q * r) * c used inside the decode step."""
     Q = _c(Q, np.int32)
@@ -182,16 +198,18 @@ def gated_delta_f64(S, alpha, q, k, v, beta) -> tuple:
     return S, y
 
 
-def quant_step_codes(kda: bool, bits: int, Q, r, c, q, k, v, beta, g) -> np.ndarray:
-    """Quantized step on unpacked codes (any bits 2..24); Q, r, c updated in place."""
+def quant_step_codes(kda: bool, bits: int, Q, r, c, q, k, v, beta, g, imp=None) -> np.ndarray:
+    """Quantized step on unpacked codes (any bits 2..24); Q, r, c updated in place.
+    imp [dk]: requantize with the key-row-aware fit instead of the closed rule."""
     assert Q.dtype == np.int32 and r.dtype == np.float32 and c.dtype == np.float32
     assert Q.flags.c_contiguous
     dk, dv = Q.shape
     y = np.empty(dv, np.float64)
     g = np.atleast_1d(_c(g, np.float32))
     q, k, v = (_c(x, np.float32) for x in (q, k, v))
+    imp = None if imp is None else _c(imp, np.float32)
     lib().sqo_quant_step_codes(int(kda), bits, dk, dv, _p(Q), _p(r), _p(c), _p(q), _p(k),
-                               _p(v), float(beta), _p(g), _p(y))
+                               _p(v), float(beta), _p(g), _p(imp), _p(y))
     return y
 
 
@@ -216,14 +234,24 @@ def record_unpack(bits, dk, dv, rec) -> tuple:
 
 
 # ---------------------------------------------------------------- batches
-def records_quantize(base: np.ndarray, offs, bits, S, dk, dv):
+def _imp(imp, n, dk):
+    if imp is None:
+        return None
+    imp = _c(imp, np.float32)
+    assert imp.size == n * dk
+    return imp
+
+
+def records_quantize(base: np.ndarray, offs, bits, S, dk, dv, imp=None):
+    """imp [n, dk]: row-impact scores per record (key-row-aware fit), or None."""
     offs = _c(offs, np.int64)
     bits = _c(bits, np.uint8)
     S = _c(S, np.float32)
+    imp = _imp(imp, offs.size, dk)
     assert base.dtype == np.uint8 and base.flags.c_contiguous
     assert S.size == offs.size * dk * dv
     if lib().sqo_records_quantize(offs.size, dk, dv, _p(bits), _p(offs), _p(base), _p(S),
-                                  n_threads()) != 0:
+                                  _p(imp), n_threads()) != 0:
         raise ValueError("bad arguments")
 
 
@@ -238,16 +266,19 @@ def records_dequantize(base: np.ndarray, offs, bits, dk, dv) -> np.ndarray:
     return S
 
 
-def records_step(kda: bool, base: np.ndarray, offs, bits, dk, dv, q, k, v, beta, g) -> np.ndarray:
-    """Quantized decode step, in place on the records at base + offs[row]; returns y (f64)."""
+def records_step(kda: bool, base: np.ndarray, offs, bits, dk, dv, q, k, v, beta, g,
+                 imp=None) -> np.ndarray:
+    """Quantized decode step, in place on the records at base + offs[row]; returns y (f64).
+    imp [n, dk]: requantize with the key-row-aware fit."""
     offs = _c(offs, np.int64)
     bits = _c(bits, np.uint8)
     n = offs.size
+    imp = _imp(imp, n, dk)
     assert base.dtype == np.uint8 and base.flags.c_contiguous
     y = np.empty((n, dv), np.float64)
     q, k, v, beta, g = (_c(x, np.float32) for x in (q, k, v, beta, g))
     if lib().sqo_records_step(int(kda), n, dk, dv, _p(bits), _p(offs), _p(base), _p(q), _p(k),
-                              _p(v), _p(beta), _p(g), _p(y), n_threads()) != 0:
+                              _p(v), _p(beta), _p(g), _p(imp), _p(y), n_threads()) != 0:
         raise ValueError("bad arguments")
     return y
 

@@ -223,6 +223,88 @@ void sqo_quantize(int bits, int dk, int dv, const float *S, int32_t *Q, float *r
 }
 
 /*
+ * Key-row-aware dual-axis fit (hyper.ai summary, "Method", the Key-Row-Aware
+ * Dual-Axis Fitting paragraph; blog.ontle.kr, the paragraph on what is fixed
+ * offline).  Each key row i has a row-impact score imp_i > 0, calibrated
+ * offline.  The row factor weighs the row's current magnitude against its
+ * impact with a square root, so large rows get a wider range and high-impact
+ * rows finer steps.  Given the row factors, each column scale is fitted to
+ * the impact-weighted reconstruction error, and every scaled entry goes to
+ * its nearest level.  The pages give no formulas; the reading used here, in
+ * fp32 with one rounding per operation unless FP64 is named:
+ *   mu_i  = max_j |S_ij|                         (row magnitude)
+ *   r_i   = sqrt(mu_i / imp_i)                   (0 if mu_i < FLT_MIN, or if
+ *                                                 r_i is not finite or < FLT_MIN)
+ *   ir_i  = r_i > 0 ? 1/r_i : 0
+ *   s_ij  = S_ij * ir_i                          (the row-scaled entry)
+ *   c0_j  = max_i |s_ij| / qmax                  (the range-covering scale;
+ *   ic0_j = c0_j >= FLT_MIN ? 1/c0_j : 0          else c0_j := 0)
+ *   P_ij  = round_half_even(s_ij * ic0_j)        (exact product)
+ *   w_i   = imp_i * r_i * r_i                    (FP64, exact: the weight of
+ *           an s-domain error, since S_ij - r_i c Q = r_i (s_ij - c Q))
+ *   A_j   = sum_i w_i s_ij P_ij,  B_j = sum_i w_i P_ij^2          (FP64)
+ *   c_j   = B_j > 0 ? (float)(A_j / B_j) : c0_j  (the least-squares scale
+ *           for the codes P; 0 if below FLT_MIN)
+ *   ic_j  = c_j > 0 ? 1/c_j : 0
+ *   Q_ij  = clamp(round_half_even(s_ij * ic_j), -qmax, qmax)  (exact product)
+ * With codes P fixed, c_j minimises sum_i imp_i (S_ij - r_i c Q_ij)^2 in the
+ * s-domain; the final codes are then the nearest levels for c_j, so the
+ * weighted error never exceeds that of the range-covering scale c0_j.
+ * One refinement step, not an iteration to convergence.
+ */
+void sqo_quantize_kra(int bits, int dk, int dv, const float *S, const float *imp, int32_t *Q,
+                      float *r, float *c) {
+    const float qmax = (float)sqo_qmax(bits);
+    float *ir = (float *)malloc(sizeof(float) * (size_t)dk);
+    float *sc = (float *)malloc(sizeof(float) * (size_t)dk * dv);
+    for (int i = 0; i < dk; ++i) {
+        float mu = 0.0f;
+        for (int j = 0; j < dv; ++j) {
+            const float a = fabsf(S[(size_t)i * dv + j]);
+            if (a > mu) mu = a;
+        }
+        float ri = 0.0f;
+        if (mu >= FLT_MIN) ri = sqrtf(mu / imp[i]);
+        if (!(ri >= FLT_MIN) || isinf(ri)) ri = 0.0f;
+        r[i] = ri;
+        ir[i] = ri > 0.0f ? 1.0f / ri : 0.0f;
+        for (int j = 0; j < dv; ++j) sc[(size_t)i * dv + j] = S[(size_t)i * dv + j] * ir[i];
+    }
+    for (int j = 0; j < dv; ++j) {
+        float m = 0.0f;
+        for (int i = 0; i < dk; ++i) {
+            const float a = fabsf(sc[(size_t)i * dv + j]);
+            if (a > m) m = a;
+        }
+        float c0 = m / qmax, ic0 = 0.0f;
+        if (c0 >= FLT_MIN)
+            ic0 = 1.0f / c0;
+        else
+            c0 = 0.0f;
+        double A = 0.0, B = 0.0;
+        for (int i = 0; i < dk; ++i) {
+            const double sv = (double)sc[(size_t)i * dv + j];
+            const double P = nearbyint(sv * (double)ic0);
+            const double w = (double)imp[i] * (double)r[i] * (double)r[i];
+            A += w * sv * P;
+            B += w * P * P;
+        }
+        float cj = B > 0.0 ? (float)(A / B) : c0;
+        if (!(cj >= FLT_MIN)) cj = 0.0f;
+        const float icj = cj > 0.0f ? 1.0f / cj : 0.0f;
+        c[j] = cj;
+        for (int i = 0; i < dk; ++i) {
+            double qv = nearbyint((double)sc[(size_t)i * dv + j] * (double)icj);
+            if (qv > qmax) qv = qmax;
+            if (qv < -qmax) qv = -qmax;
+            Q[(size_t)i * dv + j] = (int32_t)qv;
+        }
+    }
+    free(ir);
+    free(sc);
+}
+
+/*
  * Reconstruction (hyper.ai "Method" para 4: the state is the product of row
  * factors, column factors and low-bit integers): S_ij = Q_ij * r_i * c_j,
  * evaluated in FP64 as ((double)Q_ij * r_i) * c_j.  Q_ij * r_i is exact; the
@@ -290,13 +372,14 @@ static void gate_alpha(int kda, int dk, const float *g, double *alpha) {
 /*
  * Quantized step on one head with unpacked codes (any bits 2..24):
  * FP64 reconstruction -> FP64 gated delta step -> round S' to fp32 ->
- * pinned fp32 quantizer.  y receives the read-out of the unrequantized S'
+ * pinned fp32 quantizer (the closed rule, or the key-row-aware fit when
+ * imp != NULL gives the row-impact scores).  y receives the read-out of the unrequantized S'
  * (hyper.ai "Method" para 1: the state is updated in floating point and the
  * output computed, then the updated state is quantized for storage).
  */
 void sqo_quant_step_codes(int kda, int bits, int dk, int dv, int32_t *Q, float *r, float *c,
                           const float *q, const float *k, const float *v, float beta,
-                          const float *g, double *y) {
+                          const float *g, const float *imp, double *y) {
     const size_t n = (size_t)dk * dv;
     float *S = (float *)malloc(sizeof(float) * n);
     double *Sd = (double *)malloc(sizeof(double) * n);
@@ -311,7 +394,10 @@ void sqo_quant_step_codes(int kda, int bits, int dk, int dv, int32_t *Q, float *
     for (int j = 0; j < dv; ++j) vd[j] = v[j];
     sqo_gated_delta_f64(dk, dv, Sd, alpha, qd, kd, vd, (double)beta, y);
     for (size_t e = 0; e < n; ++e) S[e] = (float)Sd[e];
-    sqo_quantize(bits, dk, dv, S, Q, r, c);
+    if (imp)
+        sqo_quantize_kra(bits, dk, dv, S, imp, Q, r, c);
+    else
+        sqo_quantize(bits, dk, dv, S, Q, r, c);
     free(S);
     free(Sd);
     free(vec);
@@ -379,6 +465,7 @@ typedef struct {
     double *S64;
     const float *q, *k, *v, *beta, *g;
     double *y;
+    const float *imp; /* [n, dk] row-impact scores, or NULL for the closed rule */
 } job_t;
 
 enum { OP_QUANT = 0, OP_DEQUANT = 1, OP_STEP = 2, OP_F64STEP = 3, OP_F32STEP = 4 };
@@ -387,6 +474,7 @@ static void run_row(const job_t *J, int row) {
     const int dk = J->dk, dv = J->dv;
     const size_t n = (size_t)dk * dv;
     const float *g = J->g ? J->g + (J->kda ? (size_t)row * dk : (size_t)row) : NULL;
+    const float *imp = J->imp ? J->imp + (size_t)row * dk : NULL;
     switch (J->op) {
     case OP_QUANT: {
         uint8_t *rec = J->base + J->offs[row];
@@ -397,7 +485,10 @@ static void run_row(const job_t *J, int row) {
         }
         int32_t *Q = (int32_t *)malloc(sizeof(int32_t) * n);
         float rr[1024], cc[1024];
-        sqo_quantize(J->bits[row], dk, dv, J->S32 + (size_t)row * n, Q, rr, cc);
+        if (imp)
+            sqo_quantize_kra(J->bits[row], dk, dv, J->S32 + (size_t)row * n, imp, Q, rr, cc);
+        else
+            sqo_quantize(J->bits[row], dk, dv, J->S32 + (size_t)row * n, Q, rr, cc);
         sqo_record_pack(J->bits[row], dk, dv, Q, rr, cc, rec);
         free(Q);
         break;
@@ -429,7 +520,7 @@ static void run_row(const job_t *J, int row) {
         sqo_record_unpack(bits, dk, dv, rec, Q, rr, cc);
         sqo_quant_step_codes(J->kda, bits, dk, dv, Q, rr, cc, J->q + (size_t)row * dk,
                              J->k + (size_t)row * dk, J->v + (size_t)row * dv, J->beta[row], g,
-                             J->y + (size_t)row * dv);
+                             imp, J->y + (size_t)row * dv);
         sqo_record_pack(bits, dk, dv, Q, rr, cc, rec);
         free(Q);
         break;
@@ -491,12 +582,13 @@ static int check_bits(int n, const uint8_t *bits) {
 }
 
 
-/* Quantize fp32 states S[n, dk, dv] into the records at base + offs[row]. */
+/* Quantize fp32 states S[n, dk, dv] into the records at base + offs[row];
+ * imp [n, dk] selects the key-row-aware fit (NULL: the closed rule). */
 int sqo_records_quantize(int n, int dk, int dv, const uint8_t *bits, const int64_t *offs,
-                         uint8_t *base, const float *S, int n_threads) {
+                         uint8_t *base, const float *S, const float *imp, int n_threads) {
     if (check_bits(n, bits)) return -1;
     job_t J = {OP_QUANT, 0, dk, dv, 0, 0, bits, offs, base, (float *)S, NULL,
-               NULL, NULL, NULL, NULL, NULL, NULL};
+               NULL, NULL, NULL, NULL, NULL, NULL, imp};
     return run_rows(J, n, n_threads);
 }
 
@@ -505,29 +597,34 @@ int sqo_records_dequantize(int n, int dk, int dv, const uint8_t *bits, const int
                            const uint8_t *base, float *S, int n_threads) {
     if (check_bits(n, bits)) return -1;
     job_t J = {OP_DEQUANT, 0, dk, dv, 0, 0, bits, offs, (uint8_t *)base, S, NULL,
-               NULL, NULL, NULL, NULL, NULL, NULL};
+               NULL, NULL, NULL, NULL, NULL, NULL, NULL};
     return run_rows(J, n, n_threads);
 }
 
-/* One quantized decode step, in place on the records; y[n, dv] in double. */
+/* One quantized decode step, in place on the records; y[n, dv] in double;
+ * imp [n, dk] as for sqo_records_quantize. */
 int sqo_records_step(int kda, int n, int dk, int dv, const uint8_t *bits, const int64_t *offs,
                      uint8_t *base, const float *q, const float *k, const float *v,
-                     const float *beta, const float *g, double *y, int n_threads) {
+                     const float *beta, const float *g, const float *imp, double *y,
+                     int n_threads) {
     if (check_bits(n, bits)) return -1;
-    job_t J = {OP_STEP, kda, dk, dv, 0, 0, bits, offs, base, NULL, NULL, q, k, v, beta, g, y};
+    job_t J = {OP_STEP, kda, dk, dv, 0, 0, bits, offs, base, NULL, NULL, q, k, v, beta, g, y,
+               imp};
     return run_rows(J, n, n_threads);
 }
 
 /* One unquantized step on FP64 states S[n, dk, dv] (in place). */
 int sqo_f64_step(int kda, int n, int dk, int dv, double *S, const float *q, const float *k,
                  const float *v, const float *beta, const float *g, double *y, int n_threads) {
-    job_t J = {OP_F64STEP, kda, dk, dv, 0, 0, NULL, NULL, NULL, NULL, S, q, k, v, beta, g, y};
+    job_t J = {OP_F64STEP, kda, dk, dv, 0, 0, NULL, NULL, NULL, NULL, S, q, k, v, beta, g, y,
+               NULL};
     return run_rows(J, n, n_threads);
 }
 
 /* One step on fp32-stored states S[n, dk, dv]: widen, FP64 step, round back. */
 int sqo_f32_step(int kda, int n, int dk, int dv, float *S, const float *q, const float *k,
                  const float *v, const float *beta, const float *g, double *y, int n_threads) {
-    job_t J = {OP_F32STEP, kda, dk, dv, 0, 0, NULL, NULL, NULL, S, NULL, q, k, v, beta, g, y};
+    job_t J = {OP_F32STEP, kda, dk, dv, 0, 0, NULL, NULL, NULL, S, NULL, q, k, v, beta, g, y,
+               NULL};
     return run_rows(J, n, n_threads);
 }

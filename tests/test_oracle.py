@@ -582,3 +582,165 @@ def test_f16_record_step():
     assert np.array_equal(rec.view(np.uint16),
                           want.astype(np.float32).astype(np.float16).view(np.uint16).ravel())
     assert np.array_equal(y[0], yw)
+
+
+# ------------------------------------------------------------------ key-row-aware fit
+def _weighted_err(S, imp, Q, r, c):
+    R = Q.astype(np.float64) * r.astype(np.float64)[:, None] * c.astype(np.float64)[None, :]
+    return (imp.astype(np.float64)[:, None] * (S.astype(np.float64) - R) ** 2).sum(axis=0)
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_kra_exact_on_constructed_state(bits):
+    """S_ij = R_i C_j K_ij with power-of-two R, C and integer K whose columns
+    each reach qmax; with imp_i = 4 mu_i / R_i^2 the row factors are R_i / 2
+    exactly, the range-covering column scales 2 C_j are already the weighted
+    least-squares scales, and the fit returns K, R / 2, 2 C bit for bit.
+    (A wrong root, weight, axis or tie rule breaks this.)"""
+    rng = np.random.default_rng(100 + bits)
+    dk, dv, q = 16, 12, O.qmax(bits)
+    K = rng.integers(-q, q + 1, size=(dk, dv))
+    K[rng.integers(0, dk, dv), np.arange(dv)] = q * rng.choice([-1, 1], dv)
+    R = 2.0 ** rng.integers(-6, 7, dk)
+    C = 2.0 ** rng.integers(-6, 7, dv)
+    S = (R[:, None] * C[None, :] * K).astype(np.float32)
+    mu = np.abs(S).max(axis=1).astype(np.float64)
+    imp = (4 * mu / R ** 2).astype(np.float32)
+    Q, r, c = O.quantize_kra(bits, S, imp)
+    assert np.array_equal(Q, K)
+    assert np.array_equal(r, (R / 2).astype(np.float32))
+    assert np.array_equal(c, (2 * C).astype(np.float32))
+    assert np.array_equal(O.dequantize(Q, r, c), S)
+
+
+def test_kra_row_factor_square_root_law():
+    """r_i = sqrt(mu_i / imp_i): scaling one row's impact by 4 halves its row
+    factor exactly, scaling one row of S by 4 doubles it, other rows keep
+    theirs, and the codes of the untouched rows' pattern stay valid."""
+    rng = np.random.default_rng(7)
+    S = _rand_state(rng, 10, 9)
+    imp = rng.uniform(0.2, 3.0, 10).astype(np.float32)
+    _, r, _ = O.quantize_kra(6, S, imp)
+    imp2 = imp.copy()
+    imp2[3] *= 4
+    _, r2, _ = O.quantize_kra(6, S, imp2)
+    assert r2[3] == r[3] / 2 and np.array_equal(np.delete(r2, 3), np.delete(r, 3))
+    S2 = S.copy()
+    S2[5] *= 4
+    _, r3, _ = O.quantize_kra(6, S2, imp)
+    assert r3[5] == 2 * r[5] and np.array_equal(np.delete(r3, 5), np.delete(r, 5))
+    mu = np.abs(S).max(axis=1)
+    assert np.allclose(r, np.sqrt(mu.astype(np.float64) / imp), rtol=2e-7)
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_kra_scale_invariance(bits):
+    """S -> 4 S doubles r and c; imp -> 4 imp halves r and doubles c; the codes
+    never change (both are exact power-of-two rescalings of every step)."""
+    rng = np.random.default_rng(9 + bits)
+    S = _rand_state(rng, 24, 20)
+    imp = rng.uniform(0.1, 5.0, 24).astype(np.float32)
+    Q, r, c = O.quantize_kra(bits, S, imp)
+    Q2, r2, c2 = O.quantize_kra(bits, 4 * S, imp)
+    assert np.array_equal(Q2, Q) and np.array_equal(r2, 2 * r) and np.array_equal(c2, 2 * c)
+    Q3, r3, c3 = O.quantize_kra(bits, S, 4 * imp)
+    assert np.array_equal(Q3, Q) and np.array_equal(r3, r / 2) and np.array_equal(c3, 2 * c)
+    Q4, r4, c4 = O.quantize_kra(bits, -S, imp)
+    assert np.array_equal(Q4, -Q) and np.array_equal(r4, r) and np.array_equal(c4, c)
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_kra_fit_properties(bits):
+    """Against the range-covering codes P (c0_j = max_i |S_ij / r_i| / qmax,
+    P = nearest level): (1) the fitted c_j minimises the impact-weighted
+    error of P (perturbing c_j either way by 1e-3 increases it); (2) the
+    final codes are each the nearest level in [-qmax, qmax] to S_ij / (r_i
+    c_j) (brute force over all levels); (3) the weighted error of the final
+    codes is never above that of (c0, P)."""
+    rng = np.random.default_rng(20 + bits)
+    dk, dv, q = 32, 24, O.qmax(bits)
+    S = _rand_state(rng, dk, dv)
+    S[rng.integers(0, dk, 5), rng.integers(0, dv, 5)] *= 30      # isolated outliers
+    imp = np.exp(rng.normal(0, 1.5, dk)).astype(np.float32)
+    Q, r, c = O.quantize_kra(bits, S, imp)
+    Sd = S.astype(np.float64)
+    x = Sd / r.astype(np.float64)[:, None]
+    c0 = np.abs(x).max(axis=0) / q
+    P = np.rint(x / c0[None, :])
+    w = imp.astype(np.float64) * r.astype(np.float64) ** 2
+
+    def err_s(cc, codes):
+        return (w[:, None] * (x - cc[None, :] * codes) ** 2).sum(axis=0)
+
+    base = err_s(c.astype(np.float64), P)
+    assert (err_s(c * (1 + 1e-3), P) > base).all()
+    assert (err_s(c * (1 - 1e-3), P) > base).all()
+    levels = np.arange(-q, q + 1, dtype=np.float64)
+    t = x / c.astype(np.float64)[None, :]
+    best = levels[np.abs(t[..., None] - levels).argmin(axis=-1)]
+    assert np.array_equal(Q, best)
+    assert (_weighted_err(S, imp, Q, r, c) <= _weighted_err(S, imp, P, r, c0) * (1 + 1e-9)).all()
+    # fitting pays off somewhere: some columns shrink below the covering scale
+    assert (c < c0 * (1 - 1e-6)).any()
+
+
+def test_kra_high_impact_rows_get_finer_steps():
+    """Two copies of the same row, impacts 1 and 100: the high-impact copy
+    gets a 10x smaller row factor and a smaller reconstruction error."""
+    rng = np.random.default_rng(31)
+    S = _rand_state(rng, 8, 64)
+    S[4] = S[0]
+    imp = np.ones(8, np.float32)
+    imp[4] = 100.0
+    Q, r, c = O.quantize_kra(4, S, imp)
+    assert math.isclose(r[0] / r[4], 10.0, rel_tol=1e-6)
+    R = O.dequantize(Q, r, c).astype(np.float64)
+    e0 = ((R[0] - S[0]) ** 2).sum()
+    e4 = ((R[4] - S[4]) ** 2).sum()
+    assert e4 < e0 / 4
+
+
+def test_kra_zero_rows_columns_and_state():
+    rng = np.random.default_rng(41)
+    S = _rand_state(rng, 6, 5)
+    S[2, :] = 0.0
+    S[:, 3] = 0.0
+    imp = rng.uniform(0.5, 2, 6).astype(np.float32)
+    Q, r, c = O.quantize_kra(6, S, imp)
+    assert r[2] == 0 and (Q[2] == 0).all() and c[3] == 0 and (Q[:, 3] == 0).all()
+    assert np.isfinite(O.dequantize(Q, r, c)).all()
+    Q, r, c = O.quantize_kra(8, np.zeros((4, 4), np.float32), np.ones(4, np.float32))
+    assert (Q == 0).all() and (r == 0).all() and (c == 0).all()
+
+
+def test_kra_drivers_and_step_compose():
+    """records_quantize / records_step with per-record impacts equal the
+    single-head fit, and the quantized step with impacts is the FP64 step
+    on the reconstruction, rounded to fp32, then the key-row-aware fit."""
+    rng = np.random.default_rng(51)
+    d, bits = 16, [4, 6, 8]
+    S = np.stack([_rand_state(rng, d, d) for _ in bits])
+    imp = rng.uniform(0.1, 4, (3, d)).astype(np.float32)
+    sizes = [O.record_bytes(b, d, d) for b in bits]
+    offs = np.array([0, sizes[0], sizes[0] + sizes[1]], np.int64)
+    base = np.zeros(sum(sizes), np.uint8)
+    b8 = np.array(bits, np.uint8)
+    O.records_quantize(base, offs, b8, S, d, d, imp)
+    for i, b in enumerate(bits):
+        Q, r, c = O.quantize_kra(b, S[i], imp[i])
+        assert np.array_equal(base[offs[i]:offs[i] + sizes[i]], O.record_pack(b, Q, r, c))
+    x = [_inputs(rng, d, d, kda=True) for _ in bits]
+    q = np.stack([t[0] for t in x]).astype(np.float32)
+    k = np.stack([t[1] for t in x]).astype(np.float32)
+    v = np.stack([t[2] for t in x]).astype(np.float32)
+    beta = np.array([t[3] for t in x], np.float32)
+    g = np.log(np.stack([t[4] for t in x])).astype(np.float32)
+    before = base.copy()
+    y = O.records_step(True, base, offs, b8, d, d, q, k, v, beta, g, imp)
+    for i, b in enumerate(bits):
+        Q, r, c = O.record_unpack(b, d, d, before[offs[i]:offs[i] + sizes[i]])
+        alpha = np.exp(g[i].astype(np.float64)).astype(np.float32).astype(np.float64)
+        Sp, yw = O.gated_delta_f64(O.reconstruct_f64(Q, r, c), alpha, q[i], k[i], v[i], beta[i])
+        Q2, r2, c2 = O.quantize_kra(b, Sp.astype(np.float32), imp[i])
+        assert np.array_equal(base[offs[i]:offs[i] + sizes[i]], O.record_pack(b, Q2, r2, c2))
+        assert np.array_equal(y[i], yw)
