@@ -49,6 +49,20 @@ def f32_bytes_per_step(B, H, d, gate, io_bytes=2):
     return B * H * (2 * 4 * d * d + io) + 4 * B
 
 
+def impact_from_workload(wl, layer, steps):
+    """Row-impact scores [H, d] from the last `steps` warm-up steps' inputs
+    (the offline calibration; tokens = steps x requests)."""
+    import workload as W
+    from quantized_gated_delta_amd import allocate as A
+    acc = A.RowImpact()
+    B, H, d = wl.B, wl.H, wl.d
+    for t in range(-steps, 0):
+        x = {k: W.to_f32(v) for k, v in wl.step_inputs(layer, t).items()}
+        acc.add(x["q"].reshape(B, H, d), x["k"].reshape(B, H, d), x["beta"].reshape(B, H),
+                x["g"].reshape((B, H, d) if layer.gate == "kda" else (B, H)))
+    return acc.scores()
+
+
 def kernel_hash():
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -209,6 +223,18 @@ def main():
         eprint("fp32 state: %.2f us/step, %.1f GB/s" % (f_ms * 1e3, variants["fp32_state"]["achieved_GBps"]))
         variants["split_epilogue"] = split_epilogue(pool, slot, steps_in, y, timed, ms_step,
                                                     stream, dev, B, H, d, io_dt)
+        # the key-row-aware fit in the fused epilogue (scores from warm-up inputs)
+        imp = torch.from_numpy(impact_from_workload(wl, layer, 4)).to(dev)
+        pool.set_row_impact(imp)
+        r_ms, r_launch = timed(pool, slot)
+        pool.set_row_impact(None)
+        variants["key_row_aware_fit_6bit"] = {
+            "updates_per_s": updates / (r_ms * 1e-3), "us_per_step": r_ms * 1e3,
+            "us_per_launch": r_launch * 1e3, "algo_bytes_per_step": bytes_step,
+            "achieved_GBps": bytes_step / (r_launch * 1e-3) / 1e9,
+            "hbm_frac": bytes_step / (r_launch * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        eprint("key-row-aware fit: %.2f us/step, %.1f GB/s"
+               % (r_ms * 1e3, variants["key_row_aware_fit_6bit"]["achieved_GBps"]))
         # the mixed 4/8-bit variant (8-bit for heads whose half-life exceeds 64 steps)
         if args.workload == "c3a":
             wb = W.make("c3b")
@@ -435,18 +461,27 @@ def trajectory(args, dev):
                                  x["beta"], x["g"], yw)
         schemes = {"fixed_c4_mix": layer.head_bits.astype(np.uint8)}
         cal = None
+        kra = set()
         if args.allocate:
             cal = A.calibrate(state[:args.calib], np.stack(gsum), avg_bits=6.0, n_pivots=0)
             schemes["uniform_6"] = np.full(H, 6, np.uint8)
             schemes["lifetime_6"] = cal["bits"]
-            schemes["lifetime_6+%d_fp16_pivots" % args.pivots] = A.allocate_bits(
-                cal["distortion"], cal["weights"], 6.0, n_pivots=args.pivots)
+            piv = A.allocate_bits(cal["distortion"], cal["weights"], 6.0, n_pivots=args.pivots)
+            schemes["lifetime_6+%d_fp16_pivots" % args.pivots] = piv
             schemes["lifetime_6_incl_%d_fp16_pivots" % args.pivots] = A.allocate_bits(
                 cal["distortion"], cal["weights"], 6.0, n_pivots=args.pivots,
                 pivots_in_budget=True)
+            # the same widths with the key-row-aware fit (scores from the warm-up inputs)
+            schemes["uniform_6_key_row_aware"] = np.full(H, 6, np.uint8)
+            schemes["lifetime_6+%d_fp16_pivots_key_row_aware" % args.pivots] = piv
+            kra = {"uniform_6_key_row_aware",
+                   "lifetime_6+%d_fp16_pivots_key_row_aware" % args.pivots}
+            imp = torch.from_numpy(impact_from_workload(wl, layer, 16)).to(dev)
         pools = {}
         for name, hb in schemes.items():
             pool = Q.StatePool(B, H, d, [int(b) for b in hb], layer.gate, device=dev)
+            if name in kra:
+                pool.set_row_impact(imp)
             pool.quant_state(ident, state)
             pools[name] = pool
         layers.append((layer, kda, state, pools, schemes, cal))

@@ -120,6 +120,22 @@ sq_status sq_pool_destroy(sq_pool *pool);
 sq_status sq_pool_layout(const sq_pool *pool, int64_t *slot_stride, int64_t *head_off,
                          int64_t *record_bytes);
 
+/* Switch the pool's requantization (in sq_decode_step and sq_quant_state)
+ * to the key-row-aware dual-axis fit (hyper.ai summary, "Method", the
+ * Key-Row-Aware Dual-Axis Fitting paragraph; blog.ontle.kr, the paragraph on
+ * what is fixed offline): per key row i of head h a row-impact score
+ * impact[h][i], calibrated offline, sets the row factor
+ * r_i = sqrt(max_j |S'_ij| / impact_i), and each column scale is fitted by one
+ * impact-weighted least-squares step from the range-covering scale; entries go
+ * to the nearest level, clamped to +-qmax.  The record format is unchanged.
+ *   impact: DEVICE pointer to fp32 [n_heads][d_k], 16-byte aligned, every
+ *           value finite and > 0 (others give undefined but memory-safe
+ *           codes); owned by the caller and read by every later launch on
+ *           this pool, so it must outlive them.  NULL restores the closed
+ *           max rule.  FP16 pivot heads ignore it.
+ * Host-only: enqueues nothing.  Must not race with calls using the pool. */
+sq_status sq_pool_set_row_impact(sq_pool *pool, const float *impact);
+
 /* Quantize fp32 states S [n, H, d_k, d_v] (device) into the slots
  * slot_idx[0..n) (device int32) with each head's bit width, using the scale
  * rule above in fp32 (reciprocal-multiply; one rounding per operation).

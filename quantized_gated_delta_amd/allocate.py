@@ -1,4 +1,5 @@
-"""Lifetime-aware bit allocation with FP16 pivots (offline, once per model).
+"""Offline calibration: lifetime-aware bit allocation with FP16 pivots, and
+the row-impact scores of the key-row-aware fit (once per model).
 
 Source: hyper.ai summary of STEPQuant, "Method" paragraph 2, and blog.ontle.kr
 (the lifetime-allocation paragraphs).  For each recurrent-state unit (here a
@@ -32,6 +33,52 @@ import math
 from typing import Sequence
 
 import numpy as np
+
+
+class RowImpact:
+    """Running row-impact scores (hyper.ai summary, "Method", paragraph on
+    the spatial distribution of errors: the expected squared weighting
+    factor of a key row, from the transition matrix and the query).
+
+    An error E in the stored state reaches the next read-out as E^T A^T q
+    with A = (I - beta k k^T) diag(a) the next step's transition, so key row
+    i enters with weight w_i = a_i (q_i - beta k_i (k . q)).  The score is
+    the mean of w^2 over the calibration tokens, per head, scaled to mean 1
+    over the key rows and floored (the fit needs scores > 0)."""
+
+    def __init__(self):
+        self.sum = None
+        self.n = 0
+
+    def add(self, q, k, beta, log_gates) -> None:
+        """q, k: [T, H, d_k]; beta: [T, H]; log_gates: [T, H] (GDN) or
+        [T, H, d_k] (KDA).  Tokens may be any samples (steps x requests)."""
+        q = np.asarray(q, np.float64)
+        k = np.asarray(k, np.float64)
+        beta = np.asarray(beta, np.float64)
+        g = np.asarray(log_gates, np.float64)
+        if q.ndim != 3 or k.shape != q.shape or beta.shape != q.shape[:2]:
+            raise ValueError("q, k must be [T, H, d_k] and beta [T, H]")
+        a = np.exp(g)[..., None] if g.ndim == 2 else np.exp(g)
+        kq = (k * q).sum(axis=-1, keepdims=True)
+        w = a * (q - beta[..., None] * k * kq)
+        part = (w * w).sum(axis=0)
+        self.sum = part if self.sum is None else self.sum + part
+        self.n += q.shape[0]
+
+    def scores(self, floor: float = 1e-6) -> np.ndarray:
+        imp = self.sum / max(1, self.n)
+        mean = imp.mean(axis=1, keepdims=True)
+        imp = np.where(mean > 0, imp / np.where(mean > 0, mean, 1.0), 1.0)
+        return np.maximum(imp, floor).astype(np.float32)
+
+
+def row_impact(q, k, beta, log_gates, floor: float = 1e-6) -> np.ndarray:
+    """Row-impact scores imp[h, i] of one batch of calibration tokens (see
+    RowImpact)."""
+    acc = RowImpact()
+    acc.add(q, k, beta, log_gates)
+    return acc.scores(floor)
 
 
 def lifetime_weights(mean_log_retention) -> np.ndarray:

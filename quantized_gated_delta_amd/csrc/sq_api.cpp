@@ -168,6 +168,13 @@ sq_status sq_pool_layout(const sq_pool *pool, int64_t *slot_stride, int64_t *hea
     return SQ_OK;
 }
 
+sq_status sq_pool_set_row_impact(sq_pool *pool, const float *impact) {
+    if (!pool) return fail(SQ_EINVAL, "pool is NULL");
+    if (impact && !aligned(impact, 16)) return fail(SQ_EINVAL, "impact is not 16-byte aligned");
+    pool->view.impact = impact;
+    return SQ_OK;
+}
+
 sq_status sq_quant_state(sq_pool *pool, const int32_t *slot_idx, int32_t n, const float *S,
                          hipStream_t stream) {
     sq_status st = check_rows(pool, slot_idx, n);

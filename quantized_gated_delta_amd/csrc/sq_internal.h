@@ -20,6 +20,7 @@ struct PoolView {
     int64_t slot_stride; // bytes per slot
     int32_t n_heads;
     int32_t d;           // d_k == d_v
+    const float *impact; // row-impact scores [n_heads, d] (key-row-aware fit) or null
 };
 
 // Step inputs; dtype flags: 0 = fp32, 1 = bf16.

@@ -478,6 +478,182 @@ template <int CG, int M> __device__ __forceinline__ float band_bcast(float v) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), AND_MASK | (M << 5)));
 }
 
+// ---------------------------------------------------------------- key-row-aware fit
+// Requantization with the key-row-aware dual-axis fit (hyper.ai summary,
+// "Method", the Key-Row-Aware Dual-Axis Fitting paragraph): per key row a
+// row-impact score imp_i > 0 (calibrated offline), in fp32 with one rounding
+// per operation unless FP64 is named:
+//   r_i = sqrt(max_j |S'_ij| / imp_i), ir_i = 1 / r_i      (0 for zero rows)
+//   s_ij = S'_ij ir_i; c0_j = max_i |s_ij| / qmax           (range-covering)
+//   P_ij = nearest level of s_ij / c0_j (exact product s * (1 / c0))
+//   w_i = imp_i r_i^2; A_j = sum_i w_i s_ij P_ij, B_j = sum_i w_i P_ij^2  (FP64)
+//   c_j = B_j > 0 ? (float)(A_j / B_j) : c0_j   (the impact-weighted least-
+//          squares scale for the codes P)
+//   Q_ij = nearest level of s_ij / c_j, clamped to [-qmax, qmax]
+// The FP64 sums run over the 32 bands in two passes through the 32 KB
+// partials region (A, then B), which keeps the LDS footprint of the closed
+// rule.  c_j >= c0_j / 2 (a weighted average of s / P over |P| >= 1), so
+// |s / c_j| <= 2 qmax and the magic-number rounding stays exact.
+template <int D, int BITS>
+__device__ __forceinline__ void kra_quantize_store(float (&x)[4][16], const float *imp,
+                                                   uint8_t *rec, float *lds) {
+#pragma clang fp contract(off)
+    using G = Geo<D>;
+    constexpr int RB = D * BITS / 8;
+    constexpr int QM = (1 << (BITS - 1)) - 1;
+    constexpr float QMAX = (float)QM;
+    constexpr float MAGIC = 12582912.0f; // 1.5 * 2^23
+    const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
+    double *part64 = reinterpret_cast<double *>(lds);
+    float *plane = lds; // column maxima; used (and reduced) before part64
+    double *colA = reinterpret_cast<double *>(lds + DecodeLds<D>::PART_F);
+    float *lds_c0 = lds + DecodeLds<D>::PART_F + 2 * D;
+    float *lds_ic = lds + DecodeLds<D>::PART_F + 4 * D;
+    float *rp = reinterpret_cast<float *>(rec + D * RB);
+    float *cp = rp + D;
+    // ---- row magnitudes, reduced over the band's lanes
+    float mu[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        mu[m] = 0.0f;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) mu[m] = fmaxf(mu[m], fabsf(x[m][n]));
+        mu[m] = band_max<G::CG>(mu[m]);
+    }
+    // ---- row factors: lane cg (< 4) of the band owns row band + NB * cg
+    const float sel01 = (cg & 1) ? mu[1] : mu[0];
+    const float sel23 = (cg & 1) ? mu[3] : mu[2];
+    const float mrow = (cg & 2) ? sel23 : sel01;
+    const float im = imp[band + G::NB * (cg & 3)];
+    float r = 0.0f;
+    if (mrow >= FLT_MIN) r = sqrtf(mrow / im);
+    if (!(r >= FLT_MIN) || r == INFINITY) r = 0.0f;
+    const float ir = r > 0.0f ? 1.0f / r : 0.0f;
+    if (cg < 4) rp[band + G::NB * cg] = r;
+    constexpr int AND_MASK = 0x1F & ~(G::CG - 1);
+    float irm[4], wm_r[4], wm_i[4];
+#define SQ_BCAST(v, m) __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), AND_MASK | ((m) << 5)))
+    irm[0] = SQ_BCAST(ir, 0); irm[1] = SQ_BCAST(ir, 1); irm[2] = SQ_BCAST(ir, 2); irm[3] = SQ_BCAST(ir, 3);
+    wm_r[0] = SQ_BCAST(r, 0); wm_r[1] = SQ_BCAST(r, 1); wm_r[2] = SQ_BCAST(r, 2); wm_r[3] = SQ_BCAST(r, 3);
+    wm_i[0] = SQ_BCAST(im, 0); wm_i[1] = SQ_BCAST(im, 1); wm_i[2] = SQ_BCAST(im, 2); wm_i[3] = SQ_BCAST(im, 3);
+#undef SQ_BCAST
+    double w[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) w[m] = (double)wm_i[m] * (double)wm_r[m] * (double)wm_r[m];
+    // ---- row-scaled entries and their column maxima
+    {
+        float cm[16];
+#pragma unroll
+        for (int n = 0; n < 16; ++n) cm[n] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int n = 0; n < 16; ++n) {
+                x[m][n] = x[m][n] * irm[m];
+                cm[n] = fmaxf(cm[n], fabsf(x[m][n]));
+            }
+        write_band_partials<D>(plane, cm);
+    }
+    __syncthreads();
+    if (t < D) {
+        float c0 = column_max<D>(plane, t) / QMAX;
+        float ic0 = 0.0f;
+        if (c0 >= FLT_MIN)
+            ic0 = 1.0f / c0;
+        else
+            c0 = 0.0f;
+        lds_c0[t] = c0;
+        lds_ic[colvec4_idx(t)] = ic0;
+    }
+    __syncthreads();
+    float ic[16];
+    load_colvec16(lds_ic, cg, ic);
+    // ---- the two FP64 column sums, one pass each through part64
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        // the codes P are formed again in the second pass rather than kept
+        // live across the barrier (64 more VGPRs would spill)
+        if (pass == 1)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int n = 0; n < 16; ++n) asm volatile("" : "+v"(x[m][n]));
+#pragma unroll
+        for (int n2 = 0; n2 < 8; ++n2) {
+            double acc[2] = {0.0, 0.0};
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int n = 2 * n2 + e;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float P = __builtin_fmaf(x[m][n], ic[n], MAGIC) - MAGIC; // exact
+                    const double wp = w[m] * (double)P;
+                    acc[e] = fma(wp, pass == 0 ? (double)x[m][n] : (double)P, acc[e]);
+                }
+            }
+            *reinterpret_cast<double2 *>(part64 + part_idx<D>(band, cg, 2 * n2)) =
+                make_double2(acc[0], acc[1]);
+        }
+        __syncthreads();
+        if (t < D) {
+            double sum = 0.0;
+#pragma unroll 8
+            for (int b = 0; b < G::NB; ++b) sum += part64[part_idx<D>(b, t >> 4, t & 15)];
+            if (pass == 0) {
+                colA[t] = sum;
+            } else {
+                const double A = colA[t];
+                float c = sum > 0.0 ? (float)(A / sum) : lds_c0[t];
+                if (!(c >= FLT_MIN)) c = 0.0f;
+                cp[t] = c;
+                lds_ic[colvec4_idx(t)] = c > 0.0f ? 1.0f / c : 0.0f;
+            }
+        }
+        __syncthreads();
+    }
+    load_colvec16(lds_ic, cg, ic);
+    constexpr uint32_t MB = 0x4B400000u; // bit pattern of MAGIC
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int row = band + G::NB * m;
+        uint32_t f[16];
+#pragma unroll
+        for (int n = 0; n < 16; ++n)
+            f[n] = min(max(code_bits(x[m][n], ic[n]), MB - QM), MB + QM);
+        store_seg<BITS>(rec + row * RB + cg * (2 * BITS), pack_stream<BITS>(f));
+    }
+}
+
+template <int D, int BITS>
+__device__ __forceinline__ void quant_tile_kra(uint8_t *rec, const float *S, const float *imp,
+                                               float *lds) {
+    using G = Geo<D>;
+    const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
+    float x[4][16];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) load16<D>(S + (band + G::NB * m) * D + 16 * cg, x[m]);
+    kra_quantize_store<D, BITS>(x, imp, rec, lds);
+}
+
+template <int D>
+__global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(4)))
+void quant_state_kra_kernel(PoolView pool, HeadTable tab,
+                                                                     const int32_t *slot,
+                                                                     const float *S) {
+    __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D>::TOTAL];
+    const int H = pool.n_heads;
+    const int b = blockIdx.x / H, h = blockIdx.x - b * H;
+    uint8_t *rec = pool.base + (int64_t)slot[b] * pool.slot_stride + tab.off[h];
+    const float *src = S + (int64_t)blockIdx.x * D * D;
+    const float *imp = pool.impact + (int64_t)h * D;
+    switch (tab.bits[h]) {
+    case 4: quant_tile_kra<D, 4>(rec, src, imp, lds); break;
+    case 6: quant_tile_kra<D, 6>(rec, src, imp, lds); break;
+    case 16: quant_tile_f16<D>(rec, src); break;
+    default: quant_tile_kra<D, 8>(rec, src, imp, lds); break;
+    }
+}
+
 // Retention factor a = exp(g) rounded once to fp32 (through FP64 exp).
 __device__ __forceinline__ float gate_factor(float g) { return (float)exp((double)g); }
 
@@ -532,9 +708,10 @@ template <int BITS> __device__ __forceinline__ Seg<BITS> seg_of(const TileIn &in
 
 // SPLIT: write S' (fp32) to io.s_out instead of requantizing; the record
 // is only read.  The requantization then runs as its own launch.
-template <int D, int BITS, bool KDA, bool SPLIT, typename TI, typename TO>
+// KRA: requantize with the key-row-aware fit (row-impact scores imp[D]).
+template <int D, int BITS, bool KDA, bool SPLIT, bool KRA, typename TI, typename TO>
 __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const StepIO &io,
-                                            float *lds) {
+                                            const float *imp, float *lds) {
     using G = Geo<D>;
     constexpr int RB = D * BITS / 8;
     constexpr int PLANE = G::NB * D;
@@ -639,7 +816,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
                 }
             }
             const int pi = plane_idx<D>(band, cg, 4 * n4);
-            if constexpr (!SPLIT)
+            if constexpr (!SPLIT && !KRA)
                 *reinterpret_cast<float4 *>(plane_max + pi) = make_float4(cm[0], cm[1], cm[2], cm[3]);
             *reinterpret_cast<float4 *>(plane_y + pi) = make_float4(yp[0], yp[1], yp[2], yp[3]);
         }
@@ -662,13 +839,18 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
 #pragma unroll 8
         for (int b = 0; b < G::NB; ++b) yv += plane_y[plane_idx<D>(b, t >> 4, t & 15)];
         st<TO>(reinterpret_cast<TO *>(io.y) + row_io * D, t, yv);
-        if constexpr (!SPLIT) lds_ic[colvec4_idx(t)] = column_scale(column_max<D>(plane_max, t), cp + t);
+        if constexpr (!SPLIT && !KRA)
+            lds_ic[colvec4_idx(t)] = column_scale(column_max<D>(plane_max, t), cp + t);
     }
     if constexpr (SPLIT) return;
     __syncthreads();
-    float ic[16];
-    load_colvec16(lds_ic, cg, ic);
-    quantize_rows_store<D, BITS>(x, ic, rec);
+    if constexpr (KRA) {
+        kra_quantize_store<D, BITS>(x, imp, rec, lds);
+    } else {
+        float ic[16];
+        load_colvec16(lds_ic, cg, ic);
+        quantize_rows_store<D, BITS>(x, ic, rec);
+    }
 }
 
 // FP16 pivot record: the same FP64 look-up and update on the exactly
@@ -804,7 +986,7 @@ __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const St
 // One workgroup per (request, head) tile; four resident per CU (VGPRs and
 // LDS both sized for four 4-wave workgroups), which hides the barriers and
 // reduction phases of one tile behind the others.
-template <int D, bool KDA, bool SPLIT, typename TI, typename TO>
+template <int D, bool KDA, bool SPLIT, bool KRA, typename TI, typename TO>
 __global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(SQ_DECODE_WAVES_PER_EU)))
 void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
     __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D>::TOTAL];
@@ -812,11 +994,12 @@ void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
     const int H = pool.n_heads;
     const int b = tile / H, h = tile - b * H;
     uint8_t *rec = pool.base + (int64_t)io.slot[b] * pool.slot_stride + tab.off[h];
+    const float *imp = KRA ? pool.impact + (int64_t)h * D : nullptr;
     switch (tab.bits[h]) {
-    case 4: decode_tile<D, 4, KDA, SPLIT, TI, TO>(rec, tile, io, lds); break;
-    case 6: decode_tile<D, 6, KDA, SPLIT, TI, TO>(rec, tile, io, lds); break;
+    case 4: decode_tile<D, 4, KDA, SPLIT, KRA, TI, TO>(rec, tile, io, imp, lds); break;
+    case 6: decode_tile<D, 6, KDA, SPLIT, KRA, TI, TO>(rec, tile, io, imp, lds); break;
     case 16: decode_tile_f16<D, KDA, SPLIT, TI, TO>(rec, tile, io, lds); break;
-    default: decode_tile<D, 8, KDA, SPLIT, TI, TO>(rec, tile, io, lds); break;
+    default: decode_tile<D, 8, KDA, SPLIT, KRA, TI, TO>(rec, tile, io, imp, lds); break;
     }
 }
 
@@ -921,30 +1104,33 @@ __global__ __launch_bounds__(Geo<D>::NT) void f32_decode_kernel(float *state, in
 }
 
 // ---------------------------------------------------------------- dispatch
-template <int D, bool KDA, bool SPLIT>
+template <int D, bool KDA, bool SPLIT, bool KRA>
 hipError_t decode_dispatch(const PoolView &pool, const HeadTable &tab, const StepIO &io,
                            hipStream_t s) {
     const dim3 grid((unsigned)io.n * (unsigned)pool.n_heads), block(Geo<D>::NT);
     if (!io.in_bf16 && !io.y_bf16)
-        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, float, float>), grid, block, 0, s, pool, tab, io);
+        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, KRA, float, float>), grid, block, 0, s, pool,
+                           tab, io);
     else if (!io.in_bf16 && io.y_bf16)
-        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, float, uint16_t>), grid, block, 0, s, pool, tab, io);
+        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, KRA, float, uint16_t>), grid, block, 0, s,
+                           pool, tab, io);
     else if (io.in_bf16 && !io.y_bf16)
-        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, uint16_t, float>), grid, block, 0, s, pool, tab, io);
+        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, KRA, uint16_t, float>), grid, block, 0, s,
+                           pool, tab, io);
     else
-        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, uint16_t, uint16_t>), grid, block, 0, s, pool, tab,
-                           io);
+        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, KRA, uint16_t, uint16_t>), grid, block, 0, s,
+                           pool, tab, io);
     return hipGetLastError();
 }
 
-template <bool SPLIT>
+template <bool SPLIT, bool KRA>
 hipError_t decode_gate_dispatch(const PoolView &pool, const HeadTable &tab, const StepIO &io,
                                 hipStream_t stream) {
     if (pool.d == 128)
-        return io.kda ? decode_dispatch<128, true, SPLIT>(pool, tab, io, stream)
-                      : decode_dispatch<128, false, SPLIT>(pool, tab, io, stream);
-    return io.kda ? decode_dispatch<64, true, SPLIT>(pool, tab, io, stream)
-                  : decode_dispatch<64, false, SPLIT>(pool, tab, io, stream);
+        return io.kda ? decode_dispatch<128, true, SPLIT, KRA>(pool, tab, io, stream)
+                      : decode_dispatch<128, false, SPLIT, KRA>(pool, tab, io, stream);
+    return io.kda ? decode_dispatch<64, true, SPLIT, KRA>(pool, tab, io, stream)
+                  : decode_dispatch<64, false, SPLIT, KRA>(pool, tab, io, stream);
 }
 
 template <int D, bool KDA>
@@ -966,10 +1152,18 @@ hipError_t f32_dispatch(float *state, int64_t stride, int32_t H, const StepIO &i
 hipError_t launch_quant_state(const PoolView &pool, const HeadTable &tab, const int32_t *slot,
                               int32_t n, const float *S, hipStream_t stream) {
     const dim3 grid((unsigned)n * (unsigned)pool.n_heads);
-    if (pool.d == 128)
+    if (pool.impact) {
+        if (pool.d == 128)
+            hipLaunchKernelGGL(quant_state_kra_kernel<128>, grid, dim3(Geo<128>::NT), 0, stream, pool,
+                               tab, slot, S);
+        else
+            hipLaunchKernelGGL(quant_state_kra_kernel<64>, grid, dim3(Geo<64>::NT), 0, stream, pool,
+                               tab, slot, S);
+    } else if (pool.d == 128) {
         hipLaunchKernelGGL(quant_state_kernel<128>, grid, dim3(Geo<128>::NT), 0, stream, pool, tab, slot, S);
-    else
+    } else {
         hipLaunchKernelGGL(quant_state_kernel<64>, grid, dim3(Geo<64>::NT), 0, stream, pool, tab, slot, S);
+    }
     return hipGetLastError();
 }
 
@@ -985,12 +1179,14 @@ hipError_t launch_dequant_state(const PoolView &pool, const HeadTable &tab, cons
 
 hipError_t launch_decode(const PoolView &pool, const HeadTable &tab, const StepIO &io,
                          hipStream_t stream) {
-    return decode_gate_dispatch<false>(pool, tab, io, stream);
+    // a pool with row-impact scores requantizes with the key-row-aware fit
+    return pool.impact ? decode_gate_dispatch<false, true>(pool, tab, io, stream)
+                       : decode_gate_dispatch<false, false>(pool, tab, io, stream);
 }
 
 hipError_t launch_decode_update(const PoolView &pool, const HeadTable &tab, const StepIO &io,
                                 hipStream_t stream) {
-    return decode_gate_dispatch<true>(pool, tab, io, stream);
+    return decode_gate_dispatch<true, false>(pool, tab, io, stream);
 }
 
 hipError_t launch_f32_decode(float *state, int64_t slot_stride_floats, int32_t n_heads, int32_t d,

@@ -60,6 +60,8 @@ def lib():
         L.sq_pool_layout.restype = st
         L.sq_pool_layout.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                      ctypes.POINTER(i64)]
+        L.sq_pool_set_row_impact.restype = st
+        L.sq_pool_set_row_impact.argtypes = [vp, vp]
         L.sq_quant_state.restype = st
         L.sq_quant_state.argtypes = [vp, vp, i32, vp, vp]
         L.sq_dequant_state.restype = st
@@ -185,6 +187,11 @@ def sq_decode_step(handle, slot_idx, n: int, q, k, v, beta, g, y, in_dtype=None,
                                 _stream(stream)), "sq_decode_step")
 
 
+def sq_pool_set_row_impact(handle, impact) -> None:
+    """impact: device tensor [n_heads, d_k] fp32 (kept alive by the caller), or None."""
+    _check(lib().sq_pool_set_row_impact(handle, _ptr(impact)), "sq_pool_set_row_impact")
+
+
 def sq_decode_update(handle, slot_idx, n: int, q, k, v, beta, g, y, S_out, in_dtype=None,
                      y_dtype=None, stream=None) -> None:
     in_dtype = _dtype_code(q) if in_dtype is None else in_dtype
@@ -242,6 +249,15 @@ class StatePool:
     def decode_step(self, slot_idx, q, k, v, beta, g, y, stream=None):
         sq_decode_step(self.handle, slot_idx, slot_idx.numel(), q, k, v, beta, g, y,
                        stream=stream)
+
+    def set_row_impact(self, impact):
+        """Requantize with the key-row-aware fit from now on (impact: [H, d_k]
+        fp32 device tensor, > 0), or with the closed rule (None)."""
+        if impact is not None:
+            impact = impact.contiguous()
+            assert impact.shape == (self.n_heads, self.d) and impact.is_cuda
+        self.impact = impact  # the library keeps only the pointer
+        sq_pool_set_row_impact(self.handle, impact)
 
     def decode_update(self, slot_idx, q, k, v, beta, g, y, S_out, stream=None):
         """Split step, first half: y and S' (fp32) out, pool unchanged; store

@@ -95,3 +95,52 @@ def test_budget_edges():
     assert (A.allocate_bits(D, w, 8.0) == 8).all()
     with pytest.raises(ValueError):
         A.allocate_bits(D, w, 3.0)
+
+
+def test_row_impact_closed_forms():
+    rng = np.random.default_rng(11)
+    T, H, d = 200, 3, 8
+    q = rng.standard_normal((T, H, d))
+    k = rng.standard_normal((T, H, d))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    # beta = 0, gate 1: the weight is q itself -> imp ~ E[q_i^2], mean 1
+    imp = A.row_impact(q, k, np.zeros((T, H)), np.zeros((T, H)))
+    want = (q ** 2).mean(axis=0)
+    assert np.allclose(imp, want / want.mean(axis=1, keepdims=True), rtol=1e-6)
+    assert np.allclose(imp.mean(axis=1), 1.0, rtol=1e-6)
+    # beta = 1, k = e_0: the write replaces row 0, so an error there never
+    # reaches the read-out (w_0 = q_0 - q_0 = 0, floored); other rows keep q_i
+    e0 = np.zeros_like(q)
+    e0[..., 0] = 1.0
+    imp0 = A.row_impact(q, e0, np.ones((T, H)), np.zeros((T, H)), floor=1e-6)
+    assert (imp0[:, 0] == np.float32(1e-6)).all()
+    w1 = want[:, 1:]
+    assert np.allclose(imp0[:, 1:], w1 / (w1.sum(axis=1, keepdims=True) / d), rtol=1e-6)
+    # KDA: a per-row gate scales row i's weight by a_i
+    g = np.zeros((T, H, d))
+    g[:, :, 2] = np.log(0.5)
+    imp2 = A.row_impact(q, k, np.zeros((T, H)), g)
+    ratio = imp2[:, 2] / imp2[:, 3]
+    assert np.allclose(ratio, 0.25 * want[:, 2] / want[:, 3], rtol=1e-6)
+
+
+def test_row_impact_floor_and_shapes():
+    q = np.zeros((4, 2, 5))
+    q[..., 0] = 1.0
+    imp = A.row_impact(q, np.zeros_like(q), np.zeros((4, 2)), np.zeros((4, 2)), floor=1e-3)
+    assert imp.dtype == np.float32 and imp.shape == (2, 5)
+    assert (imp[:, 1:] == np.float32(1e-3)).all() and np.allclose(imp[:, 0], 5.0)
+    with pytest.raises(ValueError):
+        A.row_impact(q, q[:, :1], np.zeros((4, 2)), np.zeros((4, 2)))
+
+
+def test_row_impact_streaming_equals_batch():
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((30, 2, 6))
+    k = rng.standard_normal((30, 2, 6))
+    b = rng.uniform(0, 1, (30, 2))
+    g = -rng.uniform(0, 0.5, (30, 2, 6))
+    acc = A.RowImpact()
+    for lo in range(0, 30, 7):
+        acc.add(q[lo:lo + 7], k[lo:lo + 7], b[lo:lo + 7], g[lo:lo + 7])
+    assert np.allclose(acc.scores(), A.row_impact(q, k, b, g), rtol=1e-6)

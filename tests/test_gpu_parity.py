@@ -53,14 +53,23 @@ def dev_inputs(x: dict) -> dict:
 class Side:
     """One layer on both sides: GPU pool and the oracle's host image."""
 
-    def __init__(self, wl: W.Workload, layer: W.Layer):
+    def __init__(self, wl: W.Workload, layer: W.Layer, imp=None):
+        """imp [H, d] fp32: row-impact scores (key-row-aware fit on both sides)."""
         self.wl, self.layer = wl, layer
         self.kda = layer.gate == "kda"
         self.gpu = Q.StatePool(wl.n_slots, wl.H, wl.d, layer.head_bits.tolist(), layer.gate)
+        self.imp = None if imp is None else np.ascontiguousarray(imp, np.float32)
+        if self.imp is not None:
+            self.gpu.set_row_impact(to_dev(self.imp))
         self.host = Hn.HostPool(wl.n_slots, layer.head_bits, wl.d)
         assert self.gpu.slot_stride == self.host.stride
         assert np.array_equal(np.array(self.gpu.head_off), self.host.head_off)
         self.slot_dev = to_dev(layer.slot_of.astype(np.int32))
+
+    def rows_imp(self, rows):
+        if self.imp is None:
+            return None
+        return self.imp[np.asarray(rows).reshape(-1, 2)[:, 1]]
 
     def rows_offsets(self, rows):
         rows = np.asarray(rows).reshape(-1, 2)
@@ -72,7 +81,8 @@ class Side:
         if S is None:
             S = Hn.oracle_warmup(self.wl, self.layer, rows)
         offs, bits = self.rows_offsets(rows)
-        O.records_quantize(self.host.bytes, offs, bits, S, self.wl.d, self.wl.d)
+        O.records_quantize(self.host.bytes, offs, bits, S, self.wl.d, self.wl.d,
+                           self.rows_imp(rows))
         self.push_rows(rows)
 
     def push_rows(self, rows):
@@ -112,7 +122,7 @@ class Side:
         xs = {k: W.to_f32(v[idx]) for k, v in x.items()}
         offs, bits = self.rows_offsets(rows)
         y_ref = O.records_step(self.kda, self.host.bytes, offs, bits, wl.d, wl.d, xs["q"],
-                               xs["k"], xs["v"], xs["beta"], xs["g"])
+                               xs["k"], xs["v"], xs["beta"], xs["g"], self.rows_imp(rows))
         y_gpu = W.to_f32(from_dev(y)).astype(np.float64)[idx]
         if wl.dtype == "bf16":
             y_ref = Hn.to_bf16_f32(y_ref)
@@ -156,6 +166,26 @@ def sample_rows(B, H, n, seed=0):
     rng = np.random.default_rng(1234 + seed)
     flat = rng.choice(B * H, size=min(n, B * H), replace=False)
     return np.stack([flat // H, flat % H], axis=1)
+
+
+def wide_impact(H, d, seed):
+    """Row-impact scores spread over about three decades (stresses the fit)."""
+    rng = np.random.default_rng(900 + seed)
+    return np.exp(rng.normal(0.0, 1.5, (H, d))).astype(np.float32)
+
+
+def calibrated_impact(wl, layer, steps=16):
+    """Row-impact scores from the warm-up inputs, as the offline calibration does."""
+    from quantized_gated_delta_amd import allocate as A
+    qs, ks, bs, gs = [], [], [], []
+    for t in range(-steps, 0):
+        x = Hn.inputs_f32(wl.step_inputs(layer, t))
+        qs.append(x["q"].reshape(wl.B, wl.H, wl.d))
+        ks.append(x["k"].reshape(wl.B, wl.H, wl.d))
+        bs.append(x["beta"].reshape(wl.B, wl.H))
+        gs.append(x["g"].reshape((wl.B, wl.H, wl.d) if layer.gate == "kda" else (wl.B, wl.H)))
+    return A.row_impact(np.concatenate(qs), np.concatenate(ks), np.concatenate(bs),
+                        np.concatenate(gs))
 
 
 # ----------------------------------------------------------------- G1
@@ -231,22 +261,26 @@ def test_decode_step_small_full_compare(case):
 
 
 @pytest.mark.parametrize("case", [
-    ("gdn", 4, 5, 128, [6, 16, 4, 8, 6], "bf16", 6),
-    ("kda", 3, 3, 64, [8, 16, 4], "f32", 4),
+    ("gdn", 4, 5, 128, [6, 16, 4, 8, 6], "bf16", 6, False),
+    ("kda", 3, 3, 64, [8, 16, 4], "f32", 4, False),
+    ("gdn", 3, 4, 128, [4, 6, 16, 8], "bf16", 5, True),
 ])
 def test_split_update_then_quant_matches_fused(case):
     """The split step (sq_decode_update, then sq_quant_state of S' on a second
     stream ordered by an event) stores byte-identical records and y to the
-    fused sq_decode_step, whose records match the oracle's."""
-    gate, B, H, d, bits, dtype, n_slots = case
+    fused sq_decode_step, whose records match the oracle's; with row-impact
+    scores both requantize with the key-row-aware fit."""
+    gate, B, H, d, bits, dtype, n_slots, kra = case
     log("split %s" % (case,))
     wl = W.custom(gate, B, H, d, bits, dtype=dtype, n_slots=n_slots, permute=True, seed=8)
-    side = Side(wl, wl.layers[0])
+    side = Side(wl, wl.layers[0], wide_impact(H, d, 8) if kra else None)
     side.gpu.buf.fill_(0xA5)
     side.host.bytes[:] = 0xA5
     rows = Hn.rows_all(B, H)
     side.init_oracle_rows(rows)
     split = Q.StatePool(wl.n_slots, H, d, bits, gate)
+    if kra:
+        split.set_row_impact(to_dev(side.imp))
     S_out = torch.full((B, H, d, d), float("nan"), dtype=torch.float32, device=DEV)
     epi = torch.cuda.Stream()
     ydt = torch.float32 if dtype == "f32" else torch.bfloat16
@@ -510,3 +544,86 @@ def test_c4_two_layers_vs_fp32_state():
         assert np.isfinite(errs).all() and max(errs) < 0.5
         side.gpu.close()
         del state
+
+
+# ----------------------------------------------------------------- key-row-aware fit
+@pytest.mark.parametrize("d", [64, 128])
+def test_kra_quant_state_matches_oracle(d):
+    """sq_quant_state on a pool with row-impact scores: the key-row-aware fit,
+    against the oracle's; FP16 pivot heads ignore the scores."""
+    log("kra quant d=%d" % d)
+    rng = np.random.default_rng(70 + d)
+    H, B = 5, 6
+    bits = [4, 6, 8, 16, 6]
+    wl = W.custom("gdn", B, H, d, bits, n_slots=8, permute=True, seed=4)
+    side = Side(wl, wl.layers[0], wide_impact(H, d, d))
+    S = (rng.standard_normal((B, H, d, d)) * np.exp(rng.standard_normal((B, H, d, 1)))
+         * np.exp(rng.standard_normal((B, H, 1, d)))).astype(np.float32)
+    S[0, 0] = 0.0
+    S[1, 1, 5, :] = 0.0
+    S[1, 1, :, 7] = 0.0
+    S[2, 2, 3, :4] *= 200.0                        # isolated outliers
+    S[3, 4] *= np.float32(1e-30)                   # tiny state
+    side.gpu.quant_state(side.slot_dev, to_dev(S))
+    rows = Hn.rows_all(B, H)
+    offs, hb = side.rows_offsets(rows)
+    O.records_quantize(side.host.bytes, offs, hb, S.reshape(-1, d, d), d, d, side.rows_imp(rows))
+    got = side.gpu_pool()
+    check_records(side, rows, got, "kra quant")
+    for (b, h), o, bb in zip(rows, offs, hb):
+        if bb == 16:
+            continue
+        rb = d * d * int(bb) // 8
+        # row factors are elementwise fp32 arithmetic: bit-identical
+        assert np.array_equal(got[o + rb:o + rb + 4 * d], side.host.bytes[o + rb:o + rb + 4 * d])
+
+
+@pytest.mark.parametrize("case", [
+    ("gdn", 4, 4, 128, [6, 16, 4, 8], "bf16", 6),
+    ("kda", 3, 3, 64, [8, 4, 6], "f32", 4),
+    ("kda", 2, 5, 128, [6, 6, 4, 8, 6], "bf16", 3),
+])
+def test_kra_decode_step_small_full_compare(case):
+    gate, B, H, d, bits, dtype, n_slots = case
+    log("kra step %s" % (case,))
+    wl = W.custom(gate, B, H, d, bits, dtype=dtype, n_slots=n_slots, permute=True, seed=6)
+    side = Side(wl, wl.layers[0], wide_impact(H, d, B))
+    side.gpu.buf.fill_(0xA5)
+    side.host.bytes[:] = 0xA5
+    rows = Hn.rows_all(B, H)
+    side.init_oracle_rows(rows)
+    for t in range(3):
+        side.push_rows(rows)
+        y_gpu, y_ref = side.step(t, rows)
+        pool = side.gpu_pool()
+        check_records(side, rows, pool, "kra step %d" % t)
+        assert Hn.rel_l2(y_gpu, y_ref) <= Hn.Y_REL_L2, t
+        used = np.zeros(pool.size, bool)
+        for sl in side.layer.slot_of:
+            used[sl * side.host.stride:(sl + 1) * side.host.stride] = True
+        assert (pool[~used] == 0xA5).all()
+
+
+@pytest.mark.parametrize("name,n_rows", [("c1", 32), ("c2", 32)])
+def test_kra_trajectory_256_steps(name, n_rows):
+    """256 steps with the key-row-aware fit and scores calibrated from the
+    warm-up inputs: the dequantized state ends within the trajectory bound
+    of the oracle's, and y stays within the per-step bound."""
+    log("%s kra trajectory" % name)
+    wl = W.make(name)
+    layer = wl.layers[0]
+    side = Side(wl, layer, calibrated_impact(wl, layer))
+    side.gpu_warmup_all()
+    rows = sample_rows(wl.B, wl.H, n_rows, seed=2)
+    side.init_oracle_rows(rows)
+    worst_y = 0.0
+    for t in range(256):
+        y_gpu, y_ref = side.step(t, rows)
+        worst_y = max(worst_y, Hn.rel_l2(y_gpu, y_ref))
+    offs, hb = side.rows_offsets(rows)
+    s_gpu = O.records_dequantize(side.gpu_pool(), offs, hb, wl.d, wl.d)
+    s_ref = O.records_dequantize(side.host.bytes, offs, hb, wl.d, wl.d)
+    err = Hn.rel_l2(s_gpu, s_ref)
+    log("%s kra: worst y rel-L2 %.3g, final state rel-L2 %.3g" % (name, worst_y, err))
+    assert worst_y <= Hn.Y_REL_L2
+    assert err <= Hn.STATE_REL_L2
