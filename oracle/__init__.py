@@ -56,6 +56,17 @@ def lib():
         L.sqo_unpack_row.argtypes = [i32, i32, vp, vp]
         L.sqo_quantize.restype = None
         L.sqo_quantize.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+        L.sqo_quantize_rows.restype = None
+        L.sqo_quantize_rows.argtypes = [vp, i32, i32, vp, vp, vp, vp]
+        L.sqo_record_bytes_rows.restype = ctypes.c_int64
+        L.sqo_record_bytes_rows.argtypes = [vp, i32, i32]
+        L.sqo_record_pack_rows.restype = i32
+        L.sqo_record_pack_rows.argtypes = [vp, i32, i32, vp, vp, vp, vp]
+        L.sqo_record_unpack_rows.restype = i32
+        L.sqo_record_unpack_rows.argtypes = [vp, i32, i32, vp, vp, vp, vp]
+        L.sqo_quant_step_codes_rows.restype = None
+        L.sqo_quant_step_codes_rows.argtypes = [i32, vp, i32, i32, vp, vp, vp, vp, vp, vp, f32,
+                                                vp, vp, vp]
         L.sqo_quantize_kra.restype = None
         L.sqo_quantize_kra.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
         L.sqo_reconstruct_f64.restype = None
@@ -72,12 +83,12 @@ def lib():
         L.sqo_record_pack.restype = i32
         L.sqo_record_pack.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.sqo_records_quantize.restype = i32
-        L.sqo_records_quantize.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, i32]
+        L.sqo_records_quantize.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, i32]
         L.sqo_records_dequantize.restype = i32
-        L.sqo_records_dequantize.argtypes = [i32, i32, i32, vp, vp, vp, vp, i32]
+        L.sqo_records_dequantize.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, i32]
         L.sqo_records_step.restype = i32
         L.sqo_records_step.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
-                                       vp, vp, i32]
+                                       vp, vp, vp, i32]
         L.sqo_f64_step.restype = i32
         L.sqo_f64_step.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32]
         L.sqo_f32_step.restype = i32
@@ -148,6 +159,47 @@ def quantize(bits: int, S) -> tuple:
     r = np.empty(dk, np.float32)
     c = np.empty(dv, np.float32)
     lib().sqo_quantize(bits, dk, dv, _p(S), _p(Q), _p(r), _p(c))
+    return Q, r, c
+
+
+def quantize_rows(row_bits, S) -> tuple:
+    """The closed rule with a width per key row (row_bits [dk] in {4, 6, 8})."""
+    S = _c(S, np.float32)
+    rb = _c(row_bits, np.uint8)
+    dk, dv = S.shape
+    assert rb.shape == (dk,)
+    Q = np.empty((dk, dv), np.int32)
+    r = np.empty(dk, np.float32)
+    c = np.empty(dv, np.float32)
+    lib().sqo_quantize_rows(_p(rb), dk, dv, _p(S), _p(Q), _p(r), _p(c))
+    return Q, r, c
+
+
+def record_bytes_rows(row_bits, dv: int) -> int:
+    rb = _c(row_bits, np.uint8)
+    return int(lib().sqo_record_bytes_rows(_p(rb), rb.size, dv))
+
+
+def record_pack_rows(row_bits, Q, r, c) -> np.ndarray:
+    rb = _c(row_bits, np.uint8)
+    Q = _c(Q, np.int32)
+    dk, dv = Q.shape
+    rec = np.zeros(record_bytes_rows(rb, dv), np.uint8)
+    r = _c(r, np.float32)
+    c = _c(c, np.float32)
+    if lib().sqo_record_pack_rows(_p(rb), dk, dv, _p(Q), _p(r), _p(c), _p(rec)) != 0:
+        raise ValueError("code out of range")
+    return rec
+
+
+def record_unpack_rows(row_bits, dv, rec) -> tuple:
+    rb = _c(row_bits, np.uint8)
+    rec = _c(rec, np.uint8)
+    dk = rb.size
+    Q = np.empty((dk, dv), np.int32)
+    r = np.empty(dk, np.float32)
+    c = np.empty(dv, np.float32)
+    lib().sqo_record_unpack_rows(_p(rb), dk, dv, _p(rec), _p(Q), _p(r), _p(c))
     return Q, r, c
 
 
@@ -234,6 +286,14 @@ def record_unpack(bits, dk, dv, rec) -> tuple:
 
 
 # ---------------------------------------------------------------- batches
+def _rows(row_bits, n, dk):
+    if row_bits is None:
+        return None
+    rb = _c(row_bits, np.uint8)
+    assert rb.size == n * dk
+    return rb
+
+
 def _imp(imp, n, dk):
     if imp is None:
         return None
@@ -242,43 +302,47 @@ def _imp(imp, n, dk):
     return imp
 
 
-def records_quantize(base: np.ndarray, offs, bits, S, dk, dv, imp=None):
-    """imp [n, dk]: row-impact scores per record (key-row-aware fit), or None."""
+def records_quantize(base: np.ndarray, offs, bits, S, dk, dv, imp=None, row_bits=None):
+    """imp [n, dk]: row-impact scores per record (key-row-aware fit), or None;
+    row_bits [n, dk]: key-row widths of the records whose bits are 0."""
     offs = _c(offs, np.int64)
     bits = _c(bits, np.uint8)
     S = _c(S, np.float32)
     imp = _imp(imp, offs.size, dk)
+    rb = _rows(row_bits, offs.size, dk)
     assert base.dtype == np.uint8 and base.flags.c_contiguous
     assert S.size == offs.size * dk * dv
     if lib().sqo_records_quantize(offs.size, dk, dv, _p(bits), _p(offs), _p(base), _p(S),
-                                  _p(imp), n_threads()) != 0:
+                                  _p(imp), _p(rb), n_threads()) != 0:
         raise ValueError("bad arguments")
 
 
-def records_dequantize(base: np.ndarray, offs, bits, dk, dv) -> np.ndarray:
+def records_dequantize(base: np.ndarray, offs, bits, dk, dv, row_bits=None) -> np.ndarray:
     offs = _c(offs, np.int64)
     bits = _c(bits, np.uint8)
     S = np.empty((offs.size, dk, dv), np.float32)
     base = _c(base, np.uint8)
+    rb = _rows(row_bits, offs.size, dk)
     if lib().sqo_records_dequantize(offs.size, dk, dv, _p(bits), _p(offs), _p(base),
-                                    _p(S), n_threads()) != 0:
+                                    _p(S), _p(rb), n_threads()) != 0:
         raise ValueError("bad arguments")
     return S
 
 
 def records_step(kda: bool, base: np.ndarray, offs, bits, dk, dv, q, k, v, beta, g,
-                 imp=None) -> np.ndarray:
+                 imp=None, row_bits=None) -> np.ndarray:
     """Quantized decode step, in place on the records at base + offs[row]; returns y (f64).
-    imp [n, dk]: requantize with the key-row-aware fit."""
+    imp [n, dk]: requantize with the key-row-aware fit; row_bits as for records_quantize."""
     offs = _c(offs, np.int64)
     bits = _c(bits, np.uint8)
     n = offs.size
     imp = _imp(imp, n, dk)
+    rb = _rows(row_bits, n, dk)
     assert base.dtype == np.uint8 and base.flags.c_contiguous
     y = np.empty((n, dv), np.float64)
     q, k, v, beta, g = (_c(x, np.float32) for x in (q, k, v, beta, g))
     if lib().sqo_records_step(int(kda), n, dk, dv, _p(bits), _p(offs), _p(base), _p(q), _p(k),
-                              _p(v), _p(beta), _p(g), _p(imp), _p(y), n_threads()) != 0:
+                              _p(v), _p(beta), _p(g), _p(imp), _p(rb), _p(y), n_threads()) != 0:
         raise ValueError("bad arguments")
     return y
 

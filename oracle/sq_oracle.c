@@ -67,6 +67,14 @@ int64_t sqo_record_bytes(int bits, int dk, int dv) {
     return (int64_t)dk * sqo_row_bytes(bits, dv) + 4 * (int64_t)dk + 4 * (int64_t)dv;
 }
 
+/* A record whose key rows have their own widths (in {4, 6, 8}): the rows'
+ * code streams back to back, then r[d_k], c[d_v]. */
+int64_t sqo_record_bytes_rows(const uint8_t *row_bits, int dk, int dv) {
+    int64_t n = 4 * (int64_t)dk + 4 * (int64_t)dv;
+    for (int i = 0; i < dk; ++i) n += sqo_row_bytes(row_bits[i], dv);
+    return n;
+}
+
 /* ------------------------------------------------------------------ */
 /* IEEE binary16 <-> binary32, from the format's definition             */
 /* ------------------------------------------------------------------ */
@@ -177,9 +185,14 @@ void sqo_unpack_row(int bits, int n, const uint8_t *in, int32_t *codes) {
  * The last product is taken exactly (in FP64, where the product of two fp32
  * values is exact), so each code is the level nearest to the scaled entry
  * s_ij / r_i.
+ * Per-key-row widths (blog.ontle.kr, allocation paragraph: for KDA the unit
+ * of the bit allocation is a single key row): row i uses its own qmax_i in
+ * r_i = m_i / qmax_i; the column scales do not depend on the widths, so each
+ * row's codes and r_i equal those of a uniform quantization of the same
+ * state at that row's width.  sqo_quantize is the all-rows-equal case.
  */
-void sqo_quantize(int bits, int dk, int dv, const float *S, int32_t *Q, float *r, float *c) {
-    const float qmax = (float)sqo_qmax(bits);
+void sqo_quantize_rows(const uint8_t *row_bits, int dk, int dv, const float *S, int32_t *Q,
+                       float *r, float *c) {
     float *ic = (float *)malloc(sizeof(float) * (size_t)dv);
     for (int j = 0; j < dv; ++j) {
         float m = 0.0f;
@@ -196,6 +209,7 @@ void sqo_quantize(int bits, int dk, int dv, const float *S, int32_t *Q, float *r
         }
     }
     for (int i = 0; i < dk; ++i) {
+        const float qmax = (float)sqo_qmax(row_bits[i]);
         float m = 0.0f;
         for (int j = 0; j < dv; ++j) {
             const float t = fabsf(S[(size_t)i * dv + j]) * ic[j];
@@ -220,6 +234,13 @@ void sqo_quantize(int bits, int dk, int dv, const float *S, int32_t *Q, float *r
         }
     }
     free(ic);
+}
+
+void sqo_quantize(int bits, int dk, int dv, const float *S, int32_t *Q, float *r, float *c) {
+    uint8_t *rb = (uint8_t *)malloc((size_t)dk);
+    memset(rb, bits, (size_t)dk);
+    sqo_quantize_rows(rb, dk, dv, S, Q, r, c);
+    free(rb);
 }
 
 /*
@@ -377,9 +398,9 @@ static void gate_alpha(int kda, int dk, const float *g, double *alpha) {
  * (hyper.ai "Method" para 1: the state is updated in floating point and the
  * output computed, then the updated state is quantized for storage).
  */
-void sqo_quant_step_codes(int kda, int bits, int dk, int dv, int32_t *Q, float *r, float *c,
-                          const float *q, const float *k, const float *v, float beta,
-                          const float *g, const float *imp, double *y) {
+void sqo_quant_step_codes_rows(int kda, const uint8_t *row_bits, int dk, int dv, int32_t *Q,
+                               float *r, float *c, const float *q, const float *k, const float *v,
+                               float beta, const float *g, const float *imp, double *y) {
     const size_t n = (size_t)dk * dv;
     float *S = (float *)malloc(sizeof(float) * n);
     double *Sd = (double *)malloc(sizeof(double) * n);
@@ -395,34 +416,62 @@ void sqo_quant_step_codes(int kda, int bits, int dk, int dv, int32_t *Q, float *
     sqo_gated_delta_f64(dk, dv, Sd, alpha, qd, kd, vd, (double)beta, y);
     for (size_t e = 0; e < n; ++e) S[e] = (float)Sd[e];
     if (imp)
-        sqo_quantize_kra(bits, dk, dv, S, imp, Q, r, c);
+        sqo_quantize_kra(row_bits[0], dk, dv, S, imp, Q, r, c); /* uniform widths only */
     else
-        sqo_quantize(bits, dk, dv, S, Q, r, c);
+        sqo_quantize_rows(row_bits, dk, dv, S, Q, r, c);
     free(S);
     free(Sd);
     free(vec);
+}
+
+void sqo_quant_step_codes(int kda, int bits, int dk, int dv, int32_t *Q, float *r, float *c,
+                          const float *q, const float *k, const float *v, float beta,
+                          const float *g, const float *imp, double *y) {
+    uint8_t *rb = (uint8_t *)malloc((size_t)dk);
+    memset(rb, bits, (size_t)dk);
+    sqo_quant_step_codes_rows(kda, rb, dk, dv, Q, r, c, q, k, v, beta, g, imp, y);
+    free(rb);
 }
 
 /* ------------------------------------------------------------------ */
 /* Records                                                             */
 /* ------------------------------------------------------------------ */
 
-int sqo_record_unpack(int bits, int dk, int dv, const uint8_t *rec, int32_t *Q, float *r, float *c) {
-    const int64_t rb = sqo_row_bytes(bits, dv);
-    for (int i = 0; i < dk; ++i) sqo_unpack_row(bits, dv, rec + (size_t)i * rb, Q + (size_t)i * dv);
-    memcpy(r, rec + (size_t)dk * rb, sizeof(float) * (size_t)dk);
-    memcpy(c, rec + (size_t)dk * rb + 4 * (size_t)dk, sizeof(float) * (size_t)dv);
+int sqo_record_unpack_rows(const uint8_t *row_bits, int dk, int dv, const uint8_t *rec, int32_t *Q,
+                           float *r, float *c) {
+    size_t pos = 0;
+    for (int i = 0; i < dk; ++i) {
+        sqo_unpack_row(row_bits[i], dv, rec + pos, Q + (size_t)i * dv);
+        pos += (size_t)sqo_row_bytes(row_bits[i], dv);
+    }
+    memcpy(r, rec + pos, sizeof(float) * (size_t)dk);
+    memcpy(c, rec + pos + 4 * (size_t)dk, sizeof(float) * (size_t)dv);
     return 0;
+}
+
+int sqo_record_pack_rows(const uint8_t *row_bits, int dk, int dv, const int32_t *Q, const float *r,
+                         const float *c, uint8_t *rec) {
+    size_t pos = 0;
+    for (int i = 0; i < dk; ++i) {
+        if (sqo_pack_row(row_bits[i], dv, Q + (size_t)i * dv, rec + pos) != 0) return -1;
+        pos += (size_t)sqo_row_bytes(row_bits[i], dv);
+    }
+    memcpy(rec + pos, r, sizeof(float) * (size_t)dk);
+    memcpy(rec + pos + 4 * (size_t)dk, c, sizeof(float) * (size_t)dv);
+    return 0;
+}
+
+int sqo_record_unpack(int bits, int dk, int dv, const uint8_t *rec, int32_t *Q, float *r, float *c) {
+    uint8_t rb[1024];
+    memset(rb, bits, (size_t)dk);
+    return sqo_record_unpack_rows(rb, dk, dv, rec, Q, r, c);
 }
 
 int sqo_record_pack(int bits, int dk, int dv, const int32_t *Q, const float *r, const float *c,
                     uint8_t *rec) {
-    const int64_t rb = sqo_row_bytes(bits, dv);
-    for (int i = 0; i < dk; ++i)
-        if (sqo_pack_row(bits, dv, Q + (size_t)i * dv, rec + (size_t)i * rb) != 0) return -1;
-    memcpy(rec + (size_t)dk * rb, r, sizeof(float) * (size_t)dk);
-    memcpy(rec + (size_t)dk * rb + 4 * (size_t)dk, c, sizeof(float) * (size_t)dv);
-    return 0;
+    uint8_t rb[1024];
+    memset(rb, bits, (size_t)dk);
+    return sqo_record_pack_rows(rb, dk, dv, Q, r, c, rec);
 }
 
 /* FP16 pivot record: one step.  FP64 step on the exactly widened state, S'
@@ -466,6 +515,7 @@ typedef struct {
     const float *q, *k, *v, *beta, *g;
     double *y;
     const float *imp; /* [n, dk] row-impact scores, or NULL for the closed rule */
+    const uint8_t *row_bits; /* [n, dk] per-key-row widths of records with bits 0 */
 } job_t;
 
 enum { OP_QUANT = 0, OP_DEQUANT = 1, OP_STEP = 2, OP_F64STEP = 3, OP_F32STEP = 4 };
@@ -475,6 +525,12 @@ static void run_row(const job_t *J, int row) {
     const size_t n = (size_t)dk * dv;
     const float *g = J->g ? J->g + (J->kda ? (size_t)row * dk : (size_t)row) : NULL;
     const float *imp = J->imp ? J->imp + (size_t)row * dk : NULL;
+    /* the record's row widths: per key row (bits 0) or all equal */
+    uint8_t rbw[1024];
+    if (J->bits && J->bits[row] == 0)
+        memcpy(rbw, J->row_bits + (size_t)row * dk, (size_t)dk);
+    else if (J->bits)
+        memset(rbw, J->bits[row], (size_t)dk);
     switch (J->op) {
     case OP_QUANT: {
         uint8_t *rec = J->base + J->offs[row];
@@ -488,8 +544,8 @@ static void run_row(const job_t *J, int row) {
         if (imp)
             sqo_quantize_kra(J->bits[row], dk, dv, J->S32 + (size_t)row * n, imp, Q, rr, cc);
         else
-            sqo_quantize(J->bits[row], dk, dv, J->S32 + (size_t)row * n, Q, rr, cc);
-        sqo_record_pack(J->bits[row], dk, dv, Q, rr, cc, rec);
+            sqo_quantize_rows(rbw, dk, dv, J->S32 + (size_t)row * n, Q, rr, cc);
+        sqo_record_pack_rows(rbw, dk, dv, Q, rr, cc, rec);
         free(Q);
         break;
     }
@@ -502,7 +558,7 @@ static void run_row(const job_t *J, int row) {
         }
         int32_t *Q = (int32_t *)malloc(sizeof(int32_t) * n);
         float rr[1024], cc[1024];
-        sqo_record_unpack(J->bits[row], dk, dv, rec, Q, rr, cc);
+        sqo_record_unpack_rows(rbw, dk, dv, rec, Q, rr, cc);
         sqo_dequantize(dk, dv, Q, rr, cc, J->S32 + (size_t)row * n);
         free(Q);
         break;
@@ -517,11 +573,11 @@ static void run_row(const job_t *J, int row) {
         }
         int32_t *Q = (int32_t *)malloc(sizeof(int32_t) * n);
         float rr[1024], cc[1024];
-        sqo_record_unpack(bits, dk, dv, rec, Q, rr, cc);
-        sqo_quant_step_codes(J->kda, bits, dk, dv, Q, rr, cc, J->q + (size_t)row * dk,
-                             J->k + (size_t)row * dk, J->v + (size_t)row * dv, J->beta[row], g,
-                             imp, J->y + (size_t)row * dv);
-        sqo_record_pack(bits, dk, dv, Q, rr, cc, rec);
+        sqo_record_unpack_rows(rbw, dk, dv, rec, Q, rr, cc);
+        sqo_quant_step_codes_rows(J->kda, rbw, dk, dv, Q, rr, cc, J->q + (size_t)row * dk,
+                                  J->k + (size_t)row * dk, J->v + (size_t)row * dv, J->beta[row],
+                                  g, imp, J->y + (size_t)row * dv);
+        sqo_record_pack_rows(rbw, dk, dv, Q, rr, cc, rec);
         free(Q);
         break;
     }
@@ -575,41 +631,55 @@ static int run_rows(job_t proto, int n_rows, int n_threads) {
     return 0;
 }
 
-static int check_bits(int n, const uint8_t *bits) {
-    for (int i = 0; i < n; ++i)
-        if (bits[i] != 4 && bits[i] != 6 && bits[i] != 8 && bits[i] != 16) return -1;
+/* Record widths 4, 6, 8, 16, or 0 with per-key-row widths in {4, 6, 8}
+ * (which the key-row-aware fit does not take). */
+static int check_bits(int n, int dk, const uint8_t *bits, const uint8_t *row_bits,
+                      const float *imp) {
+    for (int i = 0; i < n; ++i) {
+        if (bits[i] == 0) {
+            if (!row_bits || imp) return -1;
+            for (int r = 0; r < dk; ++r) {
+                const uint8_t b = row_bits[(size_t)i * dk + r];
+                if (b != 4 && b != 6 && b != 8) return -1;
+            }
+        } else if (bits[i] != 4 && bits[i] != 6 && bits[i] != 8 && bits[i] != 16) {
+            return -1;
+        }
+    }
     return 0;
 }
 
 
 /* Quantize fp32 states S[n, dk, dv] into the records at base + offs[row];
- * imp [n, dk] selects the key-row-aware fit (NULL: the closed rule). */
+ * imp [n, dk] selects the key-row-aware fit (NULL: the closed rule);
+ * row_bits [n, dk] gives the key-row widths of records with bits 0. */
 int sqo_records_quantize(int n, int dk, int dv, const uint8_t *bits, const int64_t *offs,
-                         uint8_t *base, const float *S, const float *imp, int n_threads) {
-    if (check_bits(n, bits)) return -1;
+                         uint8_t *base, const float *S, const float *imp, const uint8_t *row_bits,
+                         int n_threads) {
+    if (check_bits(n, dk, bits, row_bits, imp)) return -1;
     job_t J = {OP_QUANT, 0, dk, dv, 0, 0, bits, offs, base, (float *)S, NULL,
-               NULL, NULL, NULL, NULL, NULL, NULL, imp};
+               NULL, NULL, NULL, NULL, NULL, NULL, imp, row_bits};
     return run_rows(J, n, n_threads);
 }
 
 /* Dequantize the records into S[n, dk, dv]. */
 int sqo_records_dequantize(int n, int dk, int dv, const uint8_t *bits, const int64_t *offs,
-                           const uint8_t *base, float *S, int n_threads) {
-    if (check_bits(n, bits)) return -1;
+                           const uint8_t *base, float *S, const uint8_t *row_bits, int n_threads) {
+    if (check_bits(n, dk, bits, row_bits, NULL)) return -1;
     job_t J = {OP_DEQUANT, 0, dk, dv, 0, 0, bits, offs, (uint8_t *)base, S, NULL,
-               NULL, NULL, NULL, NULL, NULL, NULL, NULL};
+               NULL, NULL, NULL, NULL, NULL, NULL, NULL, row_bits};
     return run_rows(J, n, n_threads);
 }
 
 /* One quantized decode step, in place on the records; y[n, dv] in double;
- * imp [n, dk] as for sqo_records_quantize. */
+ * imp and row_bits as for sqo_records_quantize. */
 int sqo_records_step(int kda, int n, int dk, int dv, const uint8_t *bits, const int64_t *offs,
                      uint8_t *base, const float *q, const float *k, const float *v,
-                     const float *beta, const float *g, const float *imp, double *y,
-                     int n_threads) {
-    if (check_bits(n, bits)) return -1;
+                     const float *beta, const float *g, const float *imp,
+                     const uint8_t *row_bits, double *y, int n_threads) {
+    if (check_bits(n, dk, bits, row_bits, imp)) return -1;
     job_t J = {OP_STEP, kda, dk, dv, 0, 0, bits, offs, base, NULL, NULL, q, k, v, beta, g, y,
-               imp};
+               imp, row_bits};
     return run_rows(J, n, n_threads);
 }
 
@@ -617,7 +687,7 @@ int sqo_records_step(int kda, int n, int dk, int dv, const uint8_t *bits, const 
 int sqo_f64_step(int kda, int n, int dk, int dv, double *S, const float *q, const float *k,
                  const float *v, const float *beta, const float *g, double *y, int n_threads) {
     job_t J = {OP_F64STEP, kda, dk, dv, 0, 0, NULL, NULL, NULL, NULL, S, q, k, v, beta, g, y,
-               NULL};
+               NULL, NULL};
     return run_rows(J, n, n_threads);
 }
 
@@ -625,6 +695,6 @@ int sqo_f64_step(int kda, int n, int dk, int dv, double *S, const float *q, cons
 int sqo_f32_step(int kda, int n, int dk, int dv, float *S, const float *q, const float *k,
                  const float *v, const float *beta, const float *g, double *y, int n_threads) {
     job_t J = {OP_F32STEP, kda, dk, dv, 0, 0, NULL, NULL, NULL, S, NULL, q, k, v, beta, g, y,
-               NULL};
+               NULL, NULL};
     return run_rows(J, n, n_threads);
 }

@@ -744,3 +744,86 @@ def test_kra_drivers_and_step_compose():
         Q2, r2, c2 = O.quantize_kra(b, Sp.astype(np.float32), imp[i])
         assert np.array_equal(base[offs[i]:offs[i] + sizes[i]], O.record_pack(b, Q2, r2, c2))
         assert np.array_equal(y[i], yw)
+
+
+# ------------------------------------------------------------------ per-key-row widths
+def test_rows_quantizer_selects_rows_of_uniform_quantizers():
+    """With a width per key row, the column scales do not depend on the
+    widths and row i only on its own width: codes and r_i of row i equal
+    those of the uniform quantizer at width w_i (a transposed or shifted
+    width index fails this)."""
+    rng = np.random.default_rng(61)
+    dk, dv = 24, 20
+    S = _rand_state(rng, dk, dv)
+    w = rng.choice([4, 6, 8], dk).astype(np.uint8)
+    Q, r, c = O.quantize_rows(w, S)
+    for b in (4, 6, 8):
+        Qb, rb, cb = O.quantize(b, S)
+        assert np.array_equal(c, cb)
+        sel = w == b
+        assert np.array_equal(Q[sel], Qb[sel]) and np.array_equal(r[sel], rb[sel])
+    Qu, ru, cu = O.quantize_rows(np.full(dk, 6, np.uint8), S)
+    Q6, r6, c6 = O.quantize(6, S)
+    assert np.array_equal(Qu, Q6) and np.array_equal(ru, r6) and np.array_equal(cu, c6)
+
+
+def test_rows_record_layout_and_roundtrip():
+    rng = np.random.default_rng(62)
+    dk, dv = 16, 32
+    w = np.sort(rng.choice([4, 6, 8], dk)).astype(np.uint8)
+    S = _rand_state(rng, dk, dv)
+    Q, r, c = O.quantize_rows(w, S)
+    rec = O.record_pack_rows(w, Q, r, c)
+    assert rec.size == sum(dv * int(b) // 8 for b in w) + 4 * (dk + dv)
+    # the rows' streams back to back, each in the uniform row format
+    pos = 0
+    for i, b in enumerate(w):
+        n = dv * int(b) // 8
+        assert np.array_equal(rec[pos:pos + n], O.pack_row(int(b), Q[i]))
+        pos += n
+    assert np.array_equal(rec[pos:pos + 4 * dk].view(np.float32), r)
+    Q2, r2, c2 = O.record_unpack_rows(w, dv, rec)
+    assert np.array_equal(Q2, Q) and np.array_equal(r2, r) and np.array_equal(c2, c)
+
+
+def test_rows_drivers_and_step_compose():
+    """Records with bits 0 take their key-row widths from row_bits; one step
+    is the FP64 step on the reconstruction, rounded to fp32, then the
+    per-row quantizer."""
+    rng = np.random.default_rng(63)
+    d = 16
+    widths = [np.sort(rng.choice([4, 6, 8], d)).astype(np.uint8) for _ in range(3)]
+    bits = np.array([0, 6, 0], np.uint8)
+    row_bits = np.stack([widths[0], np.full(d, 6, np.uint8), widths[2]])
+    S = np.stack([_rand_state(rng, d, d) for _ in range(3)])
+    sizes = [O.record_bytes_rows(row_bits[i], d) for i in range(3)]
+    assert sizes[1] == O.record_bytes(6, d, d)
+    offs = np.array([0, sizes[0], sizes[0] + sizes[1]], np.int64)
+    base = np.zeros(sum(sizes), np.uint8)
+    O.records_quantize(base, offs, bits, S, d, d, row_bits=row_bits)
+    for i in range(3):
+        Q, r, c = O.quantize_rows(row_bits[i], S[i])
+        assert np.array_equal(base[offs[i]:offs[i] + sizes[i]], O.record_pack_rows(row_bits[i], Q, r, c))
+    back = O.records_dequantize(base, offs, bits, d, d, row_bits=row_bits)
+    for i in range(3):
+        assert np.array_equal(back[i], O.dequantize(*O.quantize_rows(row_bits[i], S[i])))
+    x = [_inputs(rng, d, d, kda=True) for _ in range(3)]
+    q = np.stack([t[0] for t in x]).astype(np.float32)
+    k = np.stack([t[1] for t in x]).astype(np.float32)
+    v = np.stack([t[2] for t in x]).astype(np.float32)
+    beta = np.array([t[3] for t in x], np.float32)
+    g = np.log(np.stack([t[4] for t in x])).astype(np.float32)
+    before = base.copy()
+    y = O.records_step(True, base, offs, bits, d, d, q, k, v, beta, g, row_bits=row_bits)
+    for i in range(3):
+        Q, r, c = O.record_unpack_rows(row_bits[i], d, before[offs[i]:offs[i] + sizes[i]])
+        alpha = np.exp(g[i].astype(np.float64)).astype(np.float32).astype(np.float64)
+        Sp, yw = O.gated_delta_f64(O.reconstruct_f64(Q, r, c), alpha, q[i], k[i], v[i], beta[i])
+        Q2, r2, c2 = O.quantize_rows(row_bits[i], Sp.astype(np.float32))
+        assert np.array_equal(base[offs[i]:offs[i] + sizes[i]],
+                              O.record_pack_rows(row_bits[i], Q2, r2, c2))
+        assert np.array_equal(y[i], yw)
+    with pytest.raises(ValueError):   # bits 0 needs row widths
+        O.records_quantize(base, offs, bits, S, d, d)
+    with pytest.raises(ValueError):   # and takes no impact scores
+        O.records_quantize(base, offs, bits, S, d, d, imp=np.ones((3, d)), row_bits=row_bits)
