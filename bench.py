@@ -281,6 +281,34 @@ def main():
                 "achieved_GBps": kb / (k_launch * 1e-3) / 1e9,
                 "hbm_frac": kb / (k_launch * 1e-3) / 1e9 / HBM_PEAK_GBS}
             eprint("kda mixed: %.2f us/step, %.1f GB/s" % (k_ms * 1e3, variants["kda_mixed_4_6_8"]["achieved_GBps"]))
+            # the same KDA step with per-key-row widths: 4/6/8 bits on 25/50/25 %
+            # of every head's key rows (the KDA unit of the allocation)
+            rb, _ = W.row_widths_by_lifetime(lk.gate_rates)
+            pool_r = Q.StatePool(wl.n_slots, H, d, [0] * H, "kda", device=dev, row_bits=rb)
+            str_ = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
+            str_.copy_(state[slot_l.long()])
+            pool_r.quant_state(slot_k, str_)
+            del str_
+
+            def run_r(n, ev=None):
+                for i in range(n):
+                    x = kin[i % 4]
+                    if ev is not None:
+                        ev[i][0].record(stream)
+                    pool_r.decode_step(slot_k, x["q"], x["k"], x["v"], x["beta"], x["g"], y)
+                    if ev is not None:
+                        ev[i][1].record(stream)
+            p_ms, p_launch = timed(None, None, run_r)
+            # 6 bits on average per head: the 6-bit byte model with the KDA gate
+            pb = algo_bytes_per_step(B, H, d, [6] * H, "kda")
+            variants["kda_per_row_4_6_8"] = {
+                "updates_per_s": updates / (p_ms * 1e-3), "us_per_step": p_ms * 1e3,
+                "us_per_launch": p_launch * 1e3, "algo_bytes_per_step": pb,
+                "achieved_GBps": pb / (p_launch * 1e-3) / 1e9,
+                "hbm_frac": pb / (p_launch * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            eprint("kda per-row widths: %.2f us/step, %.1f GB/s"
+                   % (p_ms * 1e3, variants["kda_per_row_4_6_8"]["achieved_GBps"]))
+            pool_r.close()
             pool_k.close()
     del state
 
@@ -477,28 +505,49 @@ def trajectory(args, dev):
             kra = {"uniform_6_key_row_aware",
                    "lifetime_6+%d_fp16_pivots_key_row_aware" % args.pivots}
             imp = torch.from_numpy(impact_from_workload(wl, layer, 16)).to(dev)
+        perms, row_bits = {}, {}
+        if args.allocate and kda:
+            # per-key-row widths (the KDA unit): key channels permuted offline
+            # so each head's rows run from the fastest- to the slowest-decaying
+            # channel; 4/6/8 bits at 25/50/25 % of the rows in that order
+            rb, perm = W.row_widths_by_lifetime(layer.gate_rates)
+            name = "per_row_lifetime_4_6_8"
+            schemes[name] = np.zeros(H, np.uint8)
+            row_bits[name] = rb
+            perms[name] = torch.from_numpy(perm).to(dev)
         pools = {}
         for name, hb in schemes.items():
-            pool = Q.StatePool(B, H, d, [int(b) for b in hb], layer.gate, device=dev)
+            pool = Q.StatePool(B, H, d, [int(b) for b in hb], layer.gate, device=dev,
+                               row_bits=row_bits.get(name))
             if name in kra:
                 pool.set_row_impact(imp)
-            pool.quant_state(ident, state)
+            if name in perms:
+                idx = perms[name][None, :, :, None].expand(B, H, d, d)
+                pool.quant_state(ident, torch.gather(state, 2, idx).contiguous())
+            else:
+                pool.quant_state(ident, state)
             pools[name] = pool
-        layers.append((layer, kda, state, pools, schemes, cal))
+        layers.append((layer, kda, state, pools, schemes, cal, perms))
     torch.cuda.synchronize()
-    errs = {(l.index, n): [] for l, _, _, pools, _, _ in layers for n in pools}
+    errs = {(l.index, n): [] for l, _, _, pools, _, _, _ in layers for n in pools}
     yq = torch.empty((B * H, d), dtype=torch.bfloat16, device=dev)
     yf = torch.empty((B * H, d), dtype=torch.bfloat16, device=dev)
     t0 = time.time()
     for t in range(T):
-        for layer, kda, state, pools, _, _ in layers:
+        for layer, kda, state, pools, _, _, perms in layers:
             x = {k: to_dev(v) for k, v in wl.step_inputs(layer, t).items()}
             Q.sq_f32_decode_step(state, B, H, d, d, int(kda), ident, B, x["q"], x["k"], x["v"],
                                  x["beta"], x["g"], yf)
             b = yf.float()
             nb = torch.linalg.vector_norm(b)
             for name, pool in pools.items():
-                pool.decode_step(ident, x["q"], x["k"], x["v"], x["beta"], x["g"], yq)
+                xi = x
+                if name in perms:  # the same inputs with the key channels permuted
+                    idx = perms[name][None].expand(B, H, d)
+                    xi = dict(x)
+                    for key in ("q", "k", "g"):
+                        xi[key] = torch.gather(x[key].view(B, H, d), 2, idx).reshape(B * H, d)
+                pool.decode_step(ident, xi["q"], xi["k"], xi["v"], xi["beta"], xi["g"], yq)
                 errs[(layer.index, name)].append(
                     float(torch.linalg.vector_norm(yq.float() - b) / nb))
         if t in (0, 15, 63, 255, T - 1) or (t + 1) % 64 == 0:
@@ -507,13 +556,13 @@ def trajectory(args, dev):
                                             time.time() - t0))
     out = {"workload": "c4: GDN + KDA layers, B=1024, H=32, d=128, bf16, %d steps" % T,
            "y_rel_l2_vs_fp32_state": {}}
-    for layer, _, _, pools, schemes, cal in layers:
+    for layer, _, _, pools, schemes, cal, _ in layers:
         per = {}
         for name, pool in pools.items():
             hb = schemes[name]
             e = np.array(errs[(layer.index, name)])
             marks = {str(s): float(e[s - 1]) for s in (1, 16, 64, 256, T) if s <= T}
-            per[name] = {"bits": {str(b): int((hb == b).sum()) for b in (4, 6, 8, 16)
+            per[name] = {"bits": {str(b): int((hb == b).sum()) for b in (0, 4, 6, 8, 16)
                                   if (hb == b).any()},
                          "slot_bytes": int(pool.slot_stride),
                          "at_step": marks, "mean": float(e.mean()), "max": float(e.max())}

@@ -62,7 +62,8 @@
  *    slot_idx must be distinct and in [0, n_slots); slots not listed are
  *    never read or written.  Overlapping calls on the same slots race.
  *  - n = 0 is a valid no-op.
- *  - Supported shapes: d_k = d_v = d in {64, 128}; bits in {4, 6, 8, 16};
+ *  - Supported shapes: d_k = d_v = d in {64, 128}; bits in {4, 6, 8, 16},
+ *    or 0 with per-key-row widths (sq_pool_create_rows);
  *    1 <= n_heads <= 64.  Others return SQ_EUNSUPPORTED.
  *  - NaN or infinite inputs give undefined (but memory-safe) results.
  */
@@ -95,7 +96,8 @@ typedef struct {
     int32_t n_heads;          /* heads per request, 1..64 */
     int32_t d_k;              /* key dimension (rows of the state) */
     int32_t d_v;              /* value dimension (columns), must equal d_k */
-    const uint8_t *head_bits; /* host array [n_heads], each 4, 6, 8 or 16; copied */
+    const uint8_t *head_bits; /* host array [n_heads], each 4, 6, 8 or 16 (0: per-row
+                                 widths, sq_pool_create_rows only); copied */
     sq_gate gate;             /* GDN: g is [n, H]; KDA: g is [n, H, d_k] */
 } sq_pool_desc;
 
@@ -110,6 +112,28 @@ sq_status sq_pool_bytes(const sq_pool_desc *desc, size_t *bytes);
  * touched (initialise slots with sq_quant_state).  *out receives a handle
  * to release with sq_pool_destroy. */
 sq_status sq_pool_create(const sq_pool_desc *desc, void *dev_buf, size_t bytes, sq_pool **out);
+
+/* Per-key-row bit widths (blog.ontle.kr, allocation paragraph: for KDA
+ * models the unit of the bit allocation is a single key row).  Same as
+ * sq_pool_bytes / sq_pool_create, except that a head with head_bits[h] = 0
+ * gives each key row its own width row_bits[h * d_k + i] in {4, 6, 8}
+ * (host array [n_heads][d_k], read during the call; only rows of width-0
+ * heads are read, so it may be NULL when there are none).  Within such a
+ * head the widths must be non-decreasing in i and may change only at rows
+ * that are multiples of 8 (d_k = 128) or 16 (d_k = 64), so that the rows
+ * one wavefront holds share a width.  Grouping the key channels by width is
+ * an offline permutation of the model's key channels (q, k and the KDA gate
+ * alike), which leaves every output unchanged.  Record of such a head: the
+ * rows' code streams back to back (each row in the format of its width),
+ * then r[d_k], c[d_v] fp32, padded to a multiple of 256 bytes.  Row i's
+ * codes use the closed rule with its own qmax (r_i = max_j |s_ij| / qmax_i);
+ * these heads do not take the key-row-aware fit (sq_pool_set_row_impact on
+ * a pool with them returns SQ_EUNSUPPORTED).  Errors: SQ_EINVAL if a
+ * width-0 head has no row_bits, SQ_EUNSUPPORTED for widths outside
+ * {4, 6, 8}, decreasing widths or a change off the 8/16-row grid. */
+sq_status sq_pool_bytes_rows(const sq_pool_desc *desc, const uint8_t *row_bits, size_t *bytes);
+sq_status sq_pool_create_rows(const sq_pool_desc *desc, const uint8_t *row_bits, void *dev_buf,
+                              size_t bytes, sq_pool **out);
 
 /* Release the host handle.  Never frees or touches dev_buf.  NULL is a no-op. */
 sq_status sq_pool_destroy(sq_pool *pool);

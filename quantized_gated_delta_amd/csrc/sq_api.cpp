@@ -22,6 +22,7 @@ struct sq_pool {
     sqk::HeadTable tab;
     int64_t rec_bytes[sqk::kMaxHeads];
     size_t bytes;               // n_slots * slot_stride
+    bool row_mixed;             // some head has per-key-row widths
 };
 
 namespace {
@@ -42,7 +43,32 @@ sq_status hip_fail(hipError_t e, const char *what) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-sq_status check_desc(const sq_pool_desc *d) {
+// Rows of one head with per-key-row widths: non-decreasing widths in
+// {4, 6, 8} that change only at multiples of the rows a wavefront holds per
+// row slot (d / 16 at d = 128, d / 4 at d = 64).  Returns the 4- and 6-bit
+// row counts.
+sq_status row_split(const sq_pool_desc *d, const uint8_t *row_bits, int h, uint8_t *n4,
+                    uint8_t *n6) {
+    const int dk = d->d_k, grain = dk == 128 ? 8 : 16;
+    const uint8_t *w = row_bits + (size_t)h * dk;
+    int c4 = 0, c6 = 0;
+    for (int i = 0; i < dk; ++i) {
+        if (w[i] != 4 && w[i] != 6 && w[i] != 8)
+            return fail(SQ_EUNSUPPORTED, "row_bits[%d][%d] = %d, must be 4, 6 or 8", h, i, w[i]);
+        if (i > 0 && w[i] < w[i - 1])
+            return fail(SQ_EUNSUPPORTED, "row_bits[%d] must be non-decreasing (row %d)", h, i);
+        if (i > 0 && w[i] != w[i - 1] && i % grain != 0)
+            return fail(SQ_EUNSUPPORTED,
+                        "row_bits[%d] changes width at row %d, not a multiple of %d", h, i, grain);
+        c4 += w[i] == 4;
+        c6 += w[i] == 6;
+    }
+    *n4 = (uint8_t)c4;
+    *n6 = (uint8_t)c6;
+    return SQ_OK;
+}
+
+sq_status check_desc(const sq_pool_desc *d, const uint8_t *row_bits = nullptr) {
     if (!d) return fail(SQ_EINVAL, "desc is NULL");
     if (d->n_slots < 1) return fail(SQ_EINVAL, "n_slots must be >= 1 (got %d)", d->n_slots);
     if (d->n_heads < 1 || d->n_heads > sqk::kMaxHeads)
@@ -56,17 +82,35 @@ sq_status check_desc(const sq_pool_desc *d) {
     if (!d->head_bits) return fail(SQ_EINVAL, "head_bits is NULL");
     for (int h = 0; h < d->n_heads; ++h) {
         const int b = d->head_bits[h];
-        if (b != 4 && b != 6 && b != 8 && b != 16)
+        if (b == 0) {
+            if (!row_bits)
+                return fail(SQ_EINVAL, "head_bits[%d] = 0 needs per-row widths (row_bits)", h);
+            uint8_t n4, n6;
+            sq_status st = row_split(d, row_bits, h, &n4, &n6);
+            if (st) return st;
+        } else if (b != 4 && b != 6 && b != 8 && b != 16) {
             return fail(SQ_EUNSUPPORTED, "head_bits[%d] = %d, must be 4, 6, 8 or 16", h, b);
+        }
     }
     return SQ_OK;
 }
 
-// Layout: per slot, head records back to back in head order.
-int64_t layout(const sq_pool_desc *d, int64_t *off, int64_t *rec) {
+// Layout: per slot, head records back to back in head order.  row_bits is
+// read only for heads whose head_bits is 0 (already validated).
+int64_t layout(const sq_pool_desc *d, const uint8_t *row_bits, int64_t *off, int64_t *rec,
+               uint8_t *n4 = nullptr, uint8_t *n6 = nullptr) {
     int64_t pos = 0;
     for (int h = 0; h < d->n_heads; ++h) {
-        const int64_t rb = sqk::record_bytes(d->head_bits[h], d->d_k);
+        int64_t rb;
+        uint8_t a = 0, b = 0;
+        if (d->head_bits[h] == 0) {
+            row_split(d, row_bits, h, &a, &b);
+            rb = sqk::record_bytes_rows(a, b, d->d_k);
+        } else {
+            rb = sqk::record_bytes(d->head_bits[h], d->d_k);
+        }
+        if (n4) n4[h] = a;
+        if (n6) n6[h] = b;
         if (off) off[h] = pos;
         if (rec) rec[h] = rb;
         pos += rb;
@@ -115,22 +159,27 @@ const char *sq_last_error(void) { return g_err; }
 
 const char *sq_version(void) { return "sq 0.1 (gfx950)"; }
 
-sq_status sq_pool_bytes(const sq_pool_desc *desc, size_t *bytes) {
-    sq_status st = check_desc(desc);
+sq_status sq_pool_bytes_rows(const sq_pool_desc *desc, const uint8_t *row_bits, size_t *bytes) {
+    sq_status st = check_desc(desc, row_bits);
     if (st) return st;
     if (!bytes) return fail(SQ_EINVAL, "bytes is NULL");
-    const int64_t stride = layout(desc, nullptr, nullptr);
+    const int64_t stride = layout(desc, row_bits, nullptr, nullptr);
     if ((uint64_t)desc->n_slots > (uint64_t)INT64_MAX / (uint64_t)stride)
         return fail(SQ_ENOMEM, "pool size overflows");
     *bytes = (size_t)((int64_t)desc->n_slots * stride);
     return SQ_OK;
 }
 
-sq_status sq_pool_create(const sq_pool_desc *desc, void *dev_buf, size_t bytes, sq_pool **out) {
+sq_status sq_pool_bytes(const sq_pool_desc *desc, size_t *bytes) {
+    return sq_pool_bytes_rows(desc, nullptr, bytes);
+}
+
+sq_status sq_pool_create_rows(const sq_pool_desc *desc, const uint8_t *row_bits, void *dev_buf,
+                              size_t bytes, sq_pool **out) {
     if (!out) return fail(SQ_EINVAL, "out is NULL");
     *out = nullptr;
     size_t need = 0;
-    sq_status st = sq_pool_bytes(desc, &need);
+    sq_status st = sq_pool_bytes_rows(desc, row_bits, &need);
     if (st) return st;
     if (!dev_buf) return fail(SQ_EINVAL, "dev_buf is NULL");
     if (!aligned(dev_buf, 256)) return fail(SQ_EINVAL, "dev_buf is not 256-byte aligned");
@@ -141,8 +190,10 @@ sq_status sq_pool_create(const sq_pool_desc *desc, void *dev_buf, size_t bytes, 
     p->desc = *desc;
     std::memcpy(p->bits, desc->head_bits, (size_t)desc->n_heads);
     p->desc.head_bits = p->bits;
-    const int64_t stride = layout(desc, p->tab.off, p->rec_bytes);
+    const int64_t stride = layout(desc, row_bits, p->tab.off, p->rec_bytes, p->tab.n4, p->tab.n6);
     std::memcpy(p->tab.bits, p->bits, (size_t)desc->n_heads);
+    for (int h = 0; h < desc->n_heads; ++h) p->row_mixed |= desc->head_bits[h] == 0;
+    p->view.row_mixed = p->row_mixed;
     p->view.base = static_cast<uint8_t *>(dev_buf);
     p->view.slot_stride = stride;
     p->view.n_heads = desc->n_heads;
@@ -150,6 +201,10 @@ sq_status sq_pool_create(const sq_pool_desc *desc, void *dev_buf, size_t bytes, 
     p->bytes = need;
     *out = p;
     return SQ_OK;
+}
+
+sq_status sq_pool_create(const sq_pool_desc *desc, void *dev_buf, size_t bytes, sq_pool **out) {
+    return sq_pool_create_rows(desc, nullptr, dev_buf, bytes, out);
 }
 
 sq_status sq_pool_destroy(sq_pool *pool) {
@@ -171,6 +226,8 @@ sq_status sq_pool_layout(const sq_pool *pool, int64_t *slot_stride, int64_t *hea
 sq_status sq_pool_set_row_impact(sq_pool *pool, const float *impact) {
     if (!pool) return fail(SQ_EINVAL, "pool is NULL");
     if (impact && !aligned(impact, 16)) return fail(SQ_EINVAL, "impact is not 16-byte aligned");
+    if (impact && pool->row_mixed)
+        return fail(SQ_EUNSUPPORTED, "the key-row-aware fit takes heads of uniform width only");
     pool->view.impact = impact;
     return SQ_OK;
 }

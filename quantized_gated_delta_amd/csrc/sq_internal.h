@@ -12,7 +12,9 @@ constexpr int kMaxHeads = 64;
 // Per-head record placement inside one slot of the pool.
 struct HeadTable {
     int64_t off[kMaxHeads];  // byte offset of head h's record within a slot
-    uint8_t bits[kMaxHeads]; // 4, 6, 8, or 16 (FP16 pivot)
+    uint8_t bits[kMaxHeads]; // 4, 6, 8, 16 (FP16 pivot), or 0 (per-key-row widths)
+    uint8_t n4[kMaxHeads];   // bits 0: rows [0, n4) are 4-bit,
+    uint8_t n6[kMaxHeads];   //   [n4, n4 + n6) 6-bit, the rest 8-bit
 };
 
 struct PoolView {
@@ -21,6 +23,7 @@ struct PoolView {
     int32_t n_heads;
     int32_t d;           // d_k == d_v
     const float *impact; // row-impact scores [n_heads, d] (key-row-aware fit) or null
+    int32_t row_mixed;   // some head has per-key-row widths (head bits 0)
 };
 
 // Step inputs; dtype flags: 0 = fp32, 1 = bf16.
@@ -39,6 +42,14 @@ struct StepIO {
 inline int64_t record_bytes(int bits, int d) {
     if (bits == 16) return 2 * (int64_t)d * d;
     return (int64_t)d * d * bits / 8 + 8 * (int64_t)d;
+}
+
+// Bytes of a record with per-key-row widths (n4 4-bit, n6 6-bit, the rest
+// 8-bit rows), then r[d], c[d] fp32, padded to a multiple of 256 bytes.
+inline int64_t record_bytes_rows(int n4, int n6, int d) {
+    const int64_t n8 = d - n4 - n6;
+    const int64_t raw = (int64_t)d * (4 * n4 + 6 * n6 + 8 * n8) / 8 + 8 * (int64_t)d;
+    return (raw + 255) / 256 * 256;
 }
 
 hipError_t launch_quant_state(const PoolView &pool, const HeadTable &tab, const int32_t *slot,

@@ -175,6 +175,91 @@ template <int BITS> __device__ __forceinline__ Seg<BITS> pack_stream(const uint3
     return s;
 }
 
+// 16 codes of a BITS-wide segment as one sign-extended byte each (the 8-bit
+// segment layout).
+template <int BITS> __device__ __forceinline__ Seg<8> widen_seg(const Seg<BITS> &s) {
+    Seg<8> o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        o.w[q] = ((uint32_t)code_at<BITS>(s, 4 * q) & 0xFFu) |
+                 (((uint32_t)code_at<BITS>(s, 4 * q + 1) & 0xFFu) << 8) |
+                 (((uint32_t)code_at<BITS>(s, 4 * q + 2) & 0xFFu) << 16) |
+                 ((uint32_t)code_at<BITS>(s, 4 * q + 3) << 24);
+    return o;
+}
+
+// Where a record's key rows are and how wide.  Uniform heads (MIXED = false):
+// every row BITS wide.  Heads with per-key-row widths (MIXED = true, the
+// kernels then carry codes in the 8-bit segment layout, BITS = 8): rows
+// [0, n4) are 4-bit, [n4, n4 + n6) 6-bit, the rest 8-bit, each row's code
+// stream right after the previous one.  The widths change only at multiples
+// of the rows one wavefront holds per m (8 at d = 128, 16 at d = 64), so a
+// row's width is uniform over the wavefront and the branches on it are
+// scalar.
+template <int D, int BITS, bool MIXED> struct Rows {
+    int n4, n6;
+    __device__ __forceinline__ int width(int row) const {
+        if constexpr (!MIXED) return BITS;
+        return row < n4 ? 4 : (row < n4 + n6 ? 6 : 8);
+    }
+    __device__ __forceinline__ int offset(int row) const {
+        if constexpr (!MIXED) return row * (D * BITS / 8);
+        const int a = min(row, n4), b = min(max(row - n4, 0), n6), c = max(row - n4 - n6, 0);
+        return a * (D / 2) + b * (3 * D / 4) + c * D;
+    }
+    __device__ __forceinline__ int codes_bytes() const { return offset(D); }
+    __device__ __forceinline__ float qmax(int row) const {
+        return (float)((1 << (width(row) - 1)) - 1);
+    }
+    // MIXED: the widest segment (16 bytes, 4-byte aligned) is read whatever
+    // the row's width, so the four rows' loads issue back to back before any
+    // width branch.  A narrower row's extra bytes lie in the next row or in
+    // r[] of the same record (which the same workgroup only writes later).
+    __device__ __forceinline__ Seg<8> load_raw(const uint8_t *rec, int row, int cg) const {
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(rec + offset(row) + cg * (2 * width(row)));
+        Seg<8> s;
+        s.w[0] = p[0]; s.w[1] = p[1]; s.w[2] = p[2]; s.w[3] = p[3];
+        return s;
+    }
+    __device__ __forceinline__ Seg<8> widen(const Seg<8> &raw, int row) const {
+        const int w = __builtin_amdgcn_readfirstlane(width(row));
+        if (w == 4) {
+            Seg<4> s4;
+            s4.w[0] = raw.w[0]; s4.w[1] = raw.w[1];
+            return widen_seg<4>(s4);
+        }
+        if (w == 6) {
+            Seg<6> s6;
+            s6.w[0] = raw.w[0]; s6.w[1] = raw.w[1]; s6.w[2] = raw.w[2];
+            return widen_seg<6>(s6);
+        }
+        return raw;
+    }
+    __device__ __forceinline__ Seg<BITS> load(const uint8_t *rec, int row, int cg) const {
+        if constexpr (!MIXED) {
+            return load_seg<BITS>(rec + offset(row) + cg * (2 * BITS));
+        } else {
+            return widen(load_raw(rec, row, cg), row);
+        }
+    }
+    // f: code bit patterns whose low bits are the two's-complement codes
+    __device__ __forceinline__ void store(uint8_t *rec, int row, int cg,
+                                         const uint32_t (&f)[16]) const {
+        if constexpr (!MIXED) {
+            store_seg<BITS>(rec + offset(row) + cg * (2 * BITS), pack_stream<BITS>(f));
+        } else {
+            const int w = __builtin_amdgcn_readfirstlane(width(row));
+            uint8_t *p = rec + offset(row) + cg * (2 * w);
+            if (w == 4)
+                store_seg<4>(p, pack_stream<4>(f));
+            else if (w == 6)
+                store_seg<6>(p, pack_stream<6>(f));
+            else
+                store_seg<8>(p, pack_stream<8>(f));
+        }
+    }
+};
+
 // ---------------------------------------------------------------- quantizer
 // Pinned fp32 arithmetic, one rounding per operation (no contraction):
 //   c_j = max_i |S_ij|; ic_j = c_j >= FLT_MIN ? 1/c_j : 0 (else c_j := 0)
@@ -259,15 +344,13 @@ __device__ __forceinline__ void load16(const float *src, float (&v)[16]) {
 // the results are broadcast back with ds_swizzle.  Codes: round half to even
 // of the exact product s * ir (code_bits); |s * ir| <= qmax (1 + 2 eps), so
 // the clamp to [-qmax, qmax] can never act and is omitted.
-template <int D, int BITS>
+template <int D, int BITS, bool MIXED = false>
 __device__ __forceinline__ void quantize_rows_store(float (&x)[4][16], const float (&ic)[16],
-                                                    uint8_t *rec) {
+                                                    uint8_t *rec, Rows<D, BITS, MIXED> rows = {}) {
 #pragma clang fp contract(off)
     using G = Geo<D>;
-    constexpr int RB = D * BITS / 8;
-    constexpr float QMAX = (float)((1 << (BITS - 1)) - 1);
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
-    float *rp = reinterpret_cast<float *>(rec + D * RB);
+    float *rp = reinterpret_cast<float *>(rec + rows.codes_bytes());
     float rm[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -283,7 +366,7 @@ __device__ __forceinline__ void quantize_rows_store(float (&x)[4][16], const flo
     const float sel01 = (cg & 1) ? rm[1] : rm[0];
     const float sel23 = (cg & 1) ? rm[3] : rm[2];
     const float mrow = (cg & 2) ? sel23 : sel01;
-    float r = mrow / QMAX;
+    float r = mrow / rows.qmax(band + G::NB * (cg & 3));
     float ir;
     if (r >= FLT_MIN) {
         ir = 1.0f / r;
@@ -306,17 +389,18 @@ __device__ __forceinline__ void quantize_rows_store(float (&x)[4][16], const flo
         uint32_t f[16];
 #pragma unroll
         for (int n = 0; n < 16; ++n) f[n] = code_bits(x[m][n], irm[m]);
-        store_seg<BITS>(rec + row * RB + cg * (2 * BITS), pack_stream<BITS>(f));
+        rows.store(rec, row, cg, f);
     }
 }
 
 // ---------------------------------------------------------------- quant_state
-template <int D, int BITS>
-__device__ __forceinline__ void quant_tile(uint8_t *rec, const float *S, float *lds) {
+template <int D, int BITS, bool MIXED = false>
+__device__ __forceinline__ void quant_tile(uint8_t *rec, const float *S, float *lds,
+                                           Rows<D, BITS, MIXED> rows = {}) {
     using G = Geo<D>;
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     float *plane = lds, *lds_ic = lds + G::NB * D;
-    float *cp = reinterpret_cast<float *>(rec + D * (D * BITS / 8)) + D;
+    float *cp = reinterpret_cast<float *>(rec + rows.codes_bytes()) + D;
     float x[4][16];
 #pragma unroll
     for (int m = 0; m < 4; ++m) load16<D>(S + (band + G::NB * m) * D + 16 * cg, x[m]);
@@ -330,7 +414,7 @@ __device__ __forceinline__ void quant_tile(uint8_t *rec, const float *S, float *
     __syncthreads();
     float ic[16];
     load_colvec16(lds_ic, cg, ic);
-    quantize_rows_store<D, BITS>(x, ic, rec);
+    quantize_rows_store<D, BITS, MIXED>(x, ic, rec, rows);
 }
 
 // ---------------------------------------------------------------- FP16 pivot records
@@ -403,6 +487,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void quant_state_kernel(PoolView pool, 
     uint8_t *rec = pool.base + (int64_t)slot[b] * pool.slot_stride + tab.off[h];
     const float *src = S + (int64_t)blockIdx.x * D * D;
     switch (tab.bits[h]) {
+    case 0: quant_tile<D, 8, true>(rec, src, lds, {tab.n4[h], tab.n6[h]}); break;
     case 4: quant_tile<D, 4>(rec, src, lds); break;
     case 6: quant_tile<D, 6>(rec, src, lds); break;
     case 16: quant_tile_f16<D>(rec, src); break;
@@ -411,12 +496,12 @@ __global__ __launch_bounds__(Geo<D>::NT) void quant_state_kernel(PoolView pool, 
 }
 
 // ---------------------------------------------------------------- dequant_state
-template <int D, int BITS>
-__device__ __forceinline__ void dequant_tile(const uint8_t *rec, float *S) {
+template <int D, int BITS, bool MIXED = false>
+__device__ __forceinline__ void dequant_tile(const uint8_t *rec, float *S,
+                                             Rows<D, BITS, MIXED> rows = {}) {
     using G = Geo<D>;
-    constexpr int RB = D * BITS / 8;
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
-    const float *rp = reinterpret_cast<const float *>(rec + D * RB);
+    const float *rp = reinterpret_cast<const float *>(rec + rows.codes_bytes());
     const float *cp = rp + D;
     float c[16];
     {
@@ -430,7 +515,7 @@ __device__ __forceinline__ void dequant_tile(const uint8_t *rec, float *S) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int row = band + G::NB * m;
-        const Seg<BITS> s = load_seg<BITS>(rec + row * RB + cg * (2 * BITS));
+        const Seg<BITS> s = rows.load(rec, row, cg);
         const double r = (double)rp[row];
         float o[16];
 #pragma unroll
@@ -455,6 +540,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void dequant_state_kernel(PoolView pool
     const uint8_t *rec = pool.base + (int64_t)slot[b] * pool.slot_stride + tab.off[h];
     float *dst = S + (int64_t)blockIdx.x * D * D;
     switch (tab.bits[h]) {
+    case 0: dequant_tile<D, 8, true>(rec, dst, {tab.n4[h], tab.n6[h]}); break;
     case 4: dequant_tile<D, 4>(rec, dst); break;
     case 6: dequant_tile<D, 6>(rec, dst); break;
     case 16: dequant_tile_f16<D>(rec, dst); break;
@@ -667,19 +753,31 @@ struct TileIn {
     uint8_t *rec;        // the tile's record
 };
 
-template <int D, int BITS, bool KDA, typename TI>
-__device__ __forceinline__ void load_tile(TileIn &in, int tile, uint8_t *rec, const StepIO &io) {
+template <int D, int BITS, bool KDA, typename TI, bool MIXED>
+__device__ __forceinline__ void load_tile(TileIn &in, int tile, uint8_t *rec, const StepIO &io,
+                                          Rows<D, BITS, MIXED> rows) {
     using G = Geo<D>;
-    constexpr int RB = D * BITS / 8;
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     in.rec = rec;
+    if constexpr (MIXED) {
+        Seg<8> raw[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const Seg<BITS> sg = load_seg<BITS>(rec + (band + G::NB * m) * RB + cg * (2 * BITS));
+        for (int m = 0; m < 4; ++m) raw[m] = rows.load_raw(rec, band + G::NB * m, cg);
 #pragma unroll
-        for (int i = 0; i < Seg<BITS>::NWORDS; ++i) in.w[m][i] = sg.w[i];
+        for (int m = 0; m < 4; ++m) {
+            const Seg<8> sg = rows.widen(raw[m], band + G::NB * m);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) in.w[m][i] = sg.w[i];
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const Seg<BITS> sg = rows.load(rec, band + G::NB * m, cg);
+#pragma unroll
+            for (int i = 0; i < Seg<BITS>::NWORDS; ++i) in.w[m][i] = sg.w[i];
+        }
     }
-    const float *rp = reinterpret_cast<const float *>(rec + D * RB);
+    const float *rp = reinterpret_cast<const float *>(rec + rows.codes_bytes());
     const int64_t row_io = tile;
     const TI *k = reinterpret_cast<const TI *>(io.k) + row_io * D;
     const TI *q = reinterpret_cast<const TI *>(io.q) + row_io * D;
@@ -709,11 +807,14 @@ template <int BITS> __device__ __forceinline__ Seg<BITS> seg_of(const TileIn &in
 // SPLIT: write S' (fp32) to io.s_out instead of requantizing; the record
 // is only read.  The requantization then runs as its own launch.
 // KRA: requantize with the key-row-aware fit (row-impact scores imp[D]).
-template <int D, int BITS, bool KDA, bool SPLIT, bool KRA, typename TI, typename TO>
+// MIXED: per-key-row widths (BITS = 8, the codes' in-kernel layout).
+template <int D, int BITS, bool KDA, bool SPLIT, bool KRA, typename TI, typename TO,
+          bool MIXED = false>
 __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const StepIO &io,
-                                            const float *imp, float *lds) {
+                                            const float *imp, float *lds,
+                                            Rows<D, BITS, MIXED> rows = {}) {
+    static_assert(!(KRA && MIXED), "the key-row-aware fit takes uniform widths");
     using G = Geo<D>;
-    constexpr int RB = D * BITS / 8;
     constexpr int PLANE = G::NB * D;
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     double *part64 = reinterpret_cast<double *>(lds);
@@ -722,9 +823,9 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     float *lds_ic = lds + DecodeLds<D>::PART_F + 4 * D;
     float *lds_misc = lds_ic + D; // [0]: GDN gate factor
     TileIn cur;
-    load_tile<D, BITS, KDA, TI>(cur, tile, rec_in, io);
+    load_tile<D, BITS, KDA, TI, MIXED>(cur, tile, rec_in, io, rows);
     uint8_t *rec = cur.rec;
-    float *cp = reinterpret_cast<float *>(rec + D * RB) + D;
+    float *cp = reinterpret_cast<float *>(rec + rows.codes_bytes()) + D;
     const int64_t row_io = tile;
 
     Seg<BITS> seg[4];
@@ -849,7 +950,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     } else {
         float ic[16];
         load_colvec16(lds_ic, cg, ic);
-        quantize_rows_store<D, BITS>(x, ic, rec);
+        quantize_rows_store<D, BITS, MIXED>(x, ic, rec, rows);
     }
 }
 
@@ -986,7 +1087,9 @@ __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const St
 // One workgroup per (request, head) tile; four resident per CU (VGPRs and
 // LDS both sized for four 4-wave workgroups), which hides the barriers and
 // reduction phases of one tile behind the others.
-template <int D, bool KDA, bool SPLIT, bool KRA, typename TI, typename TO>
+// ROWS: the pool has heads with per-key-row widths (their own kernel, so
+// that pools without them keep the register budget of the uniform bodies).
+template <int D, bool KDA, bool SPLIT, bool KRA, bool ROWS, typename TI, typename TO>
 __global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(SQ_DECODE_WAVES_PER_EU)))
 void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
     __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D>::TOTAL];
@@ -996,6 +1099,11 @@ void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
     uint8_t *rec = pool.base + (int64_t)io.slot[b] * pool.slot_stride + tab.off[h];
     const float *imp = KRA ? pool.impact + (int64_t)h * D : nullptr;
     switch (tab.bits[h]) {
+    case 0:
+        if constexpr (ROWS)
+            decode_tile<D, 8, KDA, SPLIT, false, TI, TO, true>(rec, tile, io, nullptr, lds,
+                                                               {tab.n4[h], tab.n6[h]});
+        break;
     case 4: decode_tile<D, 4, KDA, SPLIT, KRA, TI, TO>(rec, tile, io, imp, lds); break;
     case 6: decode_tile<D, 6, KDA, SPLIT, KRA, TI, TO>(rec, tile, io, imp, lds); break;
     case 16: decode_tile_f16<D, KDA, SPLIT, TI, TO>(rec, tile, io, lds); break;
@@ -1104,33 +1212,33 @@ __global__ __launch_bounds__(Geo<D>::NT) void f32_decode_kernel(float *state, in
 }
 
 // ---------------------------------------------------------------- dispatch
-template <int D, bool KDA, bool SPLIT, bool KRA>
+template <int D, bool KDA, bool SPLIT, bool KRA, bool ROWS>
 hipError_t decode_dispatch(const PoolView &pool, const HeadTable &tab, const StepIO &io,
                            hipStream_t s) {
     const dim3 grid((unsigned)io.n * (unsigned)pool.n_heads), block(Geo<D>::NT);
     if (!io.in_bf16 && !io.y_bf16)
-        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, KRA, float, float>), grid, block, 0, s, pool,
-                           tab, io);
+        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, KRA, ROWS, float, float>), grid, block, 0, s,
+                           pool, tab, io);
     else if (!io.in_bf16 && io.y_bf16)
-        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, KRA, float, uint16_t>), grid, block, 0, s,
-                           pool, tab, io);
+        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, KRA, ROWS, float, uint16_t>), grid, block, 0,
+                           s, pool, tab, io);
     else if (io.in_bf16 && !io.y_bf16)
-        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, KRA, uint16_t, float>), grid, block, 0, s,
-                           pool, tab, io);
+        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, KRA, ROWS, uint16_t, float>), grid, block, 0,
+                           s, pool, tab, io);
     else
-        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, KRA, uint16_t, uint16_t>), grid, block, 0, s,
-                           pool, tab, io);
+        hipLaunchKernelGGL((decode_kernel<D, KDA, SPLIT, KRA, ROWS, uint16_t, uint16_t>), grid, block,
+                           0, s, pool, tab, io);
     return hipGetLastError();
 }
 
-template <bool SPLIT, bool KRA>
+template <bool SPLIT, bool KRA, bool ROWS>
 hipError_t decode_gate_dispatch(const PoolView &pool, const HeadTable &tab, const StepIO &io,
                                 hipStream_t stream) {
     if (pool.d == 128)
-        return io.kda ? decode_dispatch<128, true, SPLIT, KRA>(pool, tab, io, stream)
-                      : decode_dispatch<128, false, SPLIT, KRA>(pool, tab, io, stream);
-    return io.kda ? decode_dispatch<64, true, SPLIT, KRA>(pool, tab, io, stream)
-                  : decode_dispatch<64, false, SPLIT, KRA>(pool, tab, io, stream);
+        return io.kda ? decode_dispatch<128, true, SPLIT, KRA, ROWS>(pool, tab, io, stream)
+                      : decode_dispatch<128, false, SPLIT, KRA, ROWS>(pool, tab, io, stream);
+    return io.kda ? decode_dispatch<64, true, SPLIT, KRA, ROWS>(pool, tab, io, stream)
+                  : decode_dispatch<64, false, SPLIT, KRA, ROWS>(pool, tab, io, stream);
 }
 
 template <int D, bool KDA>
@@ -1180,13 +1288,16 @@ hipError_t launch_dequant_state(const PoolView &pool, const HeadTable &tab, cons
 hipError_t launch_decode(const PoolView &pool, const HeadTable &tab, const StepIO &io,
                          hipStream_t stream) {
     // a pool with row-impact scores requantizes with the key-row-aware fit
-    return pool.impact ? decode_gate_dispatch<false, true>(pool, tab, io, stream)
-                       : decode_gate_dispatch<false, false>(pool, tab, io, stream);
+    // (such pools have no per-key-row widths)
+    if (pool.impact) return decode_gate_dispatch<false, true, false>(pool, tab, io, stream);
+    return pool.row_mixed ? decode_gate_dispatch<false, false, true>(pool, tab, io, stream)
+                          : decode_gate_dispatch<false, false, false>(pool, tab, io, stream);
 }
 
 hipError_t launch_decode_update(const PoolView &pool, const HeadTable &tab, const StepIO &io,
                                 hipStream_t stream) {
-    return decode_gate_dispatch<true, false>(pool, tab, io, stream);
+    return pool.row_mixed ? decode_gate_dispatch<true, false, true>(pool, tab, io, stream)
+                          : decode_gate_dispatch<true, false, false>(pool, tab, io, stream);
 }
 
 hipError_t launch_f32_decode(float *state, int64_t slot_stride_floats, int32_t n_heads, int32_t d,

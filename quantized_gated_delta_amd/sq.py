@@ -55,6 +55,10 @@ def lib():
         L.sq_pool_bytes.argtypes = [pdesc, ctypes.POINTER(ctypes.c_size_t)]
         L.sq_pool_create.restype = st
         L.sq_pool_create.argtypes = [pdesc, vp, ctypes.c_size_t, ctypes.POINTER(vp)]
+        L.sq_pool_bytes_rows.restype = st
+        L.sq_pool_bytes_rows.argtypes = [pdesc, vp, ctypes.POINTER(ctypes.c_size_t)]
+        L.sq_pool_create_rows.restype = st
+        L.sq_pool_create_rows.argtypes = [pdesc, vp, vp, ctypes.c_size_t, ctypes.POINTER(vp)]
         L.sq_pool_destroy.restype = st
         L.sq_pool_destroy.argtypes = [vp]
         L.sq_pool_layout.restype = st
@@ -138,21 +142,40 @@ def sq_last_error() -> str:
     return lib().sq_last_error().decode(errors="replace")
 
 
-def sq_pool_bytes(n_slots, n_heads, d_k, d_v, head_bits, gate) -> int:
+def _row_bits(row_bits):
+    if row_bits is None:
+        return None
+    flat = [int(b) for row in row_bits for b in row]
+    return (ctypes.c_uint8 * max(1, len(flat)))(*flat)
+
+
+def sq_pool_bytes(n_slots, n_heads, d_k, d_v, head_bits, gate, row_bits=None) -> int:
+    """row_bits: [n_heads][d_k] key-row widths for heads with head_bits 0 (else None)."""
     d, keep = _desc(n_slots, n_heads, d_k, d_v, head_bits, gate)
+    rb = _row_bits(row_bits)
     out = ctypes.c_size_t(0)
-    _check(lib().sq_pool_bytes(ctypes.byref(d), ctypes.byref(out)), "sq_pool_bytes")
+    if rb is None:
+        _check(lib().sq_pool_bytes(ctypes.byref(d), ctypes.byref(out)), "sq_pool_bytes")
+    else:
+        _check(lib().sq_pool_bytes_rows(ctypes.byref(d), rb, ctypes.byref(out)),
+               "sq_pool_bytes_rows")
     return out.value
 
 
-def sq_pool_create(n_slots, n_heads, d_k, d_v, head_bits, gate, dev_buf, nbytes=None) -> int:
+def sq_pool_create(n_slots, n_heads, d_k, d_v, head_bits, gate, dev_buf, nbytes=None,
+                   row_bits=None) -> int:
     """Wrap a caller-owned device buffer (tensor or pointer); returns the handle."""
     d, keep = _desc(n_slots, n_heads, d_k, d_v, head_bits, gate)
+    rb = _row_bits(row_bits)
     if nbytes is None:
         nbytes = dev_buf.numel() * dev_buf.element_size()
     h = ctypes.c_void_p(0)
-    _check(lib().sq_pool_create(ctypes.byref(d), _ptr(dev_buf), int(nbytes), ctypes.byref(h)),
-           "sq_pool_create")
+    if rb is None:
+        _check(lib().sq_pool_create(ctypes.byref(d), _ptr(dev_buf), int(nbytes),
+                                    ctypes.byref(h)), "sq_pool_create")
+    else:
+        _check(lib().sq_pool_create_rows(ctypes.byref(d), rb, _ptr(dev_buf), int(nbytes),
+                                         ctypes.byref(h)), "sq_pool_create_rows")
     return h.value
 
 
@@ -223,15 +246,17 @@ class StatePool:
     given device, creates the pool handle and exposes the ABI calls."""
 
     def __init__(self, n_slots: int, n_heads: int, d: int, head_bits, gate: str = "gdn",
-                 device="cuda"):
+                 device="cuda", row_bits=None):
+        """row_bits: [n_heads][d] key-row widths for the heads whose head_bits is 0."""
         import torch
         self.n_slots, self.n_heads, self.d = int(n_slots), int(n_heads), int(d)
         self.head_bits = [int(b) for b in head_bits]
+        self.row_bits = None if row_bits is None else [[int(b) for b in r] for r in row_bits]
         self.gate = SQ_GATE_KDA if gate == "kda" else SQ_GATE_GDN
-        nbytes = sq_pool_bytes(n_slots, n_heads, d, d, self.head_bits, self.gate)
+        nbytes = sq_pool_bytes(n_slots, n_heads, d, d, self.head_bits, self.gate, self.row_bits)
         self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.handle = sq_pool_create(n_slots, n_heads, d, d, self.head_bits, self.gate, self.buf,
-                                     nbytes)
+                                     nbytes, self.row_bits)
         self.slot_stride, self.head_off, self.record_bytes = sq_pool_layout(self.handle, n_heads)
 
     def quant_state(self, slot_idx, S, stream=None):

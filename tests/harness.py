@@ -18,20 +18,54 @@ def record_bytes(bits: int, d: int) -> int:
     return d * d * bits // 8 + 8 * d
 
 
-def layout(head_bits, d):
+def record_bytes_rows(row_bits, d: int) -> int:
+    """A head with per-key-row widths: the rows' streams, r and c, padded to 256 B."""
+    raw = sum(d * int(b) // 8 for b in row_bits) + 8 * d
+    return (raw + 255) // 256 * 256
+
+
+def head_record_bytes(bits: int, d: int, row_bits=None) -> int:
+    return record_bytes_rows(row_bits, d) if bits == 0 else record_bytes(bits, d)
+
+
+def layout(head_bits, d, row_bits=None):
     """slot_stride and per-head record offsets of the documented pool layout."""
     offs, pos = [], 0
-    for b in head_bits:
+    for h, b in enumerate(head_bits):
         offs.append(pos)
-        pos += record_bytes(int(b), d)
+        pos += head_record_bytes(int(b), d, None if row_bits is None else row_bits[h])
     return pos, np.array(offs, np.int64)
 
 
-def unpack_codes(bits: int, d: int, rec: np.ndarray) -> np.ndarray:
+def _unpack_rows(bits: int, raw: np.ndarray, d: int) -> np.ndarray:
+    """raw: [n, d * bits / 8] packed rows -> codes [n, d]."""
+    n = raw.shape[0]
+    if bits == 8:
+        return raw.view(np.int8).astype(np.int32)
+    if bits == 4:
+        lo = (raw & 0xF).astype(np.int32)
+        hi = (raw >> 4).astype(np.int32)
+        codes = np.stack([lo, hi], axis=-1).reshape(n, d)
+        return np.where(codes >= 8, codes - 16, codes)
+    g = raw.reshape(n, d // 4, 3).astype(np.uint32)
+    word = g[..., 0] | (g[..., 1] << 8) | (g[..., 2] << 16)
+    codes = np.stack([(word >> (6 * m)) & 63 for m in range(4)], axis=-1).reshape(n, d)
+    codes = codes.astype(np.int32)
+    return np.where(codes >= 32, codes - 64, codes)
+
+
+def unpack_codes(bits: int, d: int, rec: np.ndarray, row_bits=None) -> np.ndarray:
     """Codes [d, d] of one record, decoded with numpy bit arithmetic (for an
-    FP16 pivot record: the binary16 bit patterns)."""
+    FP16 pivot record: the binary16 bit patterns; bits 0: per-row widths)."""
     if bits == 16:
         return rec[: 2 * d * d].view(np.uint16).reshape(d, d).astype(np.int32)
+    if bits == 0:
+        out, pos = [], 0
+        for b in row_bits:
+            n = d * int(b) // 8
+            out.append(_unpack_rows(int(b), rec[pos:pos + n].reshape(1, n), d)[0])
+            pos += n
+        return np.stack(out)
     rb = d * bits // 8
     raw = rec[: d * rb].reshape(d, rb)
     if bits == 8:
@@ -48,11 +82,11 @@ def unpack_codes(bits: int, d: int, rec: np.ndarray) -> np.ndarray:
     return np.where(codes >= 32, codes - 64, codes)
 
 
-def record_scales(bits: int, d: int, rec: np.ndarray):
+def record_scales(bits: int, d: int, rec: np.ndarray, row_bits=None):
     if bits == 16:
         return ()
-    rb = d * bits // 8
-    sc = rec[d * rb: d * rb + 8 * d].view(np.float32)
+    cb = sum(d * int(b) // 8 for b in row_bits) if bits == 0 else d * (d * bits // 8)
+    sc = rec[cb: cb + 8 * d].view(np.float32)
     return sc[:d].copy(), sc[d:].copy()
 
 
@@ -60,11 +94,12 @@ def record_scales(bits: int, d: int, rec: np.ndarray):
 class HostPool:
     """Host image of a pool in the documented layout (oracle side)."""
 
-    def __init__(self, n_slots, head_bits, d):
+    def __init__(self, n_slots, head_bits, d, row_bits=None):
         self.d = d
         self.head_bits = np.asarray(head_bits, np.uint8)
+        self.row_bits = row_bits
         self.H = len(head_bits)
-        self.stride, self.head_off = layout(head_bits, d)
+        self.stride, self.head_off = layout(head_bits, d, row_bits)
         self.bytes = np.zeros(n_slots * self.stride, np.uint8)
 
     def offsets(self, slots, heads):
@@ -74,7 +109,8 @@ class HostPool:
 
     def record(self, slot, h):
         o = slot * self.stride + self.head_off[h]
-        return self.bytes[o: o + record_bytes(int(self.head_bits[h]), self.d)]
+        rb = None if self.row_bits is None else self.row_bits[h]
+        return self.bytes[o: o + head_record_bytes(int(self.head_bits[h]), self.d, rb)]
 
 
 def rows_all(B, H):

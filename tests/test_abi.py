@@ -5,6 +5,7 @@ layout) or is rejected by validation before any HIP call is made, so the
 suite runs without a GPU.
 """
 import ctypes
+import functools
 import threading
 
 import pytest
@@ -186,3 +187,57 @@ def test_bench_byte_model():
     assert bench.algo_bytes_per_step(1, 1, 128, [6], "kda") == 27652 + 254 + 4
     assert bench.algo_bytes_per_step(512, 48, 128, [6] * 48, "gdn") == 679577600
     assert bench.f32_bytes_per_step(1, 1, 128, "gdn") == 132100 + 4
+
+
+def _rows_rec(w, d):
+    raw = sum(d * int(b) // 8 for b in w) + 8 * d
+    return (raw + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_per_row_width_layout(d):
+    """Heads with head_bits 0 take key-row widths; their records are the rows'
+    streams then the scales, padded to 256 bytes."""
+    g = 8 if d == 128 else 16
+    w0 = [4] * (2 * g) + [6] * (d - 3 * g) + [8] * g
+    w2 = [6] * (d - g) + [8] * g
+    rows = [w0, [6] * d, w2]
+    bits = [0, 6, 0]
+    want = [_rows_rec(w0, d), d * d * 6 // 8 + 8 * d, _rows_rec(w2, d)]
+    assert Q.sq_pool_bytes(5, 3, d, d, bits, Q.SQ_GATE_KDA, row_bits=rows) == 5 * sum(want)
+    h = Q.sq_pool_create(5, 3, d, d, bits, Q.SQ_GATE_KDA, FAKE_DEV, 5 * sum(want), row_bits=rows)
+    try:
+        st, ho, rb = Q.sq_pool_layout(h, 3)
+        assert rb == want and ho == [0, want[0], want[0] + want[1]] and st == sum(want)
+        # the key-row-aware fit takes uniform widths only
+        _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_set_row_impact, h, FAKE_DEV, text="uniform width")
+        Q.sq_pool_set_row_impact(h, None)
+    finally:
+        Q.sq_pool_destroy(h)
+
+
+def test_per_row_width_validation():
+    d, g = 128, 8
+    ok = [4] * 32 + [6] * 64 + [8] * 32
+    _expect(Q.SQ_EINVAL, Q.sq_pool_bytes, 2, 1, d, d, [0], 1, text="needs per-row widths")
+    bad = list(ok)
+    bad[40] = 5
+    _expect(Q.SQ_EUNSUPPORTED, functools.partial(Q.sq_pool_bytes, row_bits=[bad]),
+            2, 1, d, d, [0], 1,
+            text="must be 4, 6 or 8")
+    dec = [6] * 64 + [4] * 64
+    _expect(Q.SQ_EUNSUPPORTED, functools.partial(Q.sq_pool_bytes, row_bits=[dec]),
+            2, 1, d, d, [0], 1,
+            text="non-decreasing")
+    off = [4] * 36 + [8] * 92
+    _expect(Q.SQ_EUNSUPPORTED, functools.partial(Q.sq_pool_bytes, row_bits=[off]),
+            2, 1, d, d, [0], 1,
+            text="not a multiple of 8")
+    off64 = [4] * 8 + [8] * 56
+    _expect(Q.SQ_EUNSUPPORTED, functools.partial(Q.sq_pool_bytes, row_bits=[off64]),
+            2, 1, 64, 64, [0], 1,
+            text="not a multiple of 16")
+    assert Q.sq_pool_bytes(2, 1, d, d, [0], 1, row_bits=[ok]) == 2 * _rows_rec(ok, d)
+    # rows of uniform heads are not read
+    assert Q.sq_pool_bytes(2, 2, d, d, [6, 0], 1, row_bits=[[0] * d, ok]) == \
+        2 * (13312 + _rows_rec(ok, d))

@@ -57,14 +57,24 @@ class Side:
         """imp [H, d] fp32: row-impact scores (key-row-aware fit on both sides)."""
         self.wl, self.layer = wl, layer
         self.kda = layer.gate == "kda"
-        self.gpu = Q.StatePool(wl.n_slots, wl.H, wl.d, layer.head_bits.tolist(), layer.gate)
+        self.gpu = Q.StatePool(wl.n_slots, wl.H, wl.d, layer.head_bits.tolist(), layer.gate,
+                               row_bits=layer.row_bits)
         self.imp = None if imp is None else np.ascontiguousarray(imp, np.float32)
         if self.imp is not None:
             self.gpu.set_row_impact(to_dev(self.imp))
-        self.host = Hn.HostPool(wl.n_slots, layer.head_bits, wl.d)
+        self.host = Hn.HostPool(wl.n_slots, layer.head_bits, wl.d, layer.row_bits)
         assert self.gpu.slot_stride == self.host.stride
         assert np.array_equal(np.array(self.gpu.head_off), self.host.head_off)
         self.slot_dev = to_dev(layer.slot_of.astype(np.int32))
+
+    def rows_row_bits(self, rows):
+        if self.layer.row_bits is None:
+            return None
+        return self.layer.row_bits[np.asarray(rows).reshape(-1, 2)[:, 1]]
+
+    def rec_bytes(self, h):
+        rb = None if self.layer.row_bits is None else self.layer.row_bits[h]
+        return Hn.head_record_bytes(int(self.layer.head_bits[h]), self.wl.d, rb)
 
     def rows_imp(self, rows):
         if self.imp is None:
@@ -82,14 +92,14 @@ class Side:
             S = Hn.oracle_warmup(self.wl, self.layer, rows)
         offs, bits = self.rows_offsets(rows)
         O.records_quantize(self.host.bytes, offs, bits, S, self.wl.d, self.wl.d,
-                           self.rows_imp(rows))
+                           self.rows_imp(rows), self.rows_row_bits(rows))
         self.push_rows(rows)
 
     def push_rows(self, rows):
         offs, bits = self.rows_offsets(rows)
         buf = self.gpu.buf
-        for o, b in zip(offs, bits):
-            n = Hn.record_bytes(int(b), self.wl.d)
+        for o, h in zip(offs, np.asarray(rows).reshape(-1, 2)[:, 1]):
+            n = self.rec_bytes(h)
             buf[int(o):int(o) + n].copy_(torch.from_numpy(self.host.bytes[o:o + n]))
 
     def gpu_warmup_all(self):
@@ -122,7 +132,8 @@ class Side:
         xs = {k: W.to_f32(v[idx]) for k, v in x.items()}
         offs, bits = self.rows_offsets(rows)
         y_ref = O.records_step(self.kda, self.host.bytes, offs, bits, wl.d, wl.d, xs["q"],
-                               xs["k"], xs["v"], xs["beta"], xs["g"], self.rows_imp(rows))
+                               xs["k"], xs["v"], xs["beta"], xs["g"], self.rows_imp(rows),
+                               self.rows_row_bits(rows))
         y_gpu = W.to_f32(from_dev(y)).astype(np.float64)[idx]
         if wl.dtype == "bf16":
             y_ref = Hn.to_bf16_f32(y_ref)
@@ -142,9 +153,10 @@ def check_records(side: Side, rows, pool_gpu: np.ndarray, label=""):
     for (b, h) in np.asarray(rows).reshape(-1, 2):
         bits = int(side.layer.head_bits[h])
         o = int(side.host.offsets([side.layer.slot_of[b]], [h])[0])
-        n = Hn.record_bytes(bits, d)
+        n = side.rec_bytes(h)
+        rb = None if side.layer.row_bits is None else side.layer.row_bits[h]
         rg, rr = pool_gpu[o:o + n], side.host.bytes[o:o + n]
-        qg, qr = Hn.unpack_codes(bits, d, rg), Hn.unpack_codes(bits, d, rr)
+        qg, qr = Hn.unpack_codes(bits, d, rg, rb), Hn.unpack_codes(bits, d, rr, rb)
         if bits == 16:  # FP16 pivot: the binary16 values must match exactly
             assert np.array_equal(qg, qr), "%s: fp16 record differs, row %d head %d" % (label, b, h)
             continue
@@ -152,7 +164,7 @@ def check_records(side: Side, rows, pool_gpu: np.ndarray, label=""):
         worst = max(worst, mx)
         flips += int((qg != qr).sum())
         total += qg.size
-        sg, sr = Hn.record_scales(bits, d, rg), Hn.record_scales(bits, d, rr)
+        sg, sr = Hn.record_scales(bits, d, rg, rb), Hn.record_scales(bits, d, rr, rb)
         for a, bb in zip(sg, sr):
             np.testing.assert_allclose(a, bb, rtol=Hn.SCALE_RTOL, atol=0,
                                        err_msg="%s scales row %d head %d" % (label, b, h))
@@ -625,5 +637,123 @@ def test_kra_trajectory_256_steps(name, n_rows):
     s_ref = O.records_dequantize(side.host.bytes, offs, hb, wl.d, wl.d)
     err = Hn.rel_l2(s_gpu, s_ref)
     log("%s kra: worst y rel-L2 %.3g, final state rel-L2 %.3g" % (name, worst_y, err))
+    assert worst_y <= Hn.Y_REL_L2
+    assert err <= Hn.STATE_REL_L2
+
+
+# ----------------------------------------------------------------- per-key-row widths
+def _row_widths(H, d, seed):
+    """Per head a non-decreasing width pattern on the layout's grain."""
+    rng = np.random.default_rng(300 + seed)
+    g = 8 if d == 128 else 16
+    out = []
+    for _ in range(H):
+        cuts = np.sort(rng.integers(0, d // g + 1, 2)) * g
+        out.append([4] * cuts[0] + [6] * (cuts[1] - cuts[0]) + [8] * (d - cuts[1]))
+    return np.array(out, np.uint8)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rows_quant_dequant_bit_exact(d):
+    log("rows quant/dequant d=%d" % d)
+    rng = np.random.default_rng(80 + d)
+    H, B = 5, 4
+    bits = [0, 6, 0, 16, 0]
+    rows_w = _row_widths(H, d, d)
+    wl = W.custom("kda", B, H, d, bits, n_slots=6, permute=True, seed=9, row_bits=rows_w)
+    side = Side(wl, wl.layers[0])
+    S = (rng.standard_normal((B, H, d, d)) * np.exp(rng.standard_normal((B, H, d, 1)))
+         * np.exp(rng.standard_normal((B, H, 1, d)))).astype(np.float32)
+    S[0, 0] = 0.0
+    S[1, 2, 5, :] = 0.0
+    S[2, 4, :, 3] = 1e-40
+    side.gpu.quant_state(side.slot_dev, to_dev(S))
+    rows = Hn.rows_all(B, H)
+    offs, hb = side.rows_offsets(rows)
+    O.records_quantize(side.host.bytes, offs, hb, S.reshape(-1, d, d), d, d,
+                       row_bits=side.rows_row_bits(rows))
+    got = side.gpu_pool()
+    for (b, h), o in zip(rows, offs):
+        n = side.rec_bytes(h)
+        raw = n if hb[h] != 0 else sum(d * int(w) // 8 for w in rows_w[h]) + 8 * d
+        assert np.array_equal(got[o:o + raw], side.host.bytes[o:o + raw]), (b, h)
+    out = side.gpu.dequant_state(side.slot_dev)
+    want = O.records_dequantize(side.host.bytes, offs, hb, d, d, row_bits=side.rows_row_bits(rows))
+    assert np.array_equal(from_dev(out).reshape(-1, d, d), want)
+
+
+@pytest.mark.parametrize("case", [
+    ("kda", 3, 4, 128, [0, 6, 0, 16], "bf16", 5),
+    ("kda", 4, 3, 64, [0, 0, 8], "f32", 4),
+    ("gdn", 3, 3, 128, [6, 0, 4], "bf16", 3),
+])
+def test_rows_decode_step_small_full_compare(case):
+    gate, B, H, d, bits, dtype, n_slots = case
+    log("rows step %s" % (case,))
+    wl = W.custom(gate, B, H, d, bits, dtype=dtype, n_slots=n_slots, permute=True, seed=10,
+                  row_bits=_row_widths(H, d, B))
+    side = Side(wl, wl.layers[0])
+    side.gpu.buf.fill_(0xA5)
+    side.host.bytes[:] = 0xA5
+    rows = Hn.rows_all(B, H)
+    side.init_oracle_rows(rows)
+    for t in range(3):
+        side.push_rows(rows)
+        y_gpu, y_ref = side.step(t, rows)
+        pool = side.gpu_pool()
+        check_records(side, rows, pool, "rows step %d" % t)
+        assert Hn.rel_l2(y_gpu, y_ref) <= Hn.Y_REL_L2, t
+        used = np.zeros(pool.size, bool)
+        for sl in side.layer.slot_of:
+            used[sl * side.host.stride:(sl + 1) * side.host.stride] = True
+        assert (pool[~used] == 0xA5).all()
+
+
+def test_rows_split_matches_fused():
+    B, H, d = 3, 3, 128
+    log("rows split")
+    wl = W.custom("kda", B, H, d, [0, 8, 0], n_slots=4, permute=True, seed=11,
+                  row_bits=_row_widths(H, d, 7))
+    side = Side(wl, wl.layers[0])
+    rows = Hn.rows_all(B, H)
+    side.init_oracle_rows(rows)
+    split = Q.StatePool(wl.n_slots, H, d, [0, 8, 0], "kda", row_bits=wl.layers[0].row_bits)
+    split.buf.copy_(side.gpu.buf)
+    S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=DEV)
+    for t in range(2):
+        x = dev_inputs(wl.step_inputs(wl.layers[0], t))
+        y_f = torch.empty((B * H, d), dtype=torch.bfloat16, device=DEV)
+        y_s = torch.empty_like(y_f)
+        side.gpu.decode_step(side.slot_dev, x["q"], x["k"], x["v"], x["beta"], x["g"], y_f)
+        split.decode_update(side.slot_dev, x["q"], x["k"], x["v"], x["beta"], x["g"], y_s, S_out)
+        split.quant_state(side.slot_dev, S_out)
+        torch.cuda.synchronize()
+        assert torch.equal(split.buf, side.gpu.buf) and torch.equal(y_f, y_s), t
+
+
+def test_rows_kda_trajectory_256_steps():
+    """KDA with per-key-row widths 4/6/8 at 25/50/25 % of each head's rows:
+    256 steps within the trajectory bound of the oracle."""
+    log("rows kda trajectory")
+    base = W.make("c2")
+    H, d = base.H, base.d
+    g = 8
+    w = np.array([4] * (4 * g) + [6] * (d - 8 * g) + [8] * (4 * g), np.uint8)
+    wl = W.custom("kda", base.B, H, d, [0] * H, dtype="bf16", n_slots=base.n_slots,
+                  permute=True, seed=base.seed, row_bits=np.tile(w, (H, 1)))
+    side = Side(wl, wl.layers[0])
+    side.gpu_warmup_all()
+    rows = sample_rows(wl.B, wl.H, 32, seed=3)
+    side.init_oracle_rows(rows)
+    worst_y = 0.0
+    for t in range(256):
+        y_gpu, y_ref = side.step(t, rows)
+        worst_y = max(worst_y, Hn.rel_l2(y_gpu, y_ref))
+    offs, hb = side.rows_offsets(rows)
+    rb = side.rows_row_bits(rows)
+    s_gpu = O.records_dequantize(side.gpu_pool(), offs, hb, d, d, row_bits=rb)
+    s_ref = O.records_dequantize(side.host.bytes, offs, hb, d, d, row_bits=rb)
+    err = Hn.rel_l2(s_gpu, s_ref)
+    log("rows kda: worst y rel-L2 %.3g, final state rel-L2 %.3g" % (worst_y, err))
     assert worst_y <= Hn.Y_REL_L2
     assert err <= Hn.STATE_REL_L2

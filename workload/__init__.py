@@ -115,6 +115,7 @@ class Layer:
     gate_rates: np.ndarray    # float64 [H] (GDN) or [H, d] (KDA): log-gate = -rate
     slot_of: np.ndarray       # int32 [B]: request b lives in pool slot slot_of[b]
     index: int                # layer index in the seed key
+    row_bits: Optional[np.ndarray] = None  # uint8 [H, d]: key-row widths of heads with bits 0
 
 
 @dataclasses.dataclass
@@ -256,16 +257,33 @@ def make(name: str, seed: int = 0, steps: Optional[int] = None) -> Workload:
 
 def custom(gate: str, B: int, H: int, d: int, head_bits, dtype: str = "bf16",
            n_slots: Optional[int] = None, permute: bool = False, seed: int = 0,
-           steps: int = 1, name: str = "custom") -> Workload:
-    """A workload of any shape with the same value recipe (used for edge cases)."""
+           steps: int = 1, name: str = "custom", row_bits=None) -> Workload:
+    """A workload of any shape with the same value recipe (used for edge cases).
+    row_bits [H, d]: key-row widths of the heads whose head_bits is 0."""
     n_slots = B if n_slots is None else n_slots
     hb = np.asarray(head_bits, np.uint8)
     if hb.size == 1:
         hb = np.full(H, int(hb.reshape(-1)[0]), np.uint8)
     rates = gate_rates(seed, 0, H, d, gate == "kda")
     slots = slot_permutation(seed, 0, B, n_slots) if permute else np.arange(B, dtype=np.int32)
+    rb = None if row_bits is None else np.ascontiguousarray(row_bits, np.uint8)
     return Workload(name, B, H, d, dtype, n_slots, steps, seed,
-                    [Layer(gate, hb, rates, slots, 0)])
+                    [Layer(gate, hb, rates, slots, 0, rb)])
+
+
+def row_widths_by_lifetime(rates: np.ndarray, fractions=(0.25, 0.5, 0.25), grain: int = 8):
+    """Key-row widths per head for a KDA layer whose key channels are stored
+    in order of decreasing gate rate (increasing lifetime), i.e. after the
+    offline channel permutation: the fastest-decaying rows 4-bit, the middle
+    6-bit, the longest-lived 8-bit, in the given fractions rounded to the
+    grain the pool layout needs.  Returns (row_bits [H, d], the channel
+    permutation perm [H, d] with physical row p = channel perm[h, p])."""
+    H, d = rates.shape
+    perm = np.argsort(-rates, axis=1, kind="stable").astype(np.int64)
+    n4 = int(round(fractions[0] * d / grain)) * grain
+    n8 = int(round(fractions[2] * d / grain)) * grain
+    w = np.array([4] * n4 + [6] * (d - n4 - n8) + [8] * n8, np.uint8)
+    return np.tile(w, (H, 1)), perm
 
 
 def normals(seed: int, layer: int, t: int, b: int, h: int, n: int) -> np.ndarray:
