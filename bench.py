@@ -76,7 +76,7 @@ def main():
     ap.add_argument("--workload", default="c3a")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-variants", action="store_true", help="only the headline kernel")
-    ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prewarm", type=float, default=0.3,
                     help="seconds of untimed steps before the warm-up steps")
     ap.add_argument("--copy-calib", action="store_true",
@@ -311,6 +311,10 @@ def main():
             pool_r.close()
             pool_k.close()
     del state
+    copy_GBps = device_copy_GBps(dev)
+    eprint("device copy: %.0f GB/s" % copy_GBps)
+    if not args.no_variants:
+        variants["smaller_configs"] = config_timings(dev)
 
     # ---- CPU oracle on a bounded sample of the same workload
     cpu = None
@@ -344,12 +348,94 @@ def main():
                    "gate": layer.gate},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "device_copy_GBps": copy_GBps, "frac_of_device_copy": achieved / copy_GBps,
                      "algo_bytes_per_launch": bytes_step, "us_per_launch": ms_launch * 1e3,
                      "kernel": "decode_kernel<128, GDN, bf16, bf16>"},
         "cpu_baseline": cpu,
         "variants": variants,
     }
     print(json.dumps(out), flush=True)
+
+
+def device_copy_GBps(dev, nbytes=2 << 30, reps=5):
+    """A plain device copy of nbytes (read + write) timed with HIP events:
+    the practically reachable HBM rate next to the 8 TB/s peak."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        b.copy_(a)
+    ev[1].record()
+    torch.cuda.synchronize()
+    sec = ev[0].elapsed_time(ev[1]) * 1e-3 / reps
+    del a, b
+    return 2 * nbytes / sec / 1e9
+
+
+def config_timings(dev, K=20):
+    """The smaller workloads: c0 latency; c1 and c2 hot (K back-to-back steps)
+    and flushed (a 1 GiB buffer written before each step, so the pool comes
+    from HBM rather than the 256 MB Infinity Cache).  Per-step HIP events."""
+    import numpy as np
+    import torch
+
+    import quantized_gated_delta_amd as Q
+    import workload as W
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    out = {}
+    for name in ("c0", "c1", "c2"):
+        wl = W.make(name)
+        lay = wl.layers[0]
+        B, H, d = wl.B, wl.H, wl.d
+        kda = lay.gate == "kda"
+        pool = Q.StatePool(wl.n_slots, H, d, lay.head_bits.tolist(), lay.gate, device=dev)
+        slot = to_dev(lay.slot_of.astype(np.int32))
+        state = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
+        ident = torch.arange(B, dtype=torch.int32, device=dev)
+        ins = [{k: to_dev(v) for k, v in wl.step_inputs(lay, t).items()} for t in range(4)]
+        y = torch.empty((B * H, d), dtype=ins[0]["q"].dtype, device=dev)
+        for i in range(8):
+            x = ins[i % 4]
+            Q.sq_f32_decode_step(state, B, H, d, d, int(kda), ident, B, x["q"], x["k"], x["v"],
+                                 x["beta"], x["g"], y)
+        pool.quant_state(slot, state)
+        res = {}
+        for mode in ("hot", "flushed"):
+            if mode == "flushed" and name == "c0":
+                continue
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(K)]
+            for i in range(K + 3):
+                x = ins[i % 4]
+                if mode == "flushed":
+                    flush.fill_(i & 0xFF)
+                if i >= 3:
+                    ev[i - 3][0].record()
+                pool.decode_step(slot, x["q"], x["k"], x["v"], x["beta"], x["g"], y)
+                if i >= 3:
+                    ev[i - 3][1].record()
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+            nb = algo_bytes_per_step(B, H, d, lay.head_bits, lay.gate,
+                                     2 if wl.dtype == "bf16" else 4)
+            res[mode] = {"us_per_step": us, "updates_per_s": B * H / (us * 1e-6),
+                         "achieved_GBps": nb / (us * 1e-6) / 1e9}
+        out[name] = res
+        pool.close()
+        eprint("%s: %s" % (name, {m: round(v["us_per_step"], 1) for m, v in res.items()}))
+    del flush
+    return out
 
 
 def split_epilogue(pool, slot, steps_in, y, timed, fused_ms, stream, dev, B, H, d, io_dt):
@@ -578,9 +664,10 @@ def trajectory(args, dev):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, layer, seconds):
+def cpu_baseline(wl, layer, seconds, single_seconds=3.0):
     """The oracle, as it stands, on sampled (b, h) rows of the same workload,
-    all host threads; repeated until `seconds` of wall time have passed."""
+    all host threads; repeated until `seconds` of wall time have passed.
+    Then the same on one thread for `single_seconds`."""
     import numpy as np
 
     import oracle as O
@@ -602,18 +689,34 @@ def cpu_baseline(wl, layer, seconds):
     base = np.zeros(int(sizes.sum()), np.uint8)
     O.records_quantize(base, offs, bits, S.astype(np.float32), d, d)
     x = {k: W.to_f32(v) for k, v in wl.step_inputs(layer, 0, rows).items()}
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        O.records_step(layer.gate == "kda", base, offs, bits, d, d, x["q"], x["k"], x["v"],
-                       x["beta"], x["g"])
-        done += n_rows
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+
+    def run(secs, rows_per_pass):
+        sub = slice(0, rows_per_pass)
+        xs = {k: v[sub] for k, v in x.items()}
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            O.records_step(layer.gate == "kda", base, offs[sub], bits[sub], d, d, xs["q"],
+                           xs["k"], xs["v"], xs["beta"], xs["g"])
+            done += rows_per_pass
+            el = time.perf_counter() - t0
+            if el >= secs:
+                return done, el
+
+    done, el = run(seconds, n_rows)
+    prev = os.environ.get("SQO_THREADS")
+    os.environ["SQO_THREADS"] = "1"
+    try:
+        done1, el1 = run(single_seconds, 16)
+    finally:
+        if prev is None:
+            del os.environ["SQO_THREADS"]
+        else:
+            os.environ["SQO_THREADS"] = prev
     return {"value": done / el, "unit": "state-updates/s", "cores": nthr, "kind": "oracle",
             "sample": "%d rows x %d passes of the B=%d H=%d d=%d step (%.1f s wall)"
-                      % (n_rows, done // n_rows, wl.B, H, d, el)}
+                      % (n_rows, done // n_rows, wl.B, H, d, el),
+            "single_thread_value": done1 / el1}
 
 
 if __name__ == "__main__":

@@ -106,6 +106,10 @@ def _c(a, dt):
 
 
 def n_threads() -> int:
+    """Host threads the drivers use: SQO_THREADS if set, else the usable
+    cores (at most 16)."""
+    if os.environ.get("SQO_THREADS"):
+        return max(1, min(64, int(os.environ["SQO_THREADS"])))
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
