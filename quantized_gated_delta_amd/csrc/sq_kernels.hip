@@ -25,6 +25,14 @@
 //   y_j     = sum_i q_i S'_ij                         (read-out, fp32)
 //   c'_j    = max_i |S'_ij|,  r'_i = max_j |S'_ij| / c'_j / qmax
 //   code'   = round_half_even((S'_ij / c'_j) / r'_i)  (pinned fp32, in place)
+//
+// Variants of the same body, chosen per launch or per head:
+//   - split step (decode_update): S' goes to a workspace instead of being
+//     requantized; quant_state of that workspace completes it;
+//   - key-row-aware fit (pools with row-impact scores): a different
+//     requantizer, kra_quantize_store;
+//   - FP16 pivot heads (bits 16): the state kept as binary16;
+//   - per-key-row widths (bits 0): each row its own width, see Rows.
 #include <float.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -878,7 +886,6 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
         const double cj = (double)cur.cj;
         lds_cu[colvec2_idx(t)] = make_double2(cj, (double)cur.beta * ((double)cur.vj - P * cj));
     }
-#ifndef SQ_KEEP_F64_CODES
     // keep the packed codes, not their FP64 values, live across the barrier
     // (unpacking again costs two VALU per code; holding FP64 codes would cost
     // 128 VGPRs and halve the waves per SIMD)
@@ -886,7 +893,6 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int i = 0; i < Seg<BITS>::NWORDS; ++i) asm volatile("" : "+v"(seg[m].w[i]));
-#endif
     __syncthreads();
     // ---- decay + delta write in FP64, rounded once to fp32; read-out and
     //      column maxima partials in fp32
@@ -1081,16 +1087,14 @@ __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const St
     }
 }
 
-#ifndef SQ_DECODE_WAVES_PER_EU
-#define SQ_DECODE_WAVES_PER_EU 4
-#endif
+constexpr int kDecodeWavesPerEU = 4;
 // One workgroup per (request, head) tile; four resident per CU (VGPRs and
 // LDS both sized for four 4-wave workgroups), which hides the barriers and
 // reduction phases of one tile behind the others.
 // ROWS: the pool has heads with per-key-row widths (their own kernel, so
 // that pools without them keep the register budget of the uniform bodies).
 template <int D, bool KDA, bool SPLIT, bool KRA, bool ROWS, typename TI, typename TO>
-__global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(SQ_DECODE_WAVES_PER_EU)))
+__global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerEU)))
 void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
     __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D>::TOTAL];
     const int tile = blockIdx.x;
