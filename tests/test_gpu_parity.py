@@ -757,3 +757,46 @@ def test_rows_kda_trajectory_256_steps():
     log("rows kda: worst y rel-L2 %.3g, final state rel-L2 %.3g" % (worst_y, err))
     assert worst_y <= Hn.Y_REL_L2
     assert err <= Hn.STATE_REL_L2
+
+
+# ----------------------------------------------------------------- limits
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_max_heads_and_ragged_batch(gate):
+    """The largest head count (64) with every width kind in one pool, a batch
+    of 37 requests spread over 100 slots (ragged against everything): two
+    steps on sampled rows against the oracle, spare slots untouched."""
+    H, d, B, n_slots = 64, 128, 37, 100
+    log("max heads %s" % gate)
+    rng = np.random.default_rng(64)
+    bits = rng.choice([4, 6, 8, 16, 0], H)
+    rows_w = _row_widths(H, d, 64)
+    wl = W.custom(gate, B, H, d, bits, dtype="bf16", n_slots=n_slots, permute=True, seed=12,
+                  row_bits=rows_w)
+    side = Side(wl, wl.layers[0])
+    side.gpu_warmup_all()
+    rows = sample_rows(B, H, 96, seed=4)
+    side.init_oracle_rows(rows)
+    before = side.gpu_pool()
+    spare = np.setdiff1d(np.arange(n_slots), wl.layers[0].slot_of)
+    for t in range(2):
+        side.push_rows(rows)
+        y_gpu, y_ref = side.step(t, rows)
+        assert Hn.rel_l2(y_gpu, y_ref) <= Hn.Y_REL_L2
+        after = side.gpu_pool()
+        check_records(side, rows, after, "max heads step %d" % t)
+    st = side.host.stride
+    for s in spare:
+        assert np.array_equal(after[s * st:(s + 1) * st], before[s * st:(s + 1) * st]), s
+
+
+def test_single_request_single_head():
+    """B = 1, H = 1 at d = 128 (the smallest launch: one workgroup)."""
+    log("single tile")
+    wl = W.custom("kda", 1, 1, 128, [6], dtype="f32", n_slots=3, permute=True, seed=13)
+    side = Side(wl, wl.layers[0])
+    rows = Hn.rows_all(1, 1)
+    side.init_oracle_rows(rows)
+    for t in range(4):
+        y_gpu, y_ref = side.step(t, rows)
+        assert Hn.rel_l2(y_gpu, y_ref) <= Hn.Y_REL_L2
+        check_records(side, rows, side.gpu_pool(), "single step %d" % t)
