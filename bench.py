@@ -601,6 +601,15 @@ def trajectory(args, dev):
             schemes[name] = np.zeros(H, np.uint8)
             row_bits[name] = rb
             perms[name] = torch.from_numpy(perm).to(dev)
+            # per-row widths chosen by the lifetime objective (R22-R23 at the
+            # key-row unit): per-row distortion of the calibration states,
+            # per-row lifetime weights from the warm-up log-gates
+            E = A.measure_row_distortion(state[:args.calib])
+            rb2, perm2 = A.allocate_row_bits(E, A.row_lifetime_weights(np.stack(gsum)), 6.0)
+            name = "per_row_lifetime_optimized_6"
+            schemes[name] = np.zeros(H, np.uint8)
+            row_bits[name] = rb2
+            perms[name] = torch.from_numpy(perm2).to(dev)
         pools = {}
         for name, hb in schemes.items():
             pool = Q.StatePool(B, H, d, [int(b) for b in hb], layer.gate, device=dev,
@@ -613,14 +622,14 @@ def trajectory(args, dev):
             else:
                 pool.quant_state(ident, state)
             pools[name] = pool
-        layers.append((layer, kda, state, pools, schemes, cal, perms))
+        layers.append((layer, kda, state, pools, schemes, cal, perms, row_bits))
     torch.cuda.synchronize()
-    errs = {(l.index, n): [] for l, _, _, pools, _, _, _ in layers for n in pools}
+    errs = {(l.index, n): [] for l, _, _, pools, _, _, _, _ in layers for n in pools}
     yq = torch.empty((B * H, d), dtype=torch.bfloat16, device=dev)
     yf = torch.empty((B * H, d), dtype=torch.bfloat16, device=dev)
     t0 = time.time()
     for t in range(T):
-        for layer, kda, state, pools, _, _, perms in layers:
+        for layer, kda, state, pools, _, _, perms, _ in layers:
             x = {k: to_dev(v) for k, v in wl.step_inputs(layer, t).items()}
             Q.sq_f32_decode_step(state, B, H, d, d, int(kda), ident, B, x["q"], x["k"], x["v"],
                                  x["beta"], x["g"], yf)
@@ -642,14 +651,17 @@ def trajectory(args, dev):
                                             time.time() - t0))
     out = {"workload": "c4: GDN + KDA layers, B=1024, H=32, d=128, bf16, %d steps" % T,
            "y_rel_l2_vs_fp32_state": {}}
-    for layer, _, _, pools, schemes, cal, _ in layers:
+    for layer, _, _, pools, schemes, cal, _, row_bits in layers:
         per = {}
         for name, pool in pools.items():
             hb = schemes[name]
             e = np.array(errs[(layer.index, name)])
             marks = {str(s): float(e[s - 1]) for s in (1, 16, 64, 256, T) if s <= T}
+            rbn = row_bits.get(name)
             per[name] = {"bits": {str(b): int((hb == b).sum()) for b in (0, 4, 6, 8, 16)
                                   if (hb == b).any()},
+                         "row_bits": None if rbn is None else
+                         {str(b): int((rbn == b).sum()) for b in (4, 6, 8)},
                          "slot_bytes": int(pool.slot_stride),
                          "at_step": marks, "mean": float(e.mean()), "max": float(e.max())}
         entry = per if args.allocate else per["fixed_c4_mix"]

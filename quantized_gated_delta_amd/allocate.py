@@ -169,6 +169,94 @@ def measure_distortion(states, candidates: Sequence[int] = (4, 6, 8)) -> np.ndar
     return out
 
 
+def row_lifetime_weights(log_gates) -> np.ndarray:
+    """Per key row lifetime weights [H, d_k] from KDA log-gates [T, H, d_k]
+    (the KDA unit of the allocation is the key row)."""
+    g = np.asarray(log_gates, np.float64)
+    if g.ndim != 3:
+        raise ValueError("log_gates must be [T, H, d_k]")
+    return lifetime_weights(g.mean(axis=0))
+
+
+def allocate_row_bits(distortion: np.ndarray, weights: np.ndarray, avg_bits: float,
+                      candidates: Sequence[int] = (4, 6, 8), grain: int = 8):
+    """Key-row widths under an average budget over all rows of all heads.
+
+    distortion: [H, d, len(candidates)] per-row distortion at each width
+    (row i's codes depend only on its own width, so these come from uniform
+    quantizations); weights: [H, d] per-row lifetime weights.
+
+    The pool layout needs each head's widths grouped, non-decreasing, on a
+    grain of `grain` rows; the key channels may be permuted offline to get
+    there.  So each head's rows are ordered by risk (weight x distortion at
+    the smallest width), cut into groups of `grain`, and the groups take
+    widths greedily by the largest decrease of sum_i w_i D_i(b_i) per added
+    bit.  Returns (row_bits [H, d] non-decreasing along the physical rows,
+    perm [H, d]: physical row p of head h holds key channel perm[h, p])."""
+    D = np.asarray(distortion, np.float64)
+    w = np.asarray(weights, np.float64)
+    cand = list(candidates)
+    H, d, nc = D.shape
+    if w.shape != (H, d) or nc != len(cand) or d % grain:
+        raise ValueError("distortion [H, d, n_candidates], weights [H, d], d a multiple of grain")
+    perm = np.argsort(w * D[:, :, 0], axis=1, kind="stable")
+    Dp = np.take_along_axis(D, perm[:, :, None], axis=1)
+    wp = np.take_along_axis(w, perm, axis=1)
+    G = d // grain
+    obj = (wp[:, :, None] * Dp).reshape(H, G, grain, nc).sum(axis=2)   # [H, G, nc]
+    level = np.zeros((H, G), np.int64)
+    budget = (avg_bits - cand[0]) * H * d
+    if budget < -1e-9:
+        raise ValueError("budget below the smallest width")
+    while True:
+        best, best_gain = None, 0.0
+        for h in range(H):
+            for g in range(G):
+                l = level[h, g]
+                if l + 1 >= nc:
+                    continue
+                extra = (cand[l + 1] - cand[l]) * grain
+                if extra > budget + 1e-9:
+                    continue
+                gain = (obj[h, g, l] - obj[h, g, l + 1]) / extra
+                if gain > best_gain:
+                    best, best_gain = (h, g), gain
+        if best is None:
+            break
+        h, g = best
+        budget -= (cand[level[h, g] + 1] - cand[level[h, g]]) * grain
+        level[h, g] += 1
+    # groups in risk order normally come out non-decreasing; where they do
+    # not, the group order is rearranged to match (rows move with their group)
+    order = np.argsort(level, axis=1, kind="stable")
+    level = np.take_along_axis(level, order, axis=1)
+    perm = np.take_along_axis(perm.reshape(H, G, grain), order[:, :, None], axis=1).reshape(H, d)
+    widths = np.asarray(cand)[level]
+    return np.repeat(widths, grain, axis=1).astype(np.uint8), perm.astype(np.int64)
+
+
+def measure_row_distortion(states, candidates: Sequence[int] = (4, 6, 8)) -> np.ndarray:
+    """E[h, i, b]: mean over requests of ||S_i - DQ_b(S)_i||^2 / ||S||^2 for
+    each key row i of fp32 device states [N, H, d, d], through the pool's
+    quant / dequant kernels at uniform widths."""
+    import torch
+
+    from .sq import StatePool
+
+    N, H, d, _ = states.shape
+    slot = torch.arange(N, dtype=torch.int32, device=states.device)
+    out = np.zeros((H, d, len(candidates)))
+    energy = states.double().pow(2).sum(dim=(2, 3)).clamp_min(1e-300)     # [N, H]
+    for i, b in enumerate(candidates):
+        pool = StatePool(N, H, d, [b] * H, "kda", device=states.device)
+        pool.quant_state(slot, states)
+        back = pool.dequant_state(slot)
+        err = (back.double() - states.double()).pow(2).sum(dim=3)          # [N, H, d]
+        out[:, :, i] = (err / energy[:, :, None]).mean(dim=0).cpu().numpy()
+        pool.close()
+    return out
+
+
 def calibrate(states, log_gates, avg_bits: float = 6.0, candidates=(4, 6, 8),
               n_pivots: int = 0) -> dict:
     """Bits per head from calibration states [N, H, d, d] (device, fp32) and

@@ -144,3 +144,47 @@ def test_row_impact_streaming_equals_batch():
     for lo in range(0, 30, 7):
         acc.add(q[lo:lo + 7], k[lo:lo + 7], b[lo:lo + 7], g[lo:lo + 7])
     assert np.allclose(acc.scores(), A.row_impact(q, k, b, g), rtol=1e-6)
+
+
+def test_row_lifetime_weights():
+    g = np.zeros((5, 2, 4))
+    g[:, 1, 3] = -0.1
+    g[:, 0, 0] = -2.0
+    w = A.row_lifetime_weights(g)
+    assert w.shape == (2, 4)
+    assert math.isclose(w[1, 3], 1 / (1 - math.exp(-0.2)), rel_tol=1e-12)
+    assert math.isclose(w[0, 0], 1 / (1 - math.exp(-4.0)), rel_tol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_row_bits_greedy_matches_brute_force(seed):
+    """Small case: 2 heads x 2 groups of 2 rows.  With convex per-row
+    distortion the greedy reaches the best assignment of widths to the
+    risk-ordered groups (brute force); the returned widths are
+    non-decreasing along the physical rows, grouped on the grain, within
+    budget, and perm is a permutation that carries each row's terms."""
+    rng = np.random.default_rng(40 + seed)
+    H, d, grain, cand = 2, 4, 2, [4, 6, 8]
+    base = np.exp(rng.normal(0, 1, (H, d)))
+    D = np.stack([base * 4.0 ** (-(b - 4) / 2) for b in cand], axis=-1)
+    w = A.lifetime_weights(-rng.uniform(0.001, 0.5, (H, d)))
+    avg = float(rng.choice([5.0, 6.0, 7.0]))
+    rb, perm = A.allocate_row_bits(D, w, avg, cand, grain)
+    assert rb.shape == (H, d) and rb.mean() <= avg + 1e-9
+    assert (np.diff(rb.astype(int), axis=1) >= 0).all()
+    assert all(len(set(rb[h, g * grain:(g + 1) * grain])) == 1 for h in range(H) for g in range(2))
+    assert all(sorted(perm[h]) == list(range(d)) for h in range(H))
+
+    def objective(widths, pm):
+        return sum(w[h, pm[h, p]] * D[h, pm[h, p], cand.index(widths[h, p])]
+                   for h in range(H) for p in range(d))
+
+    risk = np.argsort(w * D[:, :, 0], axis=1, kind="stable")
+    best = None
+    for combo in itertools.product(cand, repeat=H * 2):
+        wd = np.repeat(np.array(combo).reshape(H, 2), grain, axis=1)
+        if wd.mean() > avg + 1e-9:
+            continue
+        o = objective(wd, risk)
+        best = o if best is None else min(best, o)
+    assert math.isclose(objective(rb, perm), best, rel_tol=1e-9)
