@@ -31,8 +31,15 @@
  * with -ffp-contract=off and without fast-math so that every fp32 operation
  * is one correctly rounded IEEE operation.
  *
+ * Also here: FP16 pivot records (bits 16), per-key-row widths (records
+ * with head width 0) and the key-row-aware dual-axis fit (sqo_quantize_kra).
+ *
  * Parity pins: see the oracle tests.  Every function below is pinned by at
- * least one closed form, identity, brute-force or convergence check.
+ * least one closed form, identity, brute-force or convergence check.  The
+ * key-row-aware fit is pinned to the reading written out above it (exact
+ * constructed case, square-root law, scale invariance, least-squares
+ * optimality, nearest levels); the pages give no formula for it, so against
+ * the pages themselves it is parity unpinned.
  */
 #include <float.h>
 #include <math.h>
