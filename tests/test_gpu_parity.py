@@ -800,3 +800,42 @@ def test_single_request_single_head():
         y_gpu, y_ref = side.step(t, rows)
         assert Hn.rel_l2(y_gpu, y_ref) <= Hn.Y_REL_L2
         check_records(side, rows, side.gpu_pool(), "single step %d" % t)
+
+
+def test_decode_step_in_a_hip_graph():
+    """The decode step records into a HIP graph (it allocates nothing and
+    enqueues no memset): three replays, each with new inputs copied into the
+    captured buffers and eager work in between, give byte-identical records
+    and y to the same steps run eagerly."""
+    B, H, d = 6, 4, 128
+    log("hip graph")
+    wl = W.custom("kda", B, H, d, [6, 4, 8, 16], dtype="bf16", n_slots=8, permute=True, seed=14)
+    side = Side(wl, wl.layers[0])
+    rows = Hn.rows_all(B, H)
+    side.init_oracle_rows(rows)
+    lay = wl.layers[0]
+    graph_pool = Q.StatePool(wl.n_slots, H, d, lay.head_bits.tolist(), lay.gate)
+    graph_pool.buf.copy_(side.gpu.buf)
+    x0 = dev_inputs(wl.step_inputs(lay, 0))
+    static = {k: v.clone() for k, v in x0.items()}
+    y_g = torch.empty((B * H, d), dtype=torch.bfloat16, device=DEV)
+    # warm up on a side stream, as graph capture requires, then capture
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graph_pool.decode_step(side.slot_dev, static["q"], static["k"], static["v"],
+                               static["beta"], static["g"], y_g)
+    torch.cuda.synchronize()
+    graph_pool.buf.copy_(side.gpu.buf)          # capture does not run the kernel
+    y_e = torch.empty_like(y_g)
+    for t in range(3):
+        x = dev_inputs(wl.step_inputs(lay, t))
+        for k in static:
+            static[k].copy_(x[k])
+        g.replay()
+        side.gpu.decode_step(side.slot_dev, x["q"], x["k"], x["v"], x["beta"], x["g"], y_e)
+        torch.cuda.synchronize()
+        assert torch.equal(graph_pool.buf, side.gpu.buf), t
+        assert torch.equal(y_g, y_e), t
