@@ -729,7 +729,11 @@ def cpu_baseline(wl, layer, seconds, single_seconds=3.0):
     return {"value": done / el, "unit": "state-updates/s", "cores": nthr, "kind": "oracle",
             "sample": "%d rows x %d passes of the B=%d H=%d d=%d step (%.1f s wall)"
                       % (n_rows, done // n_rows, wl.B, H, d, el),
-            "single_thread_value": done1 / el1}
+            "single_thread_value": done1 / el1,
+            # the same per-update byte model as the GPU line (codes + scales
+            # read and written, q/k/v/beta/g/y), per sampled update
+            "equivalent_GBps": done / el * algo_bytes_per_step(
+                1, n_rows, d, bits, layer.gate, 2 if wl.dtype == "bf16" else 4) / n_rows / 1e9}
 
 
 if __name__ == "__main__":
