@@ -2,9 +2,12 @@
 
     python -m quantized_gated_delta_amd.rocprof_summary trace <dir> <kernel-substring>
     python -m quantized_gated_delta_amd.rocprof_summary pmc <dir> <kernel-substring> [<copy-dir>]
+    python -m quantized_gated_delta_amd.rocprof_summary bygrid <dir> <kernel-substring>
 
 trace: per-kernel dispatch count and average / median / min / max duration
        from ``*_kernel_trace.csv`` (rocprofv3 --kernel-trace --output-format csv).
+bygrid: like trace, but one entry per (kernel, grid size), so one kernel
+       launched on several workload shapes is summarised per shape.
 pmc:   per-dispatch averages of every counter in ``*_counter_collection.csv``
        (rocprofv3 --pmc ... --output-format csv).  FETCH_SIZE and WRITE_SIZE
        are reported in KiB per dispatch; with a copy-run directory the same
@@ -44,6 +47,22 @@ def trace(d: str, pattern: str) -> dict:
             "vgpr": rows[0].get("VGPR_Count"), "lds": rows[0].get("LDS_Block_Size")}
 
 
+def bygrid(d: str, pattern: str) -> list:
+    groups = {}
+    for r in _rows(d, "kernel_trace.csv"):
+        if pattern not in r["Kernel_Name"]:
+            continue
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = []
+    for (name, grid, wg), durs in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        out.append({"kernel": name, "workgroups": grid // max(1, wg), "dispatches": len(durs),
+                    "avg_us": statistics.mean(durs), "median_us": statistics.median(durs),
+                    "min_us": min(durs), "max_us": max(durs)})
+    return out
+
+
 def pmc(d: str, pattern: str) -> dict:
     per = {}
     for r in _rows(d, "counter_collection.csv"):
@@ -67,6 +86,8 @@ def main(argv):
     mode, d, pattern = argv[1], argv[2], argv[3]
     if mode == "trace":
         print(json.dumps(trace(d, pattern), indent=1))
+    elif mode == "bygrid":
+        print(json.dumps(bygrid(d, pattern), indent=1))
     elif mode == "pmc":
         print(json.dumps(pmc(d, pattern), indent=1))
     else:
