@@ -102,11 +102,28 @@ def _check(status: int, func: str):
 
 
 def _ptr(x) -> Optional[int]:
+    """Raw pointer of an int, a ctypes array or a torch tensor.  Tensors must
+    be contiguous: the library reads them as dense row-major arrays."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if hasattr(x, "is_contiguous") and not x.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
     return x.data_ptr()
+
+
+def _need(t, name, numel, dtypes):
+    """Shape / dtype / device check of one tensor argument (marshalling only)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.numel() != numel:
+        raise ValueError("%s has %d elements, expected %d" % (name, t.numel(), numel))
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
 
 
 def _dtype_code(t) -> int:
@@ -259,8 +276,25 @@ class StatePool:
                                      nbytes, self.row_bits)
         self.slot_stride, self.head_off, self.record_bytes = sq_pool_layout(self.handle, n_heads)
 
+    def _step_args(self, slot_idx, q, k, v, beta, g, y):
+        import torch
+        n, H, d = slot_idx.numel(), self.n_heads, self.d
+        _need(slot_idx, "slot_idx", n, (torch.int32,))
+        dt = (q.dtype,)
+        if q.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("q must be float32 or bfloat16")
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            _need(t, name, n * H * d, dt)
+        _need(beta, "beta", n * H, dt)
+        _need(g, "g", n * H * (d if self.gate == SQ_GATE_KDA else 1), dt)
+        _need(y, "y", n * H * d, (torch.float32, torch.bfloat16))
+
     def quant_state(self, slot_idx, S, stream=None):
-        sq_quant_state(self.handle, slot_idx, slot_idx.numel(), S, stream)
+        import torch
+        n = slot_idx.numel()
+        _need(slot_idx, "slot_idx", n, (torch.int32,))
+        _need(S, "S", n * self.n_heads * self.d * self.d, (torch.float32,))
+        sq_quant_state(self.handle, slot_idx, n, S, stream)
 
     def dequant_state(self, slot_idx, S=None, stream=None):
         import torch
@@ -268,10 +302,13 @@ class StatePool:
         if S is None:
             S = torch.empty((n, self.n_heads, self.d, self.d), dtype=torch.float32,
                             device=self.buf.device)
+        _need(slot_idx, "slot_idx", n, (torch.int32,))
+        _need(S, "S", n * self.n_heads * self.d * self.d, (torch.float32,))
         sq_dequant_state(self.handle, slot_idx, n, S, stream)
         return S
 
     def decode_step(self, slot_idx, q, k, v, beta, g, y, stream=None):
+        self._step_args(slot_idx, q, k, v, beta, g, y)
         sq_decode_step(self.handle, slot_idx, slot_idx.numel(), q, k, v, beta, g, y,
                        stream=stream)
 
@@ -287,6 +324,9 @@ class StatePool:
     def decode_update(self, slot_idx, q, k, v, beta, g, y, S_out, stream=None):
         """Split step, first half: y and S' (fp32) out, pool unchanged; store
         with quant_state(slot_idx, S_out) afterwards."""
+        import torch
+        self._step_args(slot_idx, q, k, v, beta, g, y)
+        _need(S_out, "S_out", slot_idx.numel() * self.n_heads * self.d * self.d, (torch.float32,))
         sq_decode_update(self.handle, slot_idx, slot_idx.numel(), q, k, v, beta, g, y, S_out,
                          stream=stream)
 

@@ -241,3 +241,15 @@ def test_per_row_width_validation():
     # rows of uniform heads are not read
     assert Q.sq_pool_bytes(2, 2, d, d, [6, 0], 1, row_bits=[[0] * d, ok]) == \
         2 * (13312 + _rows_rec(ok, d))
+
+
+def test_binding_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    t = torch.zeros(4, 6)
+    with pytest.raises(ValueError):
+        S._ptr(t.t())                       # non-contiguous
+    assert S._ptr(t) == t.data_ptr()
+    with pytest.raises(ValueError):
+        S._need(t, "q", 24, (torch.float32,))   # host tensor
+    with pytest.raises(TypeError):
+        S._need([1, 2], "q", 2, (torch.float32,))
