@@ -82,7 +82,7 @@ extern "C" {
 typedef enum {
     SQ_OK = 0,
     SQ_EINVAL = 1,        /* bad argument (null, misaligned, out of range) */
-    SQ_EUNSUPPORTED = 2,  /* shape or bit width this build does not handle */
+    SQ_EUNSUPPORTED = 2,  /* shape or bit width the library does not handle */
     SQ_ENOMEM = 3,        /* buffer too small / host allocation failed */
     SQ_EHIP = 4           /* a HIP runtime call failed (text in sq_last_error) */
 } sq_status;
