@@ -75,6 +75,8 @@ def lib():
         L.sqo_dequantize.argtypes = [i32, i32, vp, vp, vp, vp]
         L.sqo_gated_delta_f64.restype = None
         L.sqo_gated_delta_f64.argtypes = [i32, i32, vp, vp, vp, vp, vp, ctypes.c_double, vp]
+        L.sqo_step_update.restype = None
+        L.sqo_step_update.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp]
         L.sqo_quant_step_codes.restype = None
         L.sqo_quant_step_codes.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, f32,
                                            vp, vp, vp]
@@ -251,6 +253,22 @@ def gated_delta_f64(S, alpha, q, k, v, beta) -> tuple:
     y = np.empty(dv, np.float64)
     a, q, k, v = (_c(x, np.float64) for x in (alpha, q, k, v))
     lib().sqo_gated_delta_f64(dk, dv, _p(S), _p(a), _p(q), _p(k), _p(v), float(beta), _p(y))
+    return S, y
+
+
+def step_update(Z, R, C, alpha, q, k, v, beta) -> tuple:
+    """The update of one step on stored values Z [dk, dv] with row scales R,
+    column scales C and retention alpha (all fp32): returns (S' fp32, y FP64)."""
+    Z = _c(Z, np.float32)
+    dk, dv = Z.shape
+    R, C, alpha = _c(R, np.float32), _c(C, np.float32), _c(alpha, np.float32)
+    q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+    assert R.shape == (dk,) and C.shape == (dv,) and alpha.shape == (dk,)
+    assert q.shape == (dk,) and k.shape == (dk,) and v.shape == (dv,)
+    S = np.empty((dk, dv), np.float32)
+    y = np.empty(dv, np.float64)
+    lib().sqo_step_update(dk, dv, _p(Z), _p(R), _p(C), _p(alpha), _p(q), _p(k), _p(v),
+                          float(np.float32(beta)), _p(S), _p(y))
     return S, y
 
 

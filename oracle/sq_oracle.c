@@ -26,10 +26,12 @@
  *    fit has no formula on the pages) is: c_j = max_i |S_ij|, then
  *    r_i = max_j |S_ij / c_j| / qmax.
  *
- * Precision: the step runs in FP64 between an fp32 dequantizer and an fp32
- * quantizer whose operation order is fixed here (see sqo_quantize).  Build
- * with -ffp-contract=off and without fast-math so that every fp32 operation
- * is one correctly rounded IEEE operation.
+ * Precision (the pages fix none beyond "floating point"): the step's
+ * reductions (what k retrieves) run in FP64 and are rounded once to fp32;
+ * the element-wise rank-1 update runs in fp32 in the order stated at
+ * sqo_step_update; the quantizer's fp32 order is fixed at sqo_quantize.
+ * Build with -ffp-contract=off and without fast-math so that every fp32
+ * operation is one correctly rounded IEEE operation.
  *
  * Also here: FP16 pivot records (bits 16), per-key-row widths (records
  * with head width 0) and the key-row-aware dual-axis fit (sqo_quantize_kra).
@@ -397,38 +399,83 @@ static void gate_alpha(int kda, int dk, const float *g, double *alpha) {
     }
 }
 
+static void gate_alpha_f32(int kda, int dk, const float *g, float *alpha) {
+    for (int i = 0; i < dk; ++i) alpha[i] = (float)exp((double)(kda ? g[i] : g[0]));
+}
+
+/*
+ * The update of one step on a stored state (paper section 2.1 as the
+ * ta-paperlens page explains it: decay, look-up, delta write, read-out;
+ * hyper.ai "Method" paragraph 1: the reconstructed state is updated in
+ * floating point and the output read before it is requantized).
+ * Z holds the stored numbers (integer codes, or widened binary16 values),
+ * R and C the row and column scales (r and c of a quantized record; all 1
+ * for a binary16 record), alpha the retention factors:
+ *   Sd_ij = alpha_i ((Z_ij R_i) C_j)                FP64: decayed reconstruction
+ *   u_j   = beta (v_j - sum_i k_i Sd_ij)            FP64: what k retrieves, the difference
+ *   u32_j = (float)u_j                              rounded once
+ *   W_ij  = (alpha_i R_i) C_j                       fp32, each product rounded
+ *   S'_ij = fmaf(Z_ij, W_ij, k_i u32_j)             fp32: k_i u32_j rounded, then one
+ *                                                   fused multiply-add (Sd + k u^T)
+ *   y_j   = sum_i q_i S'_ij                         FP64 over the fp32 S'
+ * The look-up sum is the only reduction over the state; in FP64 and rounded
+ * once, its value does not depend on the order of summation except on the
+ * rare exact near-ties of that rounding.  Every other step is element-wise
+ * and has one result.
+ */
+void sqo_step_update(int dk, int dv, const float *Z, const float *R, const float *C,
+                     const float *alpha, const float *q, const float *k, const float *v,
+                     float beta, float *S, double *y) {
+    float *u32 = (float *)malloc(sizeof(float) * (size_t)dv);
+    for (int j = 0; j < dv; ++j) {
+        double vo = 0.0;
+        for (int i = 0; i < dk; ++i) {
+            const double sd = (double)alpha[i] *
+                              (((double)Z[(size_t)i * dv + j] * (double)R[i]) * (double)C[j]);
+            vo += (double)k[i] * sd;
+        }
+        u32[j] = (float)((double)beta * ((double)v[j] - vo));
+    }
+    for (int i = 0; i < dk; ++i) {
+        const float wr = alpha[i] * R[i];
+        for (int j = 0; j < dv; ++j) {
+            const float w = wr * C[j];
+            const float ku = k[i] * u32[j];
+            S[(size_t)i * dv + j] = fmaf(Z[(size_t)i * dv + j], w, ku);
+        }
+    }
+    for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += (double)q[i] * (double)S[(size_t)i * dv + j];
+        y[j] = acc;
+    }
+    free(u32);
+}
+
 /*
  * Quantized step on one head with unpacked codes (any bits 2..24):
- * FP64 reconstruction -> FP64 gated delta step -> round S' to fp32 ->
+ * the step update above on the codes -> fp32 S' ->
  * pinned fp32 quantizer (the closed rule, or the key-row-aware fit when
- * imp != NULL gives the row-impact scores).  y receives the read-out of the unrequantized S'
- * (hyper.ai "Method" para 1: the state is updated in floating point and the
- * output computed, then the updated state is quantized for storage).
+ * imp != NULL gives the row-impact scores).  y receives the read-out of the
+ * unrequantized S'.
  */
 void sqo_quant_step_codes_rows(int kda, const uint8_t *row_bits, int dk, int dv, int32_t *Q,
                                float *r, float *c, const float *q, const float *k, const float *v,
                                float beta, const float *g, const float *imp, double *y) {
     const size_t n = (size_t)dk * dv;
     float *S = (float *)malloc(sizeof(float) * n);
-    double *Sd = (double *)malloc(sizeof(double) * n);
-    double *vec = (double *)malloc(sizeof(double) * (size_t)(3 * dk + dv));
-    double *alpha = vec, *qd = vec + dk, *kd = vec + 2 * dk, *vd = vec + 3 * dk;
-    sqo_reconstruct_f64(dk, dv, Q, r, c, Sd);
-    gate_alpha(kda, dk, g, alpha);
-    for (int i = 0; i < dk; ++i) {
-        qd[i] = q[i];
-        kd[i] = k[i];
-    }
-    for (int j = 0; j < dv; ++j) vd[j] = v[j];
-    sqo_gated_delta_f64(dk, dv, Sd, alpha, qd, kd, vd, (double)beta, y);
-    for (size_t e = 0; e < n; ++e) S[e] = (float)Sd[e];
+    float *Z = (float *)malloc(sizeof(float) * n);
+    float *alpha = (float *)malloc(sizeof(float) * (size_t)dk);
+    for (size_t e = 0; e < n; ++e) Z[e] = (float)Q[e]; /* exact: |Q| < 2^24 */
+    gate_alpha_f32(kda, dk, g, alpha);
+    sqo_step_update(dk, dv, Z, r, c, alpha, q, k, v, beta, S, y);
     if (imp)
         sqo_quantize_kra(row_bits[0], dk, dv, S, imp, Q, r, c); /* uniform widths only */
     else
         sqo_quantize_rows(row_bits, dk, dv, S, Q, r, c);
     free(S);
-    free(Sd);
-    free(vec);
+    free(Z);
+    free(alpha);
 }
 
 void sqo_quant_step_codes(int kda, int bits, int dk, int dv, int32_t *Q, float *r, float *c,
@@ -481,24 +528,22 @@ int sqo_record_pack(int bits, int dk, int dv, const int32_t *Q, const float *r, 
     return sqo_record_pack_rows(rb, dk, dv, Q, r, c, rec);
 }
 
-/* FP16 pivot record: one step.  FP64 step on the exactly widened state, S'
- * rounded once to fp32 (as for the quantized records), then to binary16. */
+/* FP16 pivot record: one step.  The step update on the exactly widened
+ * binary16 values (unit scales), then S' rounded from fp32 to binary16. */
 static void f16_record_step(int kda, int dk, int dv, uint8_t *rec, const float *q,
                             const float *k, const float *v, float beta, const float *g,
                             double *y) {
     const size_t n = (size_t)dk * dv;
     uint16_t *h = (uint16_t *)rec;
-    double *S = (double *)malloc(sizeof(double) * n);
-    double alpha[1024], qd[1024], kd[1024], vd[1024];
-    for (size_t e = 0; e < n; ++e) S[e] = (double)sqo_f16_to_f32(h[e]);
-    gate_alpha(kda, dk, g, alpha);
-    for (int i = 0; i < dk; ++i) {
-        qd[i] = q[i];
-        kd[i] = k[i];
-    }
-    for (int j = 0; j < dv; ++j) vd[j] = v[j];
-    sqo_gated_delta_f64(dk, dv, S, alpha, qd, kd, vd, (double)beta, y);
-    for (size_t e = 0; e < n; ++e) h[e] = sqo_f32_to_f16((float)S[e]);
+    float *Z = (float *)malloc(sizeof(float) * n);
+    float *S = (float *)malloc(sizeof(float) * n);
+    float alpha[1024], one[1024];
+    for (size_t e = 0; e < n; ++e) Z[e] = sqo_f16_to_f32(h[e]);
+    for (int i = 0; i < 1024; ++i) one[i] = 1.0f;
+    gate_alpha_f32(kda, dk, g, alpha);
+    sqo_step_update(dk, dv, Z, one, one, alpha, q, k, v, beta, S, y);
+    for (size_t e = 0; e < n; ++e) h[e] = sqo_f32_to_f16(S[e]);
+    free(Z);
     free(S);
 }
 

@@ -12,16 +12,17 @@
 // writes its 16-column partials, then lane j < d folds column j.
 //
 // The decode step, per tile (STEPQuant pages: ta-paperlens, mechanism
-// section; hyper.ai summary, Method paragraphs 1 and 4).  The look-up and
-// the update run in FP64 (full rate on CDNA4, like non-packed fp32) so that
-// the updated state rounds to the same fp32 value as an FP64 reference: the
-// quantized recurrence amplifies any +-1 code difference, so the stored
-// codes must not depend on summation order.
-//   S_ij    = code_ij r_i c_j                        (exact product, FP64)
+// section; hyper.ai summary, Method paragraphs 1 and 4).  The one reduction
+// over the state, the look-up, runs in FP64 (full rate on CDNA4, like
+// non-packed fp32) and is rounded once, so that it does not depend on the
+// order of summation: the quantized recurrence amplifies any +-1 code
+// difference, so the stored codes must be those of the stated arithmetic.
+// Everything after it is element-wise fp32 with one fixed order.
 //   a_i     = (float) exp(g) or exp(g_i)              (retention gate)
 //   v_old_j = c_j * sum_i (k_i a_i r_i) code_ij       (look-up through k, FP64)
-//   u_j     = beta (v_j - v_old_j)                    (delta, FP64)
-//   S'_ij   = fl32(code_ij (a_i r_i c_j) + k_i u_j)   (decay + delta write)
+//   u_j     = fl32(beta (v_j - v_old_j))              (delta, FP64, rounded once)
+//   S'_ij   = fma(code_ij, (a_i r_i) c_j, k_i u_j)    (decay + delta write, fp32:
+//                                                      each product rounded once)
 //   y_j     = sum_i q_i S'_ij                         (read-out, fp32)
 //   c'_j    = max_i |S'_ij|,  r'_i = max_j |S'_ij| / c'_j / qmax
 //   code'   = round_half_even((S'_ij / c'_j) / r'_i)  (pinned fp32, in place)
@@ -281,8 +282,8 @@ template <int D, int BITS, bool MIXED> struct Rows {
 // eight lanes land on eight different 16-byte bank groups.
 //   fp32 plane [NB][D]:  float4 chunk c4 of lane t stored at c4 ^ ((t >> 1) & 3)
 //   FP64 plane [NB][D]:  double2 chunk c2 of lane t stored at c2 ^ (t & 7)
-//   per-column vectors read by column group cg: element n at n ^ cg (double2),
-//   or float4 chunk c4 at c4 ^ ((cg >> 1) & 3) (floats)
+//   per-column vectors read by column group cg: element n at n ^ cg (8- or
+//   16-byte elements), or float4 chunk c4 at c4 ^ ((cg >> 1) & 3) (floats)
 template <int D> __device__ __forceinline__ int plane_idx(int band, int cg, int n) {
     const int key = ((band * Geo<D>::CG + cg) >> 1) & 3;
     return band * D + 16 * cg + (((n >> 2) ^ key) << 2) + (n & 3);
@@ -559,10 +560,11 @@ __global__ __launch_bounds__(Geo<D>::NT) void dequant_state_kernel(PoolView pool
 // ---------------------------------------------------------------- decode step
 // LDS: the band-partials region (NB x D doubles in the look-up phase, reused
 // as two NB x D fp32 planes for the column maxima and the read-out), then
-// u[D] doubles, 1/c'[D] floats and one k.q partial per wave.
+// 4 D floats of per-column vectors ({c_j, u_j} fp32 pairs in the step; FP64
+// column sums in the key-row-aware fit), 1/c'[D] floats and misc.
 template <int D> struct DecodeLds {
     static constexpr int PART_F = 2 * Geo<D>::NB * D; // floats in the partials region
-    static constexpr int TOTAL = PART_F + 4 * D + D + 8; // + {c_j, u_j} FP64 pairs, 1/c'_j, misc
+    static constexpr int TOTAL = PART_F + 4 * D + D + 8; // + column vectors, 1/c'_j, misc
 };
 
 // Lane t of a band of CG lanes reads lane (band base + m) with ds_swizzle
@@ -827,7 +829,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     double *part64 = reinterpret_cast<double *>(lds);
     float *plane_max = lds, *plane_y = lds + PLANE;
-    double2 *lds_cu = reinterpret_cast<double2 *>(lds + DecodeLds<D>::PART_F); // {c_j, u_j}
+    float2 *lds_cu = reinterpret_cast<float2 *>(lds + DecodeLds<D>::PART_F); // {c_j, u_j}
     float *lds_ic = lds + DecodeLds<D>::PART_F + 4 * D;
     float *lds_misc = lds_ic + D; // [0]: GDN gate factor
     TileIn cur;
@@ -883,8 +885,9 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
 #pragma unroll 8
         for (int b = 0; b < G::NB; ++b) P += part64[part_idx<D>(b, t >> 4, t & 15)];
         if constexpr (!KDA) P *= (double)am[0];
-        const double cj = (double)cur.cj;
-        lds_cu[colvec2_idx(t)] = make_double2(cj, (double)cur.beta * ((double)cur.vj - P * cj));
+        // u_j in FP64, rounded once to fp32
+        lds_cu[colvec2_idx(t)] =
+            make_float2(cur.cj, (float)((double)cur.beta * ((double)cur.vj - P * (double)cur.cj)));
     }
     // keep the packed codes, not their FP64 values, live across the barrier
     // (unpacking again costs two VALU per code; holding FP64 codes would cost
@@ -894,29 +897,27 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
 #pragma unroll
         for (int i = 0; i < Seg<BITS>::NWORDS; ++i) asm volatile("" : "+v"(seg[m].w[i]));
     __syncthreads();
-    // ---- decay + delta write in FP64, rounded once to fp32; read-out and
-    //      column maxima partials in fp32
+    // ---- decay + delta write in fp32: S'_mn = fma(code, (a_m r_m) c_n, k_m u_n),
+    //      each product rounded once; read-out and column maxima partials
     float x[4][16];
     float *s_out = SPLIT ? io.s_out + (int64_t)tile * D * D : nullptr;
     {
-        double ar[4];
+        float ar[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) ar[m] = (double)am[m] * (double)cur.r[m]; // exact
+        for (int m = 0; m < 4; ++m) ar[m] = am[m] * cur.r[m];
 #pragma unroll
         for (int n4 = 0; n4 < 4; ++n4) {
             float cm[4], yp[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int n = 4 * n4 + i;
-                const double2 cu = lds_cu[colvec2_idx(16 * cg + n)];
-                const double cn = cu.x, un = cu.y;
+                const float2 cu = lds_cu[colvec2_idx(16 * cg + n)];
+                const float cn = cu.x, un = cu.y;
                 cm[i] = 0.0f;
                 yp[i] = 0.0f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const double sv = fma((double)code_at<BITS>(seg[m], n), ar[m] * cn,
-                                          (double)cur.k[m] * un);
-                    const float sf = (float)sv;
+                    const float sf = fmaf((float)code_at<BITS>(seg[m], n), ar[m] * cn, cur.k[m] * un);
                     x[m][n] = sf;
                     yp[i] = fmaf(cur.q[m], sf, yp[i]);
                     cm[i] = fmaxf(cm[i], fabsf(sf));
@@ -960,8 +961,9 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     }
 }
 
-// FP16 pivot record: the same FP64 look-up and update on the exactly
-// widened state, S' rounded once to fp32 (read-out) and then to binary16.
+// FP16 pivot record: the same FP64 look-up on the exactly widened state and
+// the same fp32 update with unit scales, S' = fma(h_ij, a_i, k_i u_j), then
+// rounded to binary16.
 template <int D, bool KDA, bool SPLIT, typename TI, typename TO>
 __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const StepIO &io,
                                                 float *lds) {
@@ -970,7 +972,7 @@ __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const St
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     double *part64 = reinterpret_cast<double *>(lds);
     float *plane_y = lds + PLANE;
-    double2 *lds_cu = reinterpret_cast<double2 *>(lds + DecodeLds<D>::PART_F);
+    float2 *lds_cu = reinterpret_cast<float2 *>(lds + DecodeLds<D>::PART_F);
     float *lds_misc = lds + DecodeLds<D>::PART_F + 5 * D;
     const int64_t row_io = tile;
     const TI *k = reinterpret_cast<const TI *>(io.k) + row_io * D;
@@ -1026,7 +1028,7 @@ __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const St
 #pragma unroll 8
         for (int b = 0; b < G::NB; ++b) P += part64[part_idx<D>(b, t >> 4, t & 15)];
         if constexpr (!KDA) P *= (double)am[0];
-        lds_cu[colvec2_idx(t)] = make_double2(1.0, (double)beta * ((double)vj - P));
+        lds_cu[colvec2_idx(t)] = make_float2(1.0f, (float)((double)beta * ((double)vj - P)));
     }
     __syncthreads();
     {
@@ -1035,17 +1037,17 @@ __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const St
         // held in registers across them
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const double a = (double)am[m], kk = (double)kf[m];
             uint32_t wm[8];
             load_half16<D>(rec, band + G::NB * m, cg, wm);
             float o[16];
 #pragma unroll
             for (int n = 0; n < 16; ++n) {
-                const double un = lds_cu[colvec2_idx(16 * cg + n)].y;
-                o[n] = (float)fma(a, (double)half_at(wm, n), kk * un);
+                const float un = lds_cu[colvec2_idx(16 * cg + n)].y;
+                o[n] = fmaf(half_at(wm, n), am[m], kf[m] * un);
                 // S' is rounded to fp32 first and binary16 second; the empty
-                // asm keeps the compiler from merging the two roundings into
-                // one double -> half conversion (which differs on near-ties)
+                // asm keeps the compiler from fusing the fma with the
+                // conversion (a mixed-precision fma rounds once, to binary16,
+                // which differs on near-ties)
                 asm volatile("" : "+v"(o[n]));
             }
             if constexpr (SPLIT) {

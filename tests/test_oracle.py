@@ -356,6 +356,72 @@ def test_delta_rule_identities():
     assert np.array_equal(S1, S * 0.9)
 
 
+# ------------------------------------------------------------------ step update
+def _dyadic_case(rng, dk, dv):
+    """Inputs on a coarse binary grid: small integer codes; scales, gates,
+    keys, beta and queries powers of two; v a multiple of 1/4.  Every
+    intermediate of the step then fits in fp32 exactly, so any correct
+    evaluation order returns the exact result."""
+    Z = rng.integers(-7, 8, (dk, dv)).astype(np.float32)
+    R = 2.0 ** -rng.integers(0, 3, dk)
+    C = 2.0 ** -rng.integers(0, 3, dv)
+    alpha = 2.0 ** -rng.integers(0, 3, dk)
+    k = rng.choice([-1, 1], dk) * 2.0 ** -rng.integers(0, 3, dk)
+    q = rng.choice([-1, 1], dk) * 2.0 ** -rng.integers(0, 2, dk)
+    v = rng.integers(-32, 33, dv) / 4.0
+    beta = 2.0 ** -int(rng.integers(0, 3))
+    return Z, R, C, alpha, q, k, v, beta
+
+
+@pytest.mark.parametrize("dk,dv", [(8, 8), (6, 10), (10, 6)])
+def test_step_update_exact_on_dyadic_inputs(dk, dv):
+    """On inputs where nothing rounds, the step update equals the exact
+    rational value of S' = (I - beta k k^T) D S + beta k v^T with
+    S_ij = Z_ij R_i C_j, and y = S'^T q (a dropped term, a wrong sign, a
+    transposed scale or a row/column mix-up fails this)."""
+    rng = np.random.default_rng(90 + dk)
+    F = Fraction
+    for _ in range(20):
+        Z, R, C, alpha, q, k, v, beta = _dyadic_case(rng, dk, dv)
+        Sp, y = O.step_update(Z, R, C, alpha, q, k, v, beta)
+        S = [[F(float(Z[i, j])) * F(R[i]) * F(C[j]) for j in range(dv)] for i in range(dk)]
+        A = [[((1 if i == m else 0) - F(beta) * F(k[i]) * F(k[m])) * F(alpha[m])
+              for m in range(dk)] for i in range(dk)]
+        want = [[sum(A[i][m] * S[m][j] for m in range(dk)) + F(beta) * F(k[i]) * F(v[j])
+                 for j in range(dv)] for i in range(dk)]
+        for i in range(dk):
+            for j in range(dv):
+                assert F(float(Sp[i, j])) == want[i][j]
+        for j in range(dv):
+            assert F(float(y[j])) == sum(F(q[i]) * want[i][j] for i in range(dk))
+
+
+def test_step_update_within_fp32_rounding_of_textbook():
+    """On random inputs every S'_ij lies within the rounding bound of its
+    fp32 evaluation (u rounded once, the two scale products, k u and the
+    fused multiply-add: at most 2^-24 (|S'| + 2|Sd| + 2|k u|) with Sd the
+    decayed reconstruction) of the textbook FP64 step."""
+    rng = np.random.default_rng(95)
+    for dk, dv in ((64, 64), (32, 48)):
+        for kda in (False, True):
+            Z = rng.integers(-31, 32, (dk, dv)).astype(np.float32)
+            R = (rng.uniform(0.5, 2, dk) * 1e-2).astype(np.float32)
+            C = rng.uniform(0.5, 2, dv).astype(np.float32)
+            q, k, v, beta, alpha = _inputs(rng, dk, dv, kda)
+            alpha = alpha.astype(np.float32)
+            Sp, y = O.step_update(Z, R, C, alpha, q, k, v, beta)
+            k32, v32, q32 = (x.astype(np.float32).astype(np.float64) for x in (k, v, q))
+            b32 = float(np.float32(beta))
+            S = Z.astype(np.float64) * R.astype(np.float64)[:, None] * C.astype(np.float64)[None]
+            T, yT = O.gated_delta_f64(S, alpha.astype(np.float64), q32, k32, v32, b32)
+            Sd = alpha.astype(np.float64)[:, None] * S
+            ku = np.abs(np.outer(k32, b32 * (v32 - Sd.T @ k32)))
+            bound = 2.0 ** -24 * (np.abs(T) + 2 * np.abs(Sd) + 2 * ku) * 1.001 + 1e-300
+            err = np.abs(Sp.astype(np.float64) - T)
+            assert (err <= bound).all(), float((err / bound).max())
+            assert (np.abs(y - yT) <= np.abs(q32) @ bound + 1e-12 * np.abs(yT).max()).all()
+
+
 # ------------------------------------------------------------------ quantized loop
 def _seq(rng, T, dk, dv, kda):
     seq = []
@@ -396,7 +462,9 @@ def test_error_propagation_identity(kda):
         E_new = Sq - St
         np.testing.assert_allclose(E_new, A @ E + eps, rtol=0,
                                    atol=1e-12 * max(1.0, np.abs(St).max()))
-        np.testing.assert_allclose(y, Fq.T @ q.astype(np.float64), rtol=0, atol=1e-12)
+        # y reads the fp32 S' (each element within a few fp32 roundings of Fq)
+        np.testing.assert_allclose(y, Fq.T @ q.astype(np.float64), rtol=0,
+                                   atol=1e-6 * np.abs(q).sum() * np.abs(Fq).max())
         E = E_new
 
 
@@ -459,7 +527,7 @@ def test_beta0_gate1_keeps_codes(bits):
     np.testing.assert_allclose(c, c0, rtol=4 * 2.0 ** -23)
     St = O.reconstruct_f64(Q0, r0, c0)
     np.testing.assert_allclose(y, St.T @ q.astype(np.float32).astype(np.float64), rtol=0,
-                               atol=1e-12)
+                               atol=4 * 2.0 ** -24 * (np.abs(q) @ np.abs(St)).max())
 
 
 # ------------------------------------------------------------------ batch drivers
@@ -560,8 +628,9 @@ def test_f16_conversions_match_numpy():
 
 
 def test_f16_record_step():
-    """A pivot record holds the state in binary16; one step is the FP64 step
-    on the widened state, rounded once to fp32 and then to binary16."""
+    """A pivot record holds the state in binary16; one step is the step
+    update on the widened values with unit scales, rounded from fp32 to
+    binary16, and within a binary16 rounding of the textbook step."""
     rng = np.random.default_rng(81)
     d = 32
     S = (rng.standard_normal((d, d)) * 3).astype(np.float32)
@@ -576,12 +645,16 @@ def test_f16_record_step():
     y = O.records_step(False, rec, np.array([0], np.int64), np.array([16], np.uint8), d, d,
                        q[None].astype(np.float32), k[None].astype(np.float32),
                        v[None].astype(np.float32), np.array([beta], np.float32), g)
-    alpha = np.full(d, float(np.float32(math.exp(-0.1))))
-    want, yw = O.gated_delta_f64(S16.astype(np.float64), alpha, q.astype(np.float32),
-                                 k.astype(np.float32), v.astype(np.float32), np.float32(beta))
-    assert np.array_equal(rec.view(np.uint16),
-                          want.astype(np.float32).astype(np.float16).view(np.uint16).ravel())
+    alpha = np.full(d, np.float32(math.exp(-0.1)))
+    one = np.ones(d, np.float32)
+    want, yw = O.step_update(S16, one, one, alpha, q, k, v, beta)
+    assert np.array_equal(rec.view(np.uint16), want.astype(np.float16).view(np.uint16).ravel())
     assert np.array_equal(y[0], yw)
+    T, _ = O.gated_delta_f64(S16.astype(np.float64), alpha.astype(np.float64),
+                             q.astype(np.float32), k.astype(np.float32), v.astype(np.float32),
+                             np.float32(beta))
+    got = rec.view(np.float16).astype(np.float64).reshape(d, d)
+    assert (np.abs(got - T) <= 2.0 ** -11 * np.abs(T) + 1e-6 * np.abs(T).max()).all()
 
 
 # ------------------------------------------------------------------ key-row-aware fit
@@ -715,8 +788,8 @@ def test_kra_zero_rows_columns_and_state():
 
 def test_kra_drivers_and_step_compose():
     """records_quantize / records_step with per-record impacts equal the
-    single-head fit, and the quantized step with impacts is the FP64 step
-    on the reconstruction, rounded to fp32, then the key-row-aware fit."""
+    single-head fit, and the quantized step with impacts is the step update
+    on the codes, then the key-row-aware fit."""
     rng = np.random.default_rng(51)
     d, bits = 16, [4, 6, 8]
     S = np.stack([_rand_state(rng, d, d) for _ in bits])
@@ -739,9 +812,9 @@ def test_kra_drivers_and_step_compose():
     y = O.records_step(True, base, offs, b8, d, d, q, k, v, beta, g, imp)
     for i, b in enumerate(bits):
         Q, r, c = O.record_unpack(b, d, d, before[offs[i]:offs[i] + sizes[i]])
-        alpha = np.exp(g[i].astype(np.float64)).astype(np.float32).astype(np.float64)
-        Sp, yw = O.gated_delta_f64(O.reconstruct_f64(Q, r, c), alpha, q[i], k[i], v[i], beta[i])
-        Q2, r2, c2 = O.quantize_kra(b, Sp.astype(np.float32), imp[i])
+        alpha = np.exp(g[i].astype(np.float64)).astype(np.float32)
+        Sp, yw = O.step_update(Q, r, c, alpha, q[i], k[i], v[i], beta[i])
+        Q2, r2, c2 = O.quantize_kra(b, Sp, imp[i])
         assert np.array_equal(base[offs[i]:offs[i] + sizes[i]], O.record_pack(b, Q2, r2, c2))
         assert np.array_equal(y[i], yw)
 
@@ -788,8 +861,7 @@ def test_rows_record_layout_and_roundtrip():
 
 def test_rows_drivers_and_step_compose():
     """Records with bits 0 take their key-row widths from row_bits; one step
-    is the FP64 step on the reconstruction, rounded to fp32, then the
-    per-row quantizer."""
+    is the step update on the codes, then the per-row quantizer."""
     rng = np.random.default_rng(63)
     d = 16
     widths = [np.sort(rng.choice([4, 6, 8], d)).astype(np.uint8) for _ in range(3)]
@@ -817,9 +889,9 @@ def test_rows_drivers_and_step_compose():
     y = O.records_step(True, base, offs, bits, d, d, q, k, v, beta, g, row_bits=row_bits)
     for i in range(3):
         Q, r, c = O.record_unpack_rows(row_bits[i], d, before[offs[i]:offs[i] + sizes[i]])
-        alpha = np.exp(g[i].astype(np.float64)).astype(np.float32).astype(np.float64)
-        Sp, yw = O.gated_delta_f64(O.reconstruct_f64(Q, r, c), alpha, q[i], k[i], v[i], beta[i])
-        Q2, r2, c2 = O.quantize_rows(row_bits[i], Sp.astype(np.float32))
+        alpha = np.exp(g[i].astype(np.float64)).astype(np.float32)
+        Sp, yw = O.step_update(Q, r, c, alpha, q[i], k[i], v[i], beta[i])
+        Q2, r2, c2 = O.quantize_rows(row_bits[i], Sp)
         assert np.array_equal(base[offs[i]:offs[i] + sizes[i]],
                               O.record_pack_rows(row_bits[i], Q2, r2, c2))
         assert np.array_equal(y[i], yw)
