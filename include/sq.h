@@ -48,9 +48,10 @@
  *   bits = 16 marks an FP16 pivot head (hyper.ai summary, "Method", second
  *   paragraph: the highest-risk state units stay in FP16 as sparse
  *   pivots): its record is the state itself as IEEE binary16, row-major
- *   [d_k][d_v], 2 d_k d_v bytes, no scales; the decode step updates it in
- *   FP64 from the widened values, rounds S' to fp32 and then to binary16
- *   (nearest even; values beyond the binary16 range become infinite).
+ *   [d_k][d_v], 2 d_k d_v bytes, no scales; the decode step updates the
+ *   widened values with the arithmetic of sq_decode_step (unit scales),
+ *   then rounds S' from fp32 to binary16 (nearest even; values beyond the
+ *   binary16 range become infinite).
  *
  * Execution
  *  - Compute entry points only validate their arguments on the host and
@@ -176,6 +177,12 @@ sq_status sq_dequant_state(const sq_pool *pool, const int32_t *slot_idx, int32_t
  * for every (b, h): dequantize, decay by a = exp(g), look up v_old = Sd^T k,
  * u = beta (v - v_old), S' = Sd + k u^T, y = S'^T q (from the unrequantized
  * S'), then requantize S' to the head's bit width and store it in place.
+ * Arithmetic (the pages say only "floating point"): a_i = (float)exp(g_i);
+ * v_old and u in FP64, u_j then rounded once to fp32; the rank-1 write in
+ * fp32 as S'_ij = fma(code_ij, (a_i r_i) c_j, k_i u_j), each product rounded
+ * once; y in fp32 from that S'.  Codes are bit-exact with this arithmetic
+ * except where the FP64 look-up lands within its own rounding error of an
+ * fp32 rounding boundary of u_j.
  *   q, k: [n, H, d_k]   v: [n, H, d_v]   beta: [n, H]
  *   g (log-gate): [n, H] for GDN, [n, H, d_k] for KDA
  *   y: [n, H, d_v] output
