@@ -558,13 +558,21 @@ __global__ __launch_bounds__(Geo<D>::NT) void dequant_state_kernel(PoolView pool
 }
 
 // ---------------------------------------------------------------- decode step
-// LDS: the band-partials region (NB x D doubles in the look-up phase, reused
-// as two NB x D fp32 planes for the column maxima and the read-out), then
-// 4 D floats of per-column vectors ({c_j, u_j} fp32 pairs in the step; FP64
-// column sums in the key-row-aware fit), 1/c'[D] floats and misc.
+// LDS of the decode step (floats from the base):
+//   [0, PART_F)           the tile's codes as bytes (D x D, first half) and the
+//                         column-maximum partials of S' (NB x D fp32, second
+//                         half; before them the look-up's digit-sum exchange)
+//   [DIG_F, +4 D)         digit rows of the look-up and read-out factors (16 x D bytes)
+//   [IC_F, +D)            1/c'_j
+//   [CU_F, +2 D + 32)     {c_j, u_j}, padded to 18 per 16 columns
+//   [MISC_F, +16)         per wave: exponent maxima, k.q partial; the GDN gate
+// The FP16 pivot step and the key-row-aware fit use [0, PART_F) as NB x D
+// FP64 partials and the words after it in their own way.
 template <int D> struct DecodeLds {
     static constexpr int PART_F = 2 * Geo<D>::NB * D; // floats in the partials region
-    static constexpr int TOTAL = PART_F + 4 * D + D + 8; // + column vectors, 1/c'_j, misc
+    static constexpr int DIG_F = PART_F, IC_F = PART_F + 4 * D, CU_F = PART_F + 5 * D,
+                         MISC_F = PART_F + 7 * D + 32;
+    static constexpr int TOTAL = MISC_F + 16;
 };
 
 // Lane t of a band of CG lanes reads lane (band base + m) with ds_swizzle
@@ -759,7 +767,9 @@ struct TileIn {
     float r[4];          // row scales of the lane's rows
     float k[4], q[4];    // k, q at the lane's rows
     float g;             // KDA: log-gate of row band + NB (cg & 3); GDN: the head's
-    float cj, vj, beta;  // column lane j = t < D: c_j, v_j; beta of the (b, h) row
+    float beta;          // beta of the (b, h) row
+    float cj, vj;        // c_j, v_j of the column whose look-up this lane completes
+    float fk, fq, fr;    // k, q and r of the lane's factor row band + NB (cg & 3)
     uint8_t *rec;        // the tile's record
 };
 
@@ -767,6 +777,7 @@ template <int D, int BITS, bool KDA, typename TI, bool MIXED>
 __device__ __forceinline__ void load_tile(TileIn &in, int tile, uint8_t *rec, const StepIO &io,
                                           Rows<D, BITS, MIXED> rows) {
     using G = Geo<D>;
+    constexpr int BPW = G::CG / G::NW;
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     in.rec = rec;
     if constexpr (MIXED) {
@@ -801,10 +812,15 @@ __device__ __forceinline__ void load_tile(TileIn &in, int tile, uint8_t *rec, co
     }
     in.g = KDA ? ld<TI>(g, row_io * D + band + G::NB * (cg & 3)) : ld<TI>(g, row_io);
     in.beta = ld<TI>(reinterpret_cast<const TI *>(io.beta), row_io);
-    if (t < D) {
-        in.cj = rp[D + t];
-        in.vj = ld<TI>(reinterpret_cast<const TI *>(io.v) + row_io * D, t);
-    }
+    // the column this lane completes in the look-up: 16 (w BPW + b) + (lane & 15)
+    // with b = (lane >> 4) & 3 (lanes with b >= BPW load a duplicate)
+    const int jl = 16 * (BPW * (t >> 6) + (((t >> 4) & 3) % BPW)) + (t & 15);
+    in.cj = rp[D + jl];
+    in.vj = ld<TI>(reinterpret_cast<const TI *>(io.v) + row_io * D, jl);
+    const int rowf = band + G::NB * (cg & 3);
+    in.fk = ld<TI>(k, rowf);
+    in.fq = ld<TI>(q, rowf);
+    in.fr = rp[rowf];
 }
 
 template <int BITS> __device__ __forceinline__ Seg<BITS> seg_of(const TileIn &in, int m) {
@@ -814,6 +830,85 @@ template <int BITS> __device__ __forceinline__ Seg<BITS> seg_of(const TileIn &in
     return s;
 }
 
+// Codes in LDS during a step: column j holds its D codes as bytes in key
+// order k = 4 band + m (row band + NB m), four keys per dword.  The dword
+// index within the column is XOR-swizzled with bits 0..2 and 4..6 of j (bits
+// 2..4 of the index), so that every half-wave access touches 32 distinct
+// banks: the byte writes and phase-2 reads of one code position (lanes: 4
+// bands x 8 column groups) and the matrix-core fragment reads (16 columns x
+// 2 key groups x 2 dwords).
+template <int D> __device__ __forceinline__ int code_sw(int j) {
+    return (((((j & 3) ^ (j >> 4)) & 3) << 3) | ((((j >> 2) ^ (j >> 6)) & 1) << 2));
+}
+template <int D> __device__ __forceinline__ int code_word(int j, int kq) {
+    constexpr int NQ = D / 4;
+    return j * NQ + (kq ^ (code_sw<D>(j) & (NQ - 1)));
+}
+// Digit rows: row d holds digit d of every key's factor, packed the same way
+// (index swizzled with bits 0..2 of d).
+template <int D> __device__ __forceinline__ int digit_word(int d, int kq) {
+    constexpr int NQ = D / 4;
+    return d * NQ + (kq ^ ((((d & 3) << 3) | (((d >> 2) & 1) << 2)) & (NQ - 1)));
+}
+
+// Wavefront maximum of non-negative ints and sum of floats: DPP within rows of
+// 16 lanes (quad exchanges, then mirrors within 8 and 16), then the four row
+// results read into scalars and folded in lane order.
+constexpr int kRowMirror = 0x140; // row_mirror: lane i <-> 15 - i within 16
+__device__ __forceinline__ int wave_max_i(int v) {
+    v = max(v, (int)dpp_u<kQuadXor1>((uint32_t)v));
+    v = max(v, (int)dpp_u<kQuadXor2>((uint32_t)v));
+    v = max(v, (int)dpp_u<kHalfMirror>((uint32_t)v));
+    v = max(v, (int)dpp_u<kRowMirror>((uint32_t)v));
+    return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += __uint_as_float(dpp_u<kQuadXor1>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u<kQuadXor2>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u<kHalfMirror>(__float_as_uint(v)));
+    v += __uint_as_float(dpp_u<kRowMirror>(__float_as_uint(v)));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return ((r0 + r1) + r2) + r3;
+}
+
+// Biased binary exponent of an FP64 value (0 for zero and subnormals).
+__device__ __forceinline__ int exp_field(double x) {
+    return (int)((__double_as_longlong(x) >> 52) & 0x7FF);
+}
+
+// Signed base-256 digits d_0..d_7 of an integer-valued X, |X| < 2^62: the
+// bytes of (X + C) xor C with C = 0x8080...80, each read as int8, so that
+// sum_i d_i 256^i = X exactly (each byte is u_i - 128 for the bytes u_i of
+// X + C, and the range of such sums contains every |X| < 2^62).
+__device__ __forceinline__ uint64_t digits8(double X) {
+    const double hi = floor(X * 0x1p-32);
+    const double lo = fma(hi, -0x1p32, X); // exact, in [0, 2^32)
+    uint64_t K = ((uint64_t)(uint32_t)(int32_t)hi << 32) | (uint64_t)(uint32_t)lo;
+    K += 0x8080808080808080ull;
+    return K ^ 0x8080808080808080ull;
+}
+// The same with three digits, |X| < 2^22.
+__device__ __forceinline__ uint32_t digits3(double X) {
+    return ((uint32_t)(int32_t)X + 0x808080u) ^ 0x808080u;
+}
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) volatile uint8_t lds_u8;
+
+// One step of one (request, head) tile.
+// Look-up and read-out: v_old_j = c_j sum_i a_i r_i k_i code_ij and the
+// read-out's old-state term c_j sum_i a_i r_i q_i code_ij are exact integer
+// sums on the matrix cores (int8 x int8 -> int32): the factors k_i r_i (a_i)
+// of a tile are written as fixed-point integers on one exponent (the largest
+// of the tile), split into 8 signed base-256 digits (3 for the q factor), and
+// the digit rows multiply the code bytes.  The digit sums, combined with one
+// FP64 rounding, give the look-up at least as accurately as an FP64 sum; u_j
+// is then rounded once to fp32.  y = S_d^T q + u (k.q) (the update's rank-1
+// term folded), in fp32 to FP64 precision.
 // SPLIT: write S' (fp32) to io.s_out instead of requantizing; the record
 // is only read.  The requantization then runs as its own launch.
 // KRA: requantize with the key-row-aware fit (row-impact scores imp[D]).
@@ -825,113 +920,206 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
                                             Rows<D, BITS, MIXED> rows = {}) {
     static_assert(!(KRA && MIXED), "the key-row-aware fit takes uniform widths");
     using G = Geo<D>;
-    constexpr int PLANE = G::NB * D;
+    using L = DecodeLds<D>;
+    constexpr int NQ = D / 4;              // dwords per code column
+    constexpr int BPW = G::CG / G::NW;     // 16-column blocks per wave
+    constexpr int KS = D / 32;             // key steps of the matrix-core look-up
+    static_assert(G::CG % G::NW == 0 && BPW <= 4, "column blocks per wave");
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
-    double *part64 = reinterpret_cast<double *>(lds);
-    float *plane_max = lds, *plane_y = lds + PLANE;
-    float2 *lds_cu = reinterpret_cast<float2 *>(lds + DecodeLds<D>::PART_F); // {c_j, u_j}
-    float *lds_ic = lds + DecodeLds<D>::PART_F + 4 * D;
-    float *lds_misc = lds_ic + D; // [0]: GDN gate factor
+    const int w = t >> 6, lg = (t >> 4) & 3, ln = t & 15;
+    uint8_t *code_b = reinterpret_cast<uint8_t *>(lds);
+    const uint32_t *code_w = reinterpret_cast<const uint32_t *>(lds);
+    float *plane_max = lds + D * D / 4;
+    double *xch = reinterpret_cast<double *>(plane_max); // digit-sum exchange, before phase 2
+    uint8_t *dig_b = reinterpret_cast<uint8_t *>(lds + L::DIG_F);
+    float *lds_ic = lds + L::IC_F;
+    float2 *lds_cu = reinterpret_cast<float2 *>(lds + L::CU_F); // {c_j, u_j} at 18 (j / 16) + j % 16
+    float *misc = lds + L::MISC_F; // [4 w + 0..2]: exponent maxima, k.q partial; [15]: GDN gate
     TileIn cur;
     load_tile<D, BITS, KDA, TI, MIXED>(cur, tile, rec_in, io, rows);
     uint8_t *rec = cur.rec;
     float *cp = reinterpret_cast<float *>(rec + rows.codes_bytes()) + D;
     const int64_t row_io = tile;
-
-    Seg<BITS> seg[4];
+    // lane-dependent parts of the code addresses of columns 16 cg + n, one
+    // per value of (n & 7): code_word(16 cg + n, band) = cbase[n & 7] + n NQ
+    int cbase[8];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) seg[m] = seg_of<BITS>(cur, m);
+    for (int q = 0; q < 8; ++q) cbase[q] = 16 * cg * NQ + (band ^ (code_sw<D>(16 * cg + q) & (NQ - 1)));
     // ---- retention factors: GDN one per head (one lane, shared through LDS
     //      after the first barrier); KDA one per key row, computed by lane
     //      cg & 3 of each band for row band + NB (cg & 3) and broadcast.
     float am[4];
+    float ga = 0.0f; // KDA: the gate of row band + NB (cg & 3)
     if constexpr (KDA) {
-        const float a = gate_factor(cur.g);
-        am[0] = band_bcast<G::CG, 0>(a);
-        am[1] = band_bcast<G::CG, 1>(a);
-        am[2] = band_bcast<G::CG, 2>(a);
-        am[3] = band_bcast<G::CG, 3>(a);
+        ga = gate_factor(cur.g);
+        am[0] = band_bcast<G::CG, 0>(ga);
+        am[1] = band_bcast<G::CG, 1>(ga);
+        am[2] = band_bcast<G::CG, 2>(ga);
+        am[3] = band_bcast<G::CG, 3>(ga);
     } else {
-        if (t == 0) lds_misc[0] = gate_factor(cur.g);
+        if (t == 0) misc[15] = gate_factor(cur.g);
     }
-    // ---- look-up: band partials of sum_i k_i (a_i) r_i code_ij in FP64
-    //      (GDN: the head's factor a multiplies the folded column sum)
+    // ---- the lane's codes into LDS, one byte each
     {
-        double kar[4];
+        Seg<BITS> seg[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            kar[m] = (double)cur.k[m] * (double)cur.r[m];
-            if constexpr (KDA) kar[m] *= (double)am[m];
+        for (int m = 0; m < 4; ++m) seg[m] = seg_of<BITS>(cur, m);
+        // single-byte LDS writes (volatile: merged into words, the bytes
+        // would have to be assembled with VALU instructions first)
+        lds_u8 *cb = (lds_u8 *)code_b;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                cb[4 * (cbase[n & 7] + n * NQ) + m] = (uint8_t)code_at<BITS>(seg[m], n);
         }
+    }
+    // ---- factors of key k = 4 band + m in FP64: look-up k_i r_i, read-out
+    //      q_i r_i (times a_i for KDA; the GDN gate scales the sums).  D = 128:
+    //      lane cg < 4 takes the k factor of row m = cg, cg >= 4 the q factor of
+    //      row cg - 4; D = 64: both factors of row m = cg.
+    constexpr int NJOB = 8 / G::CG;
+    double fx[NJOB];
+    int ek = 0, eq = 0;
+    const int jm = cg & 3;
 #pragma unroll
-        for (int n2 = 0; n2 < 8; ++n2) {
-            double acc0 = 0.0, acc1 = 0.0;
+    for (int jb = 0; jb < NJOB; ++jb) {
+        const int vec = G::CG == 8 ? (cg >> 2) : jb;
+        double x = (double)(vec ? cur.fq : cur.fk) * (double)cur.fr;
+        if constexpr (KDA) x *= (double)ga; // the gate of the same row
+        fx[jb] = x;
+        if (vec) eq = max(eq, exp_field(x));
+        else ek = max(ek, exp_field(x));
+    }
+    float kq = 0.0f;
+    if (cg == 0) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                acc0 = fma(kar[m], (double)code_at<BITS>(seg[m], 2 * n2), acc0);
-                acc1 = fma(kar[m], (double)code_at<BITS>(seg[m], 2 * n2 + 1), acc1);
-            }
-            *reinterpret_cast<double2 *>(part64 + part_idx<D>(band, cg, 2 * n2)) =
-                make_double2(acc0, acc1);
-        }
+        for (int m = 0; m < 4; ++m) kq = fmaf(cur.k[m], cur.q[m], kq);
+    }
+    ek = wave_max_i(ek);
+    eq = wave_max_i(eq);
+    kq = wave_sum_dpp(kq);
+    if ((t & 63) == 0) {
+        misc[4 * w] = __int_as_float(ek);
+        misc[4 * w + 1] = __int_as_float(eq);
+        misc[4 * w + 2] = kq;
     }
     __syncthreads();
+    int Ek = 0, Eq = 0;
+    kq = 0.0f;
+#pragma unroll
+    for (int v = 0; v < G::NW; ++v) {
+        Ek = max(Ek, __float_as_int(misc[4 * v]));
+        Eq = max(Eq, __float_as_int(misc[4 * v + 1]));
+        kq += misc[4 * v + 2];
+    }
     if constexpr (!KDA) {
-        const float a = lds_misc[0];
+        const float a = misc[15];
         am[0] = am[1] = am[2] = am[3] = a;
     }
-    if (t < D) {
-        double P = 0.0;
-#pragma unroll 8
-        for (int b = 0; b < G::NB; ++b) P += part64[part_idx<D>(b, t >> 4, t & 15)];
-        if constexpr (!KDA) P *= (double)am[0];
-        // u_j in FP64, rounded once to fp32
-        lds_cu[colvec2_idx(t)] =
-            make_float2(cur.cj, (float)((double)cur.beta * ((double)cur.vj - P * (double)cur.cj)));
+    // ---- digit rows: the k factors as integers X_i = rint(x_i 2^(61 - e)) on
+    //      the tile's largest exponent e (|X| < 2^62, 8 digits, rows 0..7); the
+    //      q factors likewise with |X| < 2^22 (3 digits, rows 8..10)
+#pragma unroll
+    for (int jb = 0; jb < NJOB; ++jb) {
+        const int vec = G::CG == 8 ? (cg >> 2) : jb;
+        if (vec == 0) {
+            const uint64_t dg = digits8(rint(ldexp(fx[jb], 1084 - Ek)));
+#pragma unroll
+            for (int d = 0; d < 8; ++d) dig_b[4 * digit_word<D>(d, band) + jm] = (uint8_t)(dg >> (8 * d));
+        } else {
+            const uint32_t dg = digits3(rint(ldexp(fx[jb], 1044 - Eq)));
+#pragma unroll
+            for (int d = 0; d < 3; ++d)
+                dig_b[4 * digit_word<D>(8 + d, band) + jm] = (uint8_t)(dg >> (8 * d));
+        }
     }
-    // keep the packed codes, not their FP64 values, live across the barrier
-    // (unpacking again costs two VALU per code; holding FP64 codes would cost
-    // 128 VGPRs and halve the waves per SIMD)
+    __syncthreads();
+    // ---- matrix cores: digit sums D[d][j] = sum_k digit_d(X_k) code_kj for the
+    //      wave's column blocks, all keys (rows 11..15 of A are zero)
+    v4i acc[BPW];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int b = 0; b < BPW; ++b) acc[b] = v4i{0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < Seg<BITS>::NWORDS; ++i) asm volatile("" : "+v"(seg[m].w[i]));
+    for (int s2 = 0; s2 < KS; ++s2) {
+        const int kq8 = 8 * s2 + 2 * lg;
+        long A = 0;
+        if (ln < 11) A = *reinterpret_cast<const long *>(dig_b + 4 * digit_word<D>(ln, kq8));
+#pragma unroll
+        for (int b = 0; b < BPW; ++b) {
+            const int j = 16 * (w * BPW + b) + ln;
+            const long B = *reinterpret_cast<const long *>(code_b + 4 * code_word<D>(j, kq8));
+            acc[b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, acc[b], 0, 0, 0);
+        }
+    }
+    // lane (lg, ln) holds digits 4 lg .. 4 lg + 3 of column 16 cb + ln: their
+    // weighted sum is exact in FP64 (|sum| < 2^46); lanes lg = 1 (digits 4..7)
+    // and lg = 2 (q digits) hand theirs to lane lg = 0 through LDS
+#pragma unroll
+    for (int b = 0; b < BPW; ++b) {
+        const double part = fma((double)acc[b][3], 0x1p24,
+                                fma((double)acc[b][2], 0x1p16, fma((double)acc[b][1], 0x1p8, (double)acc[b][0])));
+        if (lg < 3) xch[((w * BPW + b) * 3 + lg) * 16 + ln] = part;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // lane (b, ln), b < BPW, completes column 16 (w BPW + b) + ln
+    if (lg < BPW) {
+        const int cbk = w * BPW + lg, j = 16 * cbk + ln;
+        const double *px = xch + cbk * 48 + ln;
+        double P = ldexp(fma(px[16], 0x1p32, px[0]), Ek - 1084); // sum_i k_i r_i (a_i) code_ij
+        double Y = ldexp(px[32], Eq - 1044);                      // sum_i q_i r_i (a_i) code_ij
+        if constexpr (!KDA) {
+            P *= (double)am[0];
+            Y *= (double)am[0];
+        }
+        const double cj = (double)cur.cj;
+        // u_j in FP64, rounded once to fp32
+        const float u = (float)((double)cur.beta * ((double)cur.vj - P * cj));
+        lds_cu[18 * cbk + ln] = make_float2(cur.cj, u);
+        st<TO>(reinterpret_cast<TO *>(io.y) + row_io * D, j, (float)fma((double)u, (double)kq, Y * cj));
+    }
     __syncthreads();
     // ---- decay + delta write in fp32: S'_mn = fma(code, (a_m r_m) c_n, k_m u_n),
-    //      each product rounded once; read-out and column maxima partials
+    //      each product rounded once; column maxima partials
     float x[4][16];
-    float *s_out = SPLIT ? io.s_out + (int64_t)tile * D * D : nullptr;
     {
         float ar[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) ar[m] = am[m] * cur.r[m];
+        // the lane's 16 {c, u} pairs: 8 aligned 16-byte reads (stride 18 pairs
+        // per column group: 4 cg + 2 n mod 32 words, no bank conflicts)
+        const float4 *cu4 = reinterpret_cast<const float4 *>(lds_cu + 18 * cg);
 #pragma unroll
         for (int n4 = 0; n4 < 4; ++n4) {
-            float cm[4], yp[4];
+            float cm[4];
+            const float4 p01 = cu4[2 * n4], p23 = cu4[2 * n4 + 1];
+            const float2 cup[4] = {make_float2(p01.x, p01.y), make_float2(p01.z, p01.w),
+                                   make_float2(p23.x, p23.y), make_float2(p23.z, p23.w)};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int n = 4 * n4 + i;
-                const float2 cu = lds_cu[colvec2_idx(16 * cg + n)];
-                const float cn = cu.x, un = cu.y;
+                const uint32_t cw = code_w[cbase[n & 7] + n * NQ];
+                const float2 cu = cup[i];
                 cm[i] = 0.0f;
-                yp[i] = 0.0f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const float sf = fmaf((float)code_at<BITS>(seg[m], n), ar[m] * cn, cur.k[m] * un);
+                    const float code = (float)(int8_t)(cw >> (8 * m));
+                    const float sf = fmaf(code, ar[m] * cu.x, cur.k[m] * cu.y);
                     x[m][n] = sf;
-                    yp[i] = fmaf(cur.q[m], sf, yp[i]);
                     cm[i] = fmaxf(cm[i], fabsf(sf));
                 }
             }
-            const int pi = plane_idx<D>(band, cg, 4 * n4);
             if constexpr (!SPLIT && !KRA)
-                *reinterpret_cast<float4 *>(plane_max + pi) = make_float4(cm[0], cm[1], cm[2], cm[3]);
-            *reinterpret_cast<float4 *>(plane_y + pi) = make_float4(yp[0], yp[1], yp[2], yp[3]);
+                *reinterpret_cast<float4 *>(plane_max + plane_idx<D>(band, cg, 4 * n4)) =
+                    make_float4(cm[0], cm[1], cm[2], cm[3]);
         }
     }
     if constexpr (SPLIT) {
         // each lane's 64 contiguous bytes of a row back to back (interleaving
         // the rows per 16-byte chunk measured 1.8x slower on MI355X)
+        float *s_out = io.s_out + (int64_t)tile * D * D;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             float4 *dst = reinterpret_cast<float4 *>(s_out + (band + G::NB * m) * D + 16 * cg);
@@ -940,21 +1128,14 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
                 dst[n4] = make_float4(x[m][4 * n4], x[m][4 * n4 + 1], x[m][4 * n4 + 2],
                                       x[m][4 * n4 + 3]);
         }
+        return;
     }
-    __syncthreads();
-    if (t < D) {
-        float yv = 0.0f;
-#pragma unroll 8
-        for (int b = 0; b < G::NB; ++b) yv += plane_y[plane_idx<D>(b, t >> 4, t & 15)];
-        st<TO>(reinterpret_cast<TO *>(io.y) + row_io * D, t, yv);
-        if constexpr (!SPLIT && !KRA)
-            lds_ic[colvec4_idx(t)] = column_scale(column_max<D>(plane_max, t), cp + t);
-    }
-    if constexpr (SPLIT) return;
     __syncthreads();
     if constexpr (KRA) {
         kra_quantize_store<D, BITS>(x, imp, rec, lds);
     } else {
+        if (t < D) lds_ic[colvec4_idx(t)] = column_scale(column_max<D>(plane_max, t), cp + t);
+        __syncthreads();
         float ic[16];
         load_colvec16(lds_ic, cg, ic);
         quantize_rows_store<D, BITS, MIXED>(x, ic, rec, rows);
