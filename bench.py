@@ -345,8 +345,9 @@ def main():
         "config": {"workload": "gdn_decode_%s" % args.workload, "B": B, "H": H, "d_k": d,
                    "d_v": d, "bits": sorted(set(int(b) for b in layer.head_bits)),
                    "pool_slots": wl.n_slots, "io_dtype": wl.dtype, "scales": "fp32",
-                   "arithmetic": "look-up sum in f64 rounded once to f32; update, read-out "
-                                 "and requantizer in f32",
+                   "arithmetic": "look-up and read-out sums exact on int8 matrix cores, "
+                                 "combined in f64, u rounded once to f32; update and "
+                                 "requantizer in f32",
                    "gate": layer.gate},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
