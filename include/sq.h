@@ -178,11 +178,12 @@ sq_status sq_dequant_state(const sq_pool *pool, const int32_t *slot_idx, int32_t
  * u = beta (v - v_old), S' = Sd + k u^T, y = S'^T q (from the unrequantized
  * S'), then requantize S' to the head's bit width and store it in place.
  * Arithmetic (the pages say only "floating point"): a_i = (float)exp(g_i);
- * v_old and u in FP64, u_j then rounded once to fp32; the rank-1 write in
- * fp32 as S'_ij = fma(code_ij, (a_i r_i) c_j, k_i u_j), each product rounded
- * once; y in fp32 from that S'.  Codes are bit-exact with this arithmetic
- * except where the FP64 look-up lands within its own rounding error of an
- * fp32 rounding boundary of u_j.
+ * v_old and u to FP64 accuracy (the kernel forms v_old as an exact integer
+ * sum and rounds it once), u_j then rounded once to fp32; the rank-1 write
+ * in fp32 as S'_ij = fma(code_ij, (a_i r_i) c_j, k_i u_j), each product
+ * rounded once; y = S'^T q to fp32 accuracy.  Codes are bit-exact with this
+ * arithmetic except where an FP64 evaluation of the look-up lands within its
+ * own rounding error of an fp32 rounding boundary of u_j.
  *   q, k: [n, H, d_k]   v: [n, H, d_v]   beta: [n, H]
  *   g (log-gate): [n, H] for GDN, [n, H, d_k] for KDA
  *   y: [n, H, d_v] output

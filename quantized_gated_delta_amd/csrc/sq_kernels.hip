@@ -13,17 +13,17 @@
 //
 // The decode step, per tile (STEPQuant pages: ta-paperlens, mechanism
 // section; hyper.ai summary, Method paragraphs 1 and 4).  The one reduction
-// over the state, the look-up, runs in FP64 (full rate on CDNA4, like
-// non-packed fp32) and is rounded once, so that it does not depend on the
-// order of summation: the quantized recurrence amplifies any +-1 code
-// difference, so the stored codes must be those of the stated arithmetic.
-// Everything after it is element-wise fp32 with one fixed order.
+// over the state, the look-up, is an exact integer sum on the matrix cores
+// (decode_tile) rounded once, so that it does not depend on the order of
+// summation: the quantized recurrence amplifies any +-1 code difference, so
+// the stored codes must be those of the stated arithmetic.  Everything after
+// it is element-wise fp32 with one fixed order.
 //   a_i     = (float) exp(g) or exp(g_i)              (retention gate)
-//   v_old_j = c_j * sum_i (k_i a_i r_i) code_ij       (look-up through k, FP64)
+//   v_old_j = c_j * sum_i (k_i a_i r_i) code_ij       (look-up through k)
 //   u_j     = fl32(beta (v_j - v_old_j))              (delta, FP64, rounded once)
 //   S'_ij   = fma(code_ij, (a_i r_i) c_j, k_i u_j)    (decay + delta write, fp32:
 //                                                      each product rounded once)
-//   y_j     = sum_i q_i S'_ij                         (read-out, fp32)
+//   y_j     = c_j sum_i (q_i a_i r_i) code_ij + u_j (k.q)   (read-out, = S'^T q)
 //   c'_j    = max_i |S'_ij|,  r'_i = max_j |S'_ij| / c'_j / qmax
 //   code'   = round_half_even((S'_ij / c'_j) / r'_i)  (pinned fp32, in place)
 //
