@@ -139,6 +139,26 @@ class Side:
             y_ref = Hn.to_bf16_f32(y_ref)
         return y_gpu, y_ref
 
+    def step_with(self, x, rows):
+        """One step on the full batch with given raw inputs x (the layout of
+        step_inputs), oracle on every row in rows (all rows of the batch)."""
+        wl = self.wl
+        xd = dev_inputs(x)
+        ydt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+        y = torch.empty((wl.B * wl.H, wl.d), dtype=ydt, device=DEV)
+        self.gpu.decode_step(self.slot_dev, xd["q"], xd["k"], xd["v"], xd["beta"], xd["g"], y)
+        rows = np.asarray(rows).reshape(-1, 2)
+        idx = rows[:, 0] * wl.H + rows[:, 1]
+        xs = {k: W.to_f32(v[idx]) for k, v in x.items()}
+        offs, bits = self.rows_offsets(rows)
+        y_ref = O.records_step(self.kda, self.host.bytes, offs, bits, wl.d, wl.d, xs["q"],
+                               xs["k"], xs["v"], xs["beta"], xs["g"], self.rows_imp(rows),
+                               self.rows_row_bits(rows))
+        y_gpu = W.to_f32(from_dev(y)).astype(np.float64)[idx]
+        if wl.dtype == "bf16":
+            y_ref = Hn.to_bf16_f32(y_ref)
+        return y_gpu, y_ref
+
     def gpu_pool(self) -> np.ndarray:
         torch.cuda.synchronize()
         return self.gpu.buf.cpu().numpy()
@@ -346,6 +366,48 @@ def test_decode_zero_state_and_identity():
         for a, bb in zip(Hn.record_scales(int(bits), d, after[o:o + n]),
                          Hn.record_scales(int(bits), d, before[o:o + n])):
             np.testing.assert_allclose(a, bb, rtol=4 * 2.0 ** -23, atol=0)
+
+
+@pytest.mark.parametrize("gate,d", [("gdn", 128), ("kda", 128), ("gdn", 64), ("kda", 64)])
+def test_lookup_edge_cases(gate, d):
+    """Inputs that stress the look-up's fixed-point factors: row scales over
+    60 binary decades (tiny factors truncated against the largest), k = 0 and
+    q = 0 (zero tile exponents), one hot key, and a huge key next to tiny ones."""
+    log("look-up edges %s d=%d" % (gate, d))
+    B, H = 3, 3
+    wl = W.custom(gate, B, H, d, [4, 6, 8], dtype="f32", seed=31)
+    layer = wl.layers[0]
+    side = Side(wl, layer)
+    rows = Hn.rows_all(B, H)
+    rng = np.random.default_rng(77)
+    S = rng.standard_normal((B * H, d, d)).astype(np.float32)
+    S *= np.exp2(-60.0 * np.arange(d) / d)[None, :, None].astype(np.float32)
+    side.init_oracle_rows(rows, S=S)
+    cases = []
+    x = wl.step_inputs(layer, 0)
+    cases.append(("wide row scales", x))
+    x = wl.step_inputs(layer, 1)
+    x["k"][:] = 0
+    cases.append(("k = 0", x))
+    x = wl.step_inputs(layer, 2)
+    x["q"][:] = 0
+    cases.append(("q = 0", x))
+    x = wl.step_inputs(layer, 3)
+    k = np.zeros_like(x["k"]).reshape(B * H, d)
+    k[:, 5] = 1.0
+    x["k"] = k.reshape(x["k"].shape)
+    cases.append(("one hot key", x))
+    x = wl.step_inputs(layer, 4)
+    k = x["k"].reshape(B * H, d).copy()
+    k *= 1e-12
+    k[:, d - 1] = 3.0  # the largest factor sits on the row with the smallest scale
+    x["k"] = k.reshape(x["k"].shape)
+    cases.append(("huge key on a tiny row", x))
+    for label, x in cases:
+        y_gpu, y_ref = side.step_with(x, rows)
+        check_records(side, rows, side.gpu_pool(), label)
+        assert Hn.rel_l2(y_gpu, y_ref) <= Hn.Y_REL_L2, label
+        side.push_rows(rows)  # both sides continue from the oracle's records
 
 
 def test_kda_equal_gates_matches_gdn():
