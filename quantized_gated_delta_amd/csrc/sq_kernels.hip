@@ -1040,15 +1040,20 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     v4i acc[BPW];
 #pragma unroll
     for (int b = 0; b < BPW; ++b) acc[b] = v4i{0, 0, 0, 0};
+    // byte addresses of key step 0; key step s2 moves only address bits 5 and 6
+    // (the index bits 3..4 of 8 s2, which the swizzles XOR but never carry), so
+    // step s2 is step 0 XOR (s2 << 5)
+    const int a_dig = 4 * digit_word<D>(ln, 2 * lg);
+    int a_code[BPW];
+#pragma unroll
+    for (int b = 0; b < BPW; ++b) a_code[b] = 4 * code_word<D>(16 * (w * BPW + b) + ln, 2 * lg);
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
-        const int kq8 = 8 * s2 + 2 * lg;
         long A = 0;
-        if (ln < 11) A = *reinterpret_cast<const long *>(dig_b + 4 * digit_word<D>(ln, kq8));
+        if (ln < 11) A = *reinterpret_cast<const long *>(dig_b + (a_dig ^ (s2 << 5)));
 #pragma unroll
         for (int b = 0; b < BPW; ++b) {
-            const int j = 16 * (w * BPW + b) + ln;
-            const long B = *reinterpret_cast<const long *>(code_b + 4 * code_word<D>(j, kq8));
+            const long B = *reinterpret_cast<const long *>(code_b + (a_code[b] ^ (s2 << 5)));
             acc[b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, acc[b], 0, 0, 0);
         }
     }
