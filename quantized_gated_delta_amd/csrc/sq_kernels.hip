@@ -197,9 +197,18 @@ template <int BITS> __device__ __forceinline__ Seg<8> widen_seg(const Seg<BITS> 
     return o;
 }
 
+// The first W / 2 words of a raw 16-byte segment as a W-wide segment.
+template <int W> __device__ __forceinline__ Seg<W> as_seg(const Seg<8> &raw) {
+    Seg<W> s;
+#pragma unroll
+    for (int i = 0; i < Seg<W>::NWORDS; ++i) s.w[i] = raw.w[i];
+    return s;
+}
+
 // Where a record's key rows are and how wide.  Uniform heads (MIXED = false):
-// every row BITS wide.  Heads with per-key-row widths (MIXED = true, the
-// kernels then carry codes in the 8-bit segment layout, BITS = 8): rows
+// every row BITS wide.  Heads with per-key-row widths (MIXED = true,
+// instantiated with BITS = 8; quant / dequant widen each segment to the
+// 8-bit layout, the decode step reads it at its own width): rows
 // [0, n4) are 4-bit, [n4, n4 + n6) 6-bit, the rest 8-bit, each row's code
 // stream right after the previous one.  The widths change only at multiples
 // of the rows one wavefront holds per m (8 at d = 128, 16 at d = 64), so a
@@ -781,14 +790,13 @@ __device__ __forceinline__ void load_tile(TileIn &in, int tile, uint8_t *rec, co
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     in.rec = rec;
     if constexpr (MIXED) {
-        Seg<8> raw[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) raw[m] = rows.load_raw(rec, band + G::NB * m, cg);
+        // raw segments, each in its row's own width (the step writes each
+        // code as a byte with a branch on the row's width)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const Seg<8> sg = rows.widen(raw[m], band + G::NB * m);
+            const Seg<8> raw = rows.load_raw(rec, band + G::NB * m, cg);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) in.w[m][i] = sg.w[i];
+            for (int i = 0; i < 4; ++i) in.w[m][i] = raw.w[i];
         }
     } else {
 #pragma unroll
@@ -912,7 +920,8 @@ typedef __attribute__((address_space(3))) volatile uint8_t lds_u8;
 // SPLIT: write S' (fp32) to io.s_out instead of requantizing; the record
 // is only read.  The requantization then runs as its own launch.
 // KRA: requantize with the key-row-aware fit (row-impact scores imp[D]).
-// MIXED: per-key-row widths (BITS = 8, the codes' in-kernel layout).
+// MIXED: per-key-row widths (instantiated with BITS = 8; each row's raw
+// segment is read at its own width when its codes go to LDS).
 template <int D, int BITS, bool KDA, bool SPLIT, bool KRA, typename TI, typename TO,
           bool MIXED = false>
 __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const StepIO &io,
@@ -960,7 +969,27 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
         if (t == 0) misc[15] = gate_factor(cur.g);
     }
     // ---- the lane's codes into LDS, one byte each
-    {
+    if constexpr (MIXED) {
+        // per row, one wavefront-uniform branch on its width
+        lds_u8 *cb = (lds_u8 *)code_b;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int wd = __builtin_amdgcn_readfirstlane(rows.width(band + G::NB * m));
+            const Seg<8> raw = seg_of<8>(cur, m);
+            if (wd == 4) {
+                const Seg<4> sg = as_seg<4>(raw);
+#pragma unroll
+                for (int n = 0; n < 16; ++n) cb[4 * (cbase[n & 7] + n * NQ) + m] = (uint8_t)code_at<4>(sg, n);
+            } else if (wd == 6) {
+                const Seg<6> sg = as_seg<6>(raw);
+#pragma unroll
+                for (int n = 0; n < 16; ++n) cb[4 * (cbase[n & 7] + n * NQ) + m] = (uint8_t)code_at<6>(sg, n);
+            } else {
+#pragma unroll
+                for (int n = 0; n < 16; ++n) cb[4 * (cbase[n & 7] + n * NQ) + m] = (uint8_t)code_at<8>(raw, n);
+            }
+        }
+    } else {
         Seg<BITS> seg[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) seg[m] = seg_of<BITS>(cur, m);
