@@ -8,8 +8,10 @@
 // d = 64: 64 lanes = 1 wave).  The CG lanes sharing a band are adjacent in a
 // wave, so a load instruction of one wave covers 64 / CG whole consecutive
 // rows (contiguous bytes), and the per-row maximum is a DPP reduction over
-// adjacent lanes.  Column reductions (over rows) go through LDS: every band
-// writes its 16-column partials, then lane j < d folds column j.
+// adjacent lanes.  Column maxima (over rows) go through LDS: every band
+// writes its 16-column partials, then lane j < d folds column j.  The step's
+// two sums over rows (look-up and read-out) run on the matrix cores instead
+// (decode_tile); the FP16 pivot step folds FP64 band partials like the maxima.
 //
 // The decode step, per tile (STEPQuant pages: ta-paperlens, mechanism
 // section; hyper.ai summary, Method paragraphs 1 and 4).  The one reduction
