@@ -576,7 +576,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void dequant_state_kernel(PoolView pool
 //   [DIG_F, +4 D)         digit rows of the look-up and read-out factors (16 x D bytes)
 //   [IC_F, +D)            1/c'_j
 //   [CU_F, +2 D + 32)     {c_j, u_j}, padded to 18 per 16 columns
-//   [MISC_F, +16)         per wave: exponent maxima, k.q partial; the GDN gate
+//   [MISC_F, +16)         the GDN gate
 // The FP16 pivot step and the key-row-aware fit use [0, PART_F) as NB x D
 // FP64 partials and the words after it in their own way.
 template <int D> struct DecodeLds {
@@ -781,6 +781,7 @@ struct TileIn {
     float beta;          // beta of the (b, h) row
     float cj, vj;        // c_j, v_j of the column whose look-up this lane completes
     float fk, fq, fr;    // k, q and r of the lane's factor row band + NB (cg & 3)
+    float kb[2], qb[2], rb[2], gb[2]; // rows (t & 63) + 64 i, i < D / 64: every wave sees all rows
     uint8_t *rec;        // the tile's record
 };
 
@@ -831,6 +832,14 @@ __device__ __forceinline__ void load_tile(TileIn &in, int tile, uint8_t *rec, co
     in.fk = ld<TI>(k, rowf);
     in.fq = ld<TI>(q, rowf);
     in.fr = rp[rowf];
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+        const int row = (t & 63) + 64 * i;
+        in.kb[i] = ld<TI>(k, row);
+        in.qb[i] = ld<TI>(q, row);
+        in.rb[i] = rp[row];
+        in.gb[i] = KDA ? ld<TI>(g, row_io * D + row) : 0.0f;
+    }
 }
 
 template <int BITS> __device__ __forceinline__ Seg<BITS> seg_of(const TileIn &in, int m) {
@@ -901,9 +910,9 @@ __device__ __forceinline__ uint64_t digits8(double X) {
     K += 0x8080808080808080ull;
     return K ^ 0x8080808080808080ull;
 }
-// The same with three digits, |X| < 2^22.
-__device__ __forceinline__ uint32_t digits3(double X) {
-    return ((uint32_t)(int32_t)X + 0x808080u) ^ 0x808080u;
+// The same with four digits, |X| < 2^30.
+__device__ __forceinline__ uint32_t digits4(double X) {
+    return ((uint32_t)(int32_t)X + 0x80808080u) ^ 0x80808080u;
 }
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -914,7 +923,7 @@ typedef __attribute__((address_space(3))) volatile uint8_t lds_u8;
 // read-out's old-state term c_j sum_i a_i r_i q_i code_ij are exact integer
 // sums on the matrix cores (int8 x int8 -> int32): the factors k_i r_i (a_i)
 // of a tile are written as fixed-point integers on one exponent (the largest
-// of the tile), split into 8 signed base-256 digits (3 for the q factor), and
+// of the tile), split into 8 signed base-256 digits (4 for the q factor), and
 // the digit rows multiply the code bytes.  The digit sums, combined with one
 // FP64 rounding, give the look-up at least as accurately as an FP64 sum; u_j
 // is then rounded once to fp32.  y = S_d^T q + u (k.q) (the update's rank-1
@@ -945,7 +954,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     uint8_t *dig_b = reinterpret_cast<uint8_t *>(lds + L::DIG_F);
     float *lds_ic = lds + L::IC_F;
     float2 *lds_cu = reinterpret_cast<float2 *>(lds + L::CU_F); // {c_j, u_j} at 18 (j / 16) + j % 16
-    float *misc = lds + L::MISC_F; // [4 w + 0..2]: exponent maxima, k.q partial; [15]: GDN gate
+    float *misc = lds + L::MISC_F; // [15]: GDN gate
     TileIn cur;
     load_tile<D, BITS, KDA, TI, MIXED>(cur, tile, rec_in, io, rows);
     uint8_t *rec = cur.rec;
@@ -1011,7 +1020,6 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     //      row cg - 4; D = 64: both factors of row m = cg.
     constexpr int NJOB = 8 / G::CG;
     double fx[NJOB];
-    int ek = 0, eq = 0;
     const int jm = cg & 3;
 #pragma unroll
     for (int jb = 0; jb < NJOB; ++jb) {
@@ -1019,38 +1027,30 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
         double x = (double)(vec ? cur.fq : cur.fk) * (double)cur.fr;
         if constexpr (KDA) x *= (double)ga; // the gate of the same row
         fx[jb] = x;
-        if (vec) eq = max(eq, exp_field(x));
-        else ek = max(ek, exp_field(x));
     }
+    // ---- the tile's exponents, computed by every wave over all D rows (no
+    //      exchange between waves): Ek >= the biased exponent of every k
+    //      factor, Eq of every q factor.  GDN: exactly the largest.  KDA: the
+    //      gate enters through a bound, a_i = exp(g_i) < 2^(ceil(g_i log2 e)
+    //      + 1), which can only make E larger, and a larger E only drops
+    //      bits far below the 53 the look-up needs (|X| < 2^62).  And k.q.
+    int ek = 0, eq = 0;
     float kq = 0.0f;
-    if (cg == 0) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) kq = fmaf(cur.k[m], cur.q[m], kq);
+    for (int i = 0; i < D / 64; ++i) {
+        const double kr = (double)cur.kb[i] * (double)cur.rb[i];
+        const double qr = (double)cur.qb[i] * (double)cur.rb[i];
+        int ea = 0;
+        if constexpr (KDA) ea = (int)ceilf(cur.gb[i] * 1.44269504f) + 2;
+        ek = max(ek, exp_field(kr) + ea);
+        eq = max(eq, exp_field(qr) + ea);
+        kq = fmaf(cur.kb[i], cur.qb[i], kq);
     }
-    ek = wave_max_i(ek);
-    eq = wave_max_i(eq);
+    const int Ek = wave_max_i(ek), Eq = wave_max_i(eq);
     kq = wave_sum_dpp(kq);
-    if ((t & 63) == 0) {
-        misc[4 * w] = __int_as_float(ek);
-        misc[4 * w + 1] = __int_as_float(eq);
-        misc[4 * w + 2] = kq;
-    }
-    __syncthreads();
-    int Ek = 0, Eq = 0;
-    kq = 0.0f;
-#pragma unroll
-    for (int v = 0; v < G::NW; ++v) {
-        Ek = max(Ek, __float_as_int(misc[4 * v]));
-        Eq = max(Eq, __float_as_int(misc[4 * v + 1]));
-        kq += misc[4 * v + 2];
-    }
-    if constexpr (!KDA) {
-        const float a = misc[15];
-        am[0] = am[1] = am[2] = am[3] = a;
-    }
     // ---- digit rows: the k factors as integers X_i = rint(x_i 2^(61 - e)) on
-    //      the tile's largest exponent e (|X| < 2^62, 8 digits, rows 0..7); the
-    //      q factors likewise with |X| < 2^22 (3 digits, rows 8..10)
+    //      the tile's exponent e (|X| < 2^62, 8 digits, rows 0..7); the q
+    //      factors likewise with |X| < 2^30 (4 digits, rows 8..11)
 #pragma unroll
     for (int jb = 0; jb < NJOB; ++jb) {
         const int vec = G::CG == 8 ? (cg >> 2) : jb;
@@ -1059,15 +1059,19 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
 #pragma unroll
             for (int d = 0; d < 8; ++d) dig_b[4 * digit_word<D>(d, band) + jm] = (uint8_t)(dg >> (8 * d));
         } else {
-            const uint32_t dg = digits3(rint(ldexp(fx[jb], 1044 - Eq)));
+            const uint32_t dg = digits4(rint(ldexp(fx[jb], 1052 - Eq)));
 #pragma unroll
-            for (int d = 0; d < 3; ++d)
+            for (int d = 0; d < 4; ++d)
                 dig_b[4 * digit_word<D>(8 + d, band) + jm] = (uint8_t)(dg >> (8 * d));
         }
     }
     __syncthreads();
+    if constexpr (!KDA) {
+        const float a = misc[15];
+        am[0] = am[1] = am[2] = am[3] = a;
+    }
     // ---- matrix cores: digit sums D[d][j] = sum_k digit_d(X_k) code_kj for the
-    //      wave's column blocks, all keys (rows 11..15 of A are zero)
+    //      wave's column blocks, all keys (rows 12..15 of A are zero)
     v4i acc[BPW];
 #pragma unroll
     for (int b = 0; b < BPW; ++b) acc[b] = v4i{0, 0, 0, 0};
@@ -1081,7 +1085,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
         long A = 0;
-        if (ln < 11) A = *reinterpret_cast<const long *>(dig_b + (a_dig ^ (s2 << 5)));
+        if (ln < 12) A = *reinterpret_cast<const long *>(dig_b + (a_dig ^ (s2 << 5)));
 #pragma unroll
         for (int b = 0; b < BPW; ++b) {
             const long B = *reinterpret_cast<const long *>(code_b + (a_code[b] ^ (s2 << 5)));
@@ -1105,7 +1109,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
         const int cbk = w * BPW + lg, j = 16 * cbk + ln;
         const double *px = xch + cbk * 48 + ln;
         double P = ldexp(fma(px[16], 0x1p32, px[0]), Ek - 1084); // sum_i k_i r_i (a_i) code_ij
-        double Y = ldexp(px[32], Eq - 1044);                      // sum_i q_i r_i (a_i) code_ij
+        double Y = ldexp(px[32], Eq - 1052);                      // sum_i q_i r_i (a_i) code_ij
         if constexpr (!KDA) {
             P *= (double)am[0];
             Y *= (double)am[0];

@@ -429,7 +429,13 @@ def test_kda_equal_gates_matches_gdn():
         y = torch.empty((B * H, d), dtype=torch.bfloat16, device=DEV)
         side.gpu.decode_step(side.slot_dev, xd["q"], xd["k"], xd["v"], xd["beta"], xd["g"], y)
         outs.append((side.gpu_pool(), from_dev(y)))
-    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    # the records must be identical; y is formed from differently scaled
+    # fixed-point factors (GDN applies the gate to the sum, KDA to each row),
+    # so it agrees to ~2^-27 before the bf16 rounding, not bit for bit
+    assert np.array_equal(outs[0][0], outs[1][0])
+    yg, yk = W.to_f32(outs[0][1]).astype(np.float64), W.to_f32(outs[1][1]).astype(np.float64)
+    assert np.all(np.abs(yg - yk) <= 2.0 ** -8 * np.abs(yg))  # at most one bf16 rounding step
+    assert Hn.rel_l2(yk, yg) <= 1e-4
 
 
 # ----------------------------------------------------------------- workloads
