@@ -922,12 +922,13 @@ typedef __attribute__((address_space(3))) volatile uint8_t lds_u8;
 // Look-up and read-out: v_old_j = c_j sum_i a_i r_i k_i code_ij and the
 // read-out's old-state term c_j sum_i a_i r_i q_i code_ij are exact integer
 // sums on the matrix cores (int8 x int8 -> int32): the factors k_i r_i (a_i)
-// of a tile are written as fixed-point integers on one exponent (the largest
-// of the tile), split into 8 signed base-256 digits (4 for the q factor), and
-// the digit rows multiply the code bytes.  The digit sums, combined with one
-// FP64 rounding, give the look-up at least as accurately as an FP64 sum; u_j
-// is then rounded once to fp32.  y = S_d^T q + u (k.q) (the update's rank-1
-// term folded), in fp32 to FP64 precision.
+// of a tile are written as fixed-point integers on one exponent (an upper
+// bound of the tile's largest), split into 8 signed base-256 digits (4 for
+// the q factor), and the digit rows multiply the code bytes.  The digit sums,
+// combined with one FP64 rounding, give the look-up at least as accurately as
+// an FP64 sum; u_j is then rounded once to fp32.  y = S_d^T q + u (k.q) (the
+// update's rank-1 term folded), to about 2^-27 relative before its output
+// rounding.
 // SPLIT: write S' (fp32) to io.s_out instead of requantizing; the record
 // is only read.  The requantization then runs as its own launch.
 // KRA: requantize with the key-row-aware fit (row-impact scores imp[D]).
