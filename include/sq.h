@@ -223,6 +223,19 @@ sq_status sq_f32_decode_step(float *state_pool, int32_t n_slots, int32_t n_heads
 sq_status sq_check_slots(const sq_pool *pool, const int32_t *slot_idx, int32_t n,
                          hipStream_t stream);
 
+/* Self-check of the hardware arithmetic the quantizer relies on.  The
+ * quantizer's divisions (the dual-axis scale rule above) are computed by
+ * short sequences that are correctly rounded only because of how this GPU's
+ * reciprocal instruction rounds; this call re-checks them on every input
+ * they can receive: 1/x for every float x in [FLT_MIN, 2^126) (counts[0])
+ * and m / qmax for every float m in [0, 2] and qmax = 7, 31, 127
+ * (counts[1..3]), each against the IEEE division.  counts: 4 uint64 in
+ * device memory (8-byte aligned), cleared and then filled on `stream` with
+ * the number of differing results (all zero on a conforming GPU); read them
+ * after synchronising the stream.  About 5 * 10^9 evaluations, tens of
+ * milliseconds.  counts NULL gives SQ_EINVAL. */
+sq_status sq_arith_selfcheck(uint64_t *counts, hipStream_t stream);
+
 /* Text describing the last non-OK status returned on this thread. */
 const char *sq_last_error(void);
 

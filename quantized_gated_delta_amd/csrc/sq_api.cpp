@@ -344,4 +344,12 @@ sq_status sq_check_slots(const sq_pool *pool, const int32_t *slot_idx, int32_t n
     return SQ_OK;
 }
 
+sq_status sq_arith_selfcheck(uint64_t *counts, hipStream_t stream) {
+    if (!counts) return fail(SQ_EINVAL, "counts is NULL");
+    if (!aligned(counts, 8)) return fail(SQ_EINVAL, "counts is not 8-byte aligned");
+    const hipError_t e =
+        sqk::launch_arith_selfcheck(reinterpret_cast<unsigned long long *>(counts), stream);
+    return e == hipSuccess ? SQ_OK : hip_fail(e, "arith_selfcheck launch");
+}
+
 } // extern "C"

@@ -64,4 +64,8 @@ hipError_t launch_decode_update(const PoolView &pool, const HeadTable &tab, cons
 hipError_t launch_f32_decode(float *state, int64_t slot_stride_floats, int32_t n_heads, int32_t d,
                              const StepIO &io, hipStream_t stream);
 
+// Exhaustive check of the quantizer's division sequences: counts[0..4)
+// (device) receive the mismatches against the IEEE division.
+hipError_t launch_arith_selfcheck(unsigned long long *counts, hipStream_t stream);
+
 } // namespace sqk

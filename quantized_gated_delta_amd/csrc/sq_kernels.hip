@@ -231,6 +231,11 @@ template <int D, int BITS, bool MIXED> struct Rows {
     __device__ __forceinline__ float qmax(int row) const {
         return (float)((1 << (width(row) - 1)) - 1);
     }
+    // 1 / qmax rounded to nearest
+    __device__ __forceinline__ float inv_qmax(int row) const {
+        const int w = width(row);
+        return w == 4 ? 1.0f / 7.0f : (w == 6 ? 1.0f / 31.0f : 1.0f / 127.0f);
+    }
     // MIXED: the widest segment (16 bytes, 4-byte aligned) is read whatever
     // the row's width, so the four rows' loads issue back to back before any
     // width branch.  A narrower row's extra bytes lie in the next row or in
@@ -286,6 +291,24 @@ template <int D, int BITS, bool MIXED> struct Rows {
 //   s_ij = S_ij ic_j (rounded); m_i = max_j |s_ij|; r_i = m_i / qmax;
 //   ir_i = r_i >= FLT_MIN ? 1/r_i : 0;  code = clamp(rint(s_ij * ir_i)),
 //   the last product exact (not rounded before rint)
+// The three divisions are correctly rounded, by short sequences in their
+// input ranges (every value of each range checked against the IEEE division
+// on MI355X by sq_arith_selfcheck):
+//   1/x, x in [FLT_MIN, 2^126): the hardware reciprocal y, refined once,
+//     fma(fma(-x, y, 1), y, y)  (outside the range: the IEEE division);
+//   m / qmax, m in [0, 2], qmax in {7, 31, 127}: q = m z with z = 1/qmax
+//     rounded, then fma(fma(-q, qmax, m), z, q), the correction step of a
+//     faithful quotient with a correctly rounded reciprocal (Markstein).
+//     |s| <= 1 + 2^-23 for every scaled entry, so m stays in range.
+__device__ __forceinline__ float recip_rn(float x) {
+    const float y = __builtin_amdgcn_rcpf(x);
+    return __builtin_fmaf(__builtin_fmaf(-x, y, 1.0f), y, y);
+}
+__device__ __forceinline__ float div_qmax(float m, float qmax, float z) {
+#pragma clang fp contract(off)
+    const float q = m * z;
+    return __builtin_fmaf(__builtin_fmaf(-q, qmax, m), z, q);
+}
 // LDS layouts.  A band's 16-column group is written by one lane as 16-byte
 // chunks; eight consecutive lanes write the same chunk index at the same
 // time, and the 32 x 4-byte LDS banks repeat every 128 bytes.  The chunk
@@ -344,7 +367,12 @@ __device__ __forceinline__ float column_scale(float cmax, float *cp_j) {
 #pragma clang fp contract(off)
     const bool ok = cmax >= FLT_MIN;
     *cp_j = ok ? cmax : 0.0f;
-    return ok ? 1.0f / cmax : 0.0f;
+    float ic = recip_rn(cmax);
+    // maxima of 2^126 and above (reciprocal subnormal): the IEEE division,
+    // on a wavefront-uniform branch
+    if (__builtin_amdgcn_ballot_w64(cmax >= 0x1p126f) != 0)
+        if (cmax >= 0x1p126f) ic = 1.0f / cmax;
+    return ok ? ic : 0.0f;
 }
 
 template <int D>
@@ -386,10 +414,11 @@ __device__ __forceinline__ void quantize_rows_store(float (&x)[4][16], const flo
     const float sel01 = (cg & 1) ? rm[1] : rm[0];
     const float sel23 = (cg & 1) ? rm[3] : rm[2];
     const float mrow = (cg & 2) ? sel23 : sel01;
-    float r = mrow / rows.qmax(band + G::NB * (cg & 3));
+    const int row_own = band + G::NB * (cg & 3);
+    float r = div_qmax(mrow, rows.qmax(row_own), rows.inv_qmax(row_own));
     float ir;
     if (r >= FLT_MIN) {
-        ir = 1.0f / r;
+        ir = recip_rn(r); // r <= (1 + 2^-23) / 7
     } else {
         r = 0.0f;
         ir = 0.0f;
@@ -910,10 +939,6 @@ __device__ __forceinline__ uint64_t digits8(double X) {
     K += 0x8080808080808080ull;
     return K ^ 0x8080808080808080ull;
 }
-// The same with four digits, |X| < 2^30.
-__device__ __forceinline__ uint32_t digits4(double X) {
-    return ((uint32_t)(int32_t)X + 0x80808080u) ^ 0x80808080u;
-}
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) volatile uint8_t lds_u8;
@@ -949,7 +974,6 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     const int w = t >> 6, lg = (t >> 4) & 3, ln = t & 15;
     uint8_t *code_b = reinterpret_cast<uint8_t *>(lds);
-    const uint32_t *code_w = reinterpret_cast<const uint32_t *>(lds);
     float *plane_max = lds + D * D / 4;
     double *xch = reinterpret_cast<double *>(plane_max); // digit-sum exchange, before phase 2
     uint8_t *dig_b = reinterpret_cast<uint8_t *>(lds + L::DIG_F);
@@ -961,11 +985,15 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     uint8_t *rec = cur.rec;
     float *cp = reinterpret_cast<float *>(rec + rows.codes_bytes()) + D;
     const int64_t row_io = tile;
-    // lane-dependent parts of the code addresses of columns 16 cg + n, one
-    // per value of (n & 7): code_word(16 cg + n, band) = cbase[n & 7] + n NQ
+    // byte addresses of the lane's codes of columns 16 cg + n, one per value
+    // of (n & 7): 4 code_word(16 cg + n, band) = cbase[n & 7] + 4 n NQ.  For
+    // n < 8 the swizzle splits, code_sw(16 cg + n) = code_sw(16 cg) ^
+    // code_sw(n), and it only touches the bits below NQ, so the lane part is
+    // formed once and each n & 7 is one XOR with a constant.
+    const int cb0 = 4 * (16 * cg * NQ + (band ^ (code_sw<D>(16 * cg) & (NQ - 1))));
     int cbase[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) cbase[q] = 16 * cg * NQ + (band ^ (code_sw<D>(16 * cg + q) & (NQ - 1)));
+    for (int q = 0; q < 8; ++q) cbase[q] = cb0 ^ (4 * (code_sw<D>(q) & (NQ - 1)));
     // ---- retention factors: GDN one per head (one lane, shared through LDS
     //      after the first barrier); KDA one per key row, computed by lane
     //      cg & 3 of each band for row band + NB (cg & 3) and broadcast.
@@ -991,14 +1019,14 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
             if (wd == 4) {
                 const Seg<4> sg = as_seg<4>(raw);
 #pragma unroll
-                for (int n = 0; n < 16; ++n) cb[4 * (cbase[n & 7] + n * NQ) + m] = (uint8_t)code_at<4>(sg, n);
+                for (int n = 0; n < 16; ++n) cb[cbase[n & 7] + 4 * n * NQ + m] = (uint8_t)code_at<4>(sg, n);
             } else if (wd == 6) {
                 const Seg<6> sg = as_seg<6>(raw);
 #pragma unroll
-                for (int n = 0; n < 16; ++n) cb[4 * (cbase[n & 7] + n * NQ) + m] = (uint8_t)code_at<6>(sg, n);
+                for (int n = 0; n < 16; ++n) cb[cbase[n & 7] + 4 * n * NQ + m] = (uint8_t)code_at<6>(sg, n);
             } else {
 #pragma unroll
-                for (int n = 0; n < 16; ++n) cb[4 * (cbase[n & 7] + n * NQ) + m] = (uint8_t)code_at<8>(raw, n);
+                for (int n = 0; n < 16; ++n) cb[cbase[n & 7] + 4 * n * NQ + m] = (uint8_t)code_at<8>(raw, n);
             }
         }
     } else {
@@ -1012,7 +1040,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
         for (int n = 0; n < 16; ++n) {
 #pragma unroll
             for (int m = 0; m < 4; ++m)
-                cb[4 * (cbase[n & 7] + n * NQ) + m] = (uint8_t)code_at<BITS>(seg[m], n);
+                cb[cbase[n & 7] + 4 * n * NQ + m] = (uint8_t)code_at<BITS>(seg[m], n);
         }
     }
     // ---- factors of key k = 4 band + m in FP64: look-up k_i r_i, read-out
@@ -1051,20 +1079,17 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     kq = wave_sum_dpp(kq);
     // ---- digit rows: the k factors as integers X_i = rint(x_i 2^(61 - e)) on
     //      the tile's exponent e (|X| < 2^62, 8 digits, rows 0..7); the q
-    //      factors likewise with |X| < 2^30 (4 digits, rows 8..11)
+    //      factors likewise with |X| < 2^30 (4 digits, rows 8..11).  One code
+    //      path for both: a q factor's digits 4..7 are zero and land in rows
+    //      12..15, which the matrix cores never read.
 #pragma unroll
     for (int jb = 0; jb < NJOB; ++jb) {
         const int vec = G::CG == 8 ? (cg >> 2) : jb;
-        if (vec == 0) {
-            const uint64_t dg = digits8(rint(ldexp(fx[jb], 1084 - Ek)));
+        const uint64_t dg = digits8(rint(ldexp(fx[jb], vec ? 1052 - Eq : 1084 - Ek)));
+        const int r0 = vec ? 8 : 0;
 #pragma unroll
-            for (int d = 0; d < 8; ++d) dig_b[4 * digit_word<D>(d, band) + jm] = (uint8_t)(dg >> (8 * d));
-        } else {
-            const uint32_t dg = digits4(rint(ldexp(fx[jb], 1052 - Eq)));
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-                dig_b[4 * digit_word<D>(8 + d, band) + jm] = (uint8_t)(dg >> (8 * d));
-        }
+        for (int d = 0; d < 8; ++d)
+            dig_b[4 * digit_word<D>(r0 + d, band) + jm] = (uint8_t)(dg >> (8 * d));
     }
     __syncthreads();
     if constexpr (!KDA) {
@@ -1079,10 +1104,17 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     // byte addresses of key step 0; key step s2 moves only address bits 5 and 6
     // (the index bits 3..4 of 8 s2, which the swizzles XOR but never carry), so
     // step s2 is step 0 XOR (s2 << 5)
-    const int a_dig = 4 * digit_word<D>(ln, 2 * lg);
+    // (the digit rows are swizzled like code columns 0..15, and the code
+    // swizzle splits as above: column 16 c + ln is column ln XOR the
+    // wave-uniform part of c)
+    const int a_dig = 4 * digit_word<D>(ln, 2 * lg); // = 4 code_word(ln, 2 lg)
+    const int wu = __builtin_amdgcn_readfirstlane(w);
     int a_code[BPW];
 #pragma unroll
-    for (int b = 0; b < BPW; ++b) a_code[b] = 4 * code_word<D>(16 * (w * BPW + b) + ln, 2 * lg);
+    for (int b = 0; b < BPW; ++b) {
+        const int c = wu * BPW + b;
+        a_code[b] = (a_dig ^ (4 * (code_sw<D>(16 * c) & (NQ - 1)))) + 64 * c * NQ;
+    }
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
         long A = 0;
@@ -1141,7 +1173,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int n = 4 * n4 + i;
-                const uint32_t cw = code_w[cbase[n & 7] + n * NQ];
+                const uint32_t cw = *reinterpret_cast<const uint32_t *>(code_b + cbase[n & 7] + 4 * n * NQ);
                 const float2 cu = cup[i];
                 cm[i] = 0.0f;
 #pragma unroll
@@ -1526,6 +1558,42 @@ hipError_t launch_decode_update(const PoolView &pool, const HeadTable &tab, cons
                                 hipStream_t stream) {
     return pool.row_mixed ? decode_gate_dispatch<true, false, true>(pool, tab, io, stream)
                           : decode_gate_dispatch<true, false, false>(pool, tab, io, stream);
+}
+
+// ---------------------------------------------------------------- arithmetic self-check
+// Every input of the quantizer's short division sequences (recip_rn on
+// [FLT_MIN, 2^126), div_qmax on [0, 2] for qmax = 7, 31, 127) against the
+// IEEE division; counts[k] += the number of results that differ.
+__global__ void clear_counts_kernel(unsigned long long *counts) {
+    if (threadIdx.x < 4) counts[threadIdx.x] = 0;
+}
+__global__ __launch_bounds__(256) void arith_selfcheck_kernel(unsigned long long *counts) {
+#pragma clang fp contract(off)
+    unsigned long long bad[4] = {0, 0, 0, 0};
+    const uint32_t stride = gridDim.x * blockDim.x;
+    const uint32_t first = blockIdx.x * blockDim.x + threadIdx.x;
+    // i < 0x7e000000 and stride < 2^21: i + stride never wraps
+    for (uint32_t i = first; i < 0x7e000000u; i += stride) {
+        const float x = __uint_as_float(0x00800000u + i);
+        bad[0] += __float_as_uint(recip_rn(x)) != __float_as_uint(1.0f / x);
+    }
+    for (uint32_t i = first; i <= 0x40000000u; i += stride) {
+        const float m = __uint_as_float(i);
+        bad[1] += __float_as_uint(div_qmax(m, 7.0f, 1.0f / 7.0f)) != __float_as_uint(m / 7.0f);
+        bad[2] += __float_as_uint(div_qmax(m, 31.0f, 1.0f / 31.0f)) != __float_as_uint(m / 31.0f);
+        bad[3] += __float_as_uint(div_qmax(m, 127.0f, 1.0f / 127.0f)) != __float_as_uint(m / 127.0f);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (bad[k]) atomicAdd(&counts[k], bad[k]);
+}
+
+hipError_t launch_arith_selfcheck(unsigned long long *counts, hipStream_t stream) {
+    clear_counts_kernel<<<1, 64, 0, stream>>>(counts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    arith_selfcheck_kernel<<<2048, 256, 0, stream>>>(counts);
+    return hipGetLastError();
 }
 
 hipError_t launch_f32_decode(float *state, int64_t slot_stride_floats, int32_t n_heads, int32_t d,

@@ -81,6 +81,8 @@ def lib():
                                          vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp]
         L.sq_check_slots.restype = st
         L.sq_check_slots.argtypes = [vp, vp, i32, vp]
+        L.sq_arith_selfcheck.restype = st
+        L.sq_arith_selfcheck.argtypes = [vp, vp]
         L.sq_last_error.restype = ctypes.c_char_p
         L.sq_last_error.argtypes = []
         L.sq_version.restype = ctypes.c_char_p
@@ -254,6 +256,11 @@ def sq_f32_decode_step(state, n_slots, n_heads, d_k, d_v, gate, slot_idx, n, q, 
 def sq_check_slots(handle, slot_idx, n: int, stream=None) -> None:
     _check(lib().sq_check_slots(handle, _ptr(slot_idx), int(n), _stream(stream)),
            "sq_check_slots")
+
+
+def sq_arith_selfcheck(counts, stream=None) -> None:
+    """counts: a device tensor of 4 int64 that receives the mismatch counts."""
+    _check(lib().sq_arith_selfcheck(_ptr(counts), _stream(stream)), "sq_arith_selfcheck")
 
 
 class StatePool:

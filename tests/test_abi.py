@@ -129,6 +129,11 @@ def test_step_validation_without_launch(pool):
             text="pool is NULL")
 
 
+def test_arith_selfcheck_validation_without_launch():
+    _expect(Q.SQ_EINVAL, Q.sq_arith_selfcheck, None, 0, text="counts is NULL")
+    _expect(Q.SQ_EINVAL, Q.sq_arith_selfcheck, FAKE_DEV + 4, 0, text="counts is not 8-byte")
+
+
 def test_split_update_validation_without_launch(pool):
     P = FAKE_DEV + 4096
     io = (P, P, P, P, P, P)

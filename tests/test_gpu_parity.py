@@ -220,6 +220,18 @@ def calibrated_impact(wl, layer, steps=16):
                         np.concatenate(gs))
 
 
+# ----------------------------------------------------------------- G0
+def test_arith_selfcheck():
+    """The quantizer's short division sequences (hardware reciprocal refined
+    once; division by qmax through its rounded reciprocal with one
+    correction) equal the IEEE division on every input they can receive."""
+    log("G0 arithmetic self-check")
+    counts = torch.full((4,), -1, dtype=torch.int64, device=DEV)
+    Q.sq_arith_selfcheck(counts)
+    torch.cuda.synchronize()
+    assert counts.cpu().tolist() == [0, 0, 0, 0]
+
+
 # ----------------------------------------------------------------- G1
 @pytest.mark.parametrize("d", [64, 128])
 def test_quant_dequant_bit_exact(d):
