@@ -190,9 +190,17 @@ sq_status sq_pool_create_rows(const sq_pool_desc *desc, const uint8_t *row_bits,
     p->desc = *desc;
     std::memcpy(p->bits, desc->head_bits, (size_t)desc->n_heads);
     p->desc.head_bits = p->bits;
-    const int64_t stride = layout(desc, row_bits, p->tab.off, p->rec_bytes, p->tab.n4, p->tab.n6);
-    std::memcpy(p->tab.bits, p->bits, (size_t)desc->n_heads);
-    for (int h = 0; h < desc->n_heads; ++h) p->row_mixed |= desc->head_bits[h] == 0;
+    uint8_t n4[sqk::kMaxHeads] = {}, n6[sqk::kMaxHeads] = {};
+    const int64_t stride = layout(desc, row_bits, p->tab.off, p->rec_bytes, n4, n6);
+    for (int h = 0; h < desc->n_heads; ++h) {
+        p->tab.info[h] = sqk::head_info(desc->head_bits[h], n4[h], n6[h]);
+        p->row_mixed |= desc->head_bits[h] == 0;
+    }
+    int s = 0;
+    while ((1 << s) < desc->n_heads) ++s;
+    p->view.h_shift = 31 + s;
+    p->view.h_magic = (uint32_t)((((uint64_t)1 << (31 + s)) + (uint64_t)desc->n_heads - 1) /
+                                 (uint64_t)desc->n_heads);
     p->view.row_mixed = p->row_mixed;
     p->view.base = static_cast<uint8_t *>(dev_buf);
     p->view.slot_stride = stride;

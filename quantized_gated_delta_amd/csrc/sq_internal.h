@@ -9,18 +9,27 @@ namespace sqk {
 
 constexpr int kMaxHeads = 64;
 
-// Per-head record placement inside one slot of the pool.
+// Per-head record placement inside one slot of the pool.  One 32-bit word of
+// widths per head, so that a kernel reads it with a scalar load:
+//   bits = info & 0xff: 4, 6, 8, 16 (FP16 pivot), or 0 (per-key-row widths);
+//   n4 = (info >> 8) & 0xff, n6 = (info >> 16) & 0xff: for bits 0, rows
+//   [0, n4) are 4-bit, [n4, n4 + n6) 6-bit, the rest 8-bit.
 struct HeadTable {
-    int64_t off[kMaxHeads];  // byte offset of head h's record within a slot
-    uint8_t bits[kMaxHeads]; // 4, 6, 8, 16 (FP16 pivot), or 0 (per-key-row widths)
-    uint8_t n4[kMaxHeads];   // bits 0: rows [0, n4) are 4-bit,
-    uint8_t n6[kMaxHeads];   //   [n4, n4 + n6) 6-bit, the rest 8-bit
+    int64_t off[kMaxHeads];   // byte offset of head h's record within a slot
+    uint32_t info[kMaxHeads]; // widths, as above
 };
+inline uint32_t head_info(int bits, int n4, int n6) {
+    return (uint32_t)bits | ((uint32_t)n4 << 8) | ((uint32_t)n6 << 16);
+}
 
 struct PoolView {
     uint8_t *base;       // device pointer to slot 0
     int64_t slot_stride; // bytes per slot
     int32_t n_heads;
+    // request of tile t (t < 2^31): (t * h_magic) >> h_shift = t / n_heads,
+    // with h_shift = 31 + ceil(log2 n_heads), h_magic = ceil(2^h_shift / n_heads)
+    uint32_t h_magic;
+    int32_t h_shift;
     int32_t d;           // d_k == d_v
     const float *impact; // row-impact scores [n_heads, d] (key-row-aware fit) or null
     int32_t row_mixed;   // some head has per-key-row widths (head bits 0)

@@ -53,6 +53,15 @@ template <int D> struct Geo {
 };
 
 // ---------------------------------------------------------------- helpers
+// Request and head of tile t = b H + h, without a division (scalar ALU).
+__device__ __forceinline__ void tile_bh(const PoolView &pool, uint32_t t, int &b, int &h) {
+    const uint32_t q = (uint32_t)(((uint64_t)t * pool.h_magic) >> pool.h_shift);
+    b = (int)q;
+    h = (int)(t - q * (uint32_t)pool.n_heads);
+}
+__device__ __forceinline__ int info_bits(uint32_t info) { return (int)(info & 0xffu); }
+__device__ __forceinline__ int info_n4(uint32_t info) { return (int)((info >> 8) & 0xffu); }
+__device__ __forceinline__ int info_n6(uint32_t info) { return (int)((info >> 16) & 0xffu); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
@@ -531,12 +540,13 @@ __global__ __launch_bounds__(Geo<D>::NT) void quant_state_kernel(PoolView pool, 
                                                                  const int32_t *slot,
                                                                  const float *S) {
     __shared__ __attribute__((aligned(16))) float lds[Geo<D>::NB * D + D];
-    const int H = pool.n_heads;
-    const int b = blockIdx.x / H, h = blockIdx.x - b * H;
+    int b, h;
+    tile_bh(pool, blockIdx.x, b, h);
+    const uint32_t info = tab.info[h];
     uint8_t *rec = pool.base + (int64_t)slot[b] * pool.slot_stride + tab.off[h];
     const float *src = S + (int64_t)blockIdx.x * D * D;
-    switch (tab.bits[h]) {
-    case 0: quant_tile<D, 8, true>(rec, src, lds, {tab.n4[h], tab.n6[h]}); break;
+    switch (info_bits(info)) {
+    case 0: quant_tile<D, 8, true>(rec, src, lds, {info_n4(info), info_n6(info)}); break;
     case 4: quant_tile<D, 4>(rec, src, lds); break;
     case 6: quant_tile<D, 6>(rec, src, lds); break;
     case 16: quant_tile_f16<D>(rec, src); break;
@@ -584,12 +594,13 @@ __device__ __forceinline__ void dequant_tile(const uint8_t *rec, float *S,
 template <int D>
 __global__ __launch_bounds__(Geo<D>::NT) void dequant_state_kernel(PoolView pool, HeadTable tab,
                                                                    const int32_t *slot, float *S) {
-    const int H = pool.n_heads;
-    const int b = blockIdx.x / H, h = blockIdx.x - b * H;
+    int b, h;
+    tile_bh(pool, blockIdx.x, b, h);
+    const uint32_t info = tab.info[h];
     const uint8_t *rec = pool.base + (int64_t)slot[b] * pool.slot_stride + tab.off[h];
     float *dst = S + (int64_t)blockIdx.x * D * D;
-    switch (tab.bits[h]) {
-    case 0: dequant_tile<D, 8, true>(rec, dst, {tab.n4[h], tab.n6[h]}); break;
+    switch (info_bits(info)) {
+    case 0: dequant_tile<D, 8, true>(rec, dst, {info_n4(info), info_n6(info)}); break;
     case 4: dequant_tile<D, 4>(rec, dst); break;
     case 6: dequant_tile<D, 6>(rec, dst); break;
     case 16: dequant_tile_f16<D>(rec, dst); break;
@@ -785,12 +796,12 @@ void quant_state_kra_kernel(PoolView pool, HeadTable tab,
                                                                      const int32_t *slot,
                                                                      const float *S) {
     __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D>::TOTAL];
-    const int H = pool.n_heads;
-    const int b = blockIdx.x / H, h = blockIdx.x - b * H;
+    int b, h;
+    tile_bh(pool, blockIdx.x, b, h);
     uint8_t *rec = pool.base + (int64_t)slot[b] * pool.slot_stride + tab.off[h];
     const float *src = S + (int64_t)blockIdx.x * D * D;
     const float *imp = pool.impact + (int64_t)h * D;
-    switch (tab.bits[h]) {
+    switch (info_bits(tab.info[h])) {
     case 4: quant_tile_kra<D, 4>(rec, src, imp, lds); break;
     case 6: quant_tile_kra<D, 6>(rec, src, imp, lds); break;
     case 16: quant_tile_f16<D>(rec, src); break;
@@ -1354,15 +1365,30 @@ __global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(kDec
 void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
     __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D>::TOTAL];
     const int tile = blockIdx.x;
-    const int H = pool.n_heads;
-    const int b = tile / H, h = tile - b * H;
-    uint8_t *rec = pool.base + (int64_t)io.slot[b] * pool.slot_stride + tab.off[h];
+    // Two rounds of scalar loads before the record's address is known: the
+    // pool and step arguments, then slot, offset and widths together (the
+    // empty asm statements keep the compiler from spreading them over more
+    // rounds).
+    const int32_t *slot_idx = io.slot;
+    uint8_t *base = pool.base;
+    const int64_t stride = pool.slot_stride;
+    asm volatile("" ::"s"(slot_idx), "s"(base), "s"(stride), "s"(pool.h_magic), "s"(pool.h_shift),
+                 "s"(pool.n_heads));
+    int b, h;
+    tile_bh(pool, tile, b, h);
+    // slot_idx is read-only for the kernel: a scalar (constant-space) load
+    const int32_t slot =
+        *(const __attribute__((address_space(4))) int32_t *)(uintptr_t)(slot_idx + b);
+    const int64_t head_off = tab.off[h];
+    const uint32_t info = tab.info[h];
+    asm volatile("" ::"s"(slot), "s"(head_off), "s"(info));
+    uint8_t *rec = base + (int64_t)slot * stride + head_off;
     const float *imp = KRA ? pool.impact + (int64_t)h * D : nullptr;
-    switch (tab.bits[h]) {
+    switch (info_bits(info)) {
     case 0:
         if constexpr (ROWS)
             decode_tile<D, 8, KDA, SPLIT, false, TI, TO, true>(rec, tile, io, nullptr, lds,
-                                                               {tab.n4[h], tab.n6[h]});
+                                                               {info_n4(info), info_n6(info)});
         break;
     case 4: decode_tile<D, 4, KDA, SPLIT, KRA, TI, TO>(rec, tile, io, imp, lds); break;
     case 6: decode_tile<D, 6, KDA, SPLIT, KRA, TI, TO>(rec, tile, io, imp, lds); break;
