@@ -633,6 +633,23 @@ template <int CG, int M> __device__ __forceinline__ float band_bcast(float v) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), AND_MASK | (M << 5)));
 }
 
+// v plus the value of the lane holding the other band of the lane's band pair
+// (lanes t and t ^ CG within a wave): DPP row rotation by 8 for CG = 8,
+// ds_swizzle with xor mask 4 for CG = 4.  Both lanes get the same sum.
+template <int CG> __device__ __forceinline__ double pair_sum(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+    if constexpr (CG == 8) {
+        lo = __builtin_amdgcn_mov_dpp(lo, 0x128, 0xF, 0xF, false); // row_ror:8
+        hi = __builtin_amdgcn_mov_dpp(hi, 0x128, 0xF, 0xF, false);
+    } else {
+        static_assert(CG == 4, "band pairs of 4 or 8 lanes");
+        lo = __builtin_amdgcn_ds_swizzle(lo, 0x1F | (4 << 10));
+        hi = __builtin_amdgcn_ds_swizzle(hi, 0x1F | (4 << 10));
+    }
+    return v + __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
 // ---------------------------------------------------------------- key-row-aware fit
 // Requantization with the key-row-aware dual-axis fit (hyper.ai summary,
 // "Method", the Key-Row-Aware Dual-Axis Fitting paragraph): per key row a
@@ -645,9 +662,9 @@ template <int CG, int M> __device__ __forceinline__ float band_bcast(float v) {
 //   c_j = B_j > 0 ? (float)(A_j / B_j) : c0_j   (the impact-weighted least-
 //          squares scale for the codes P)
 //   Q_ij = nearest level of s_ij / c_j, clamped to [-qmax, qmax]
-// The FP64 sums run over the 32 bands in two passes through the 32 KB
-// partials region (A, then B), which keeps the LDS footprint of the closed
-// rule.  c_j >= c0_j / 2 (a weighted average of s / P over |P| >= 1), so
+// The FP64 sums run in one pass: each lane sums its 4 rows, lane pairs add
+// their two bands, and the A and B pair sums share the 32 KB partials
+// region (the LDS footprint of the closed rule).  c_j >= c0_j / 2 (a weighted average of s / P over |P| >= 1), so
 // |s / c_j| <= 2 qmax and the magic-number rounding stays exact.
 template <int D, int BITS>
 __device__ __forceinline__ void kra_quantize_store(float (&x)[4][16], const float *imp,
@@ -661,7 +678,6 @@ __device__ __forceinline__ void kra_quantize_store(float (&x)[4][16], const floa
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     double *part64 = reinterpret_cast<double *>(lds);
     float *plane = lds; // column maxima; used (and reduced) before part64
-    double *colA = reinterpret_cast<double *>(lds + DecodeLds<D>::PART_F);
     float *lds_c0 = lds + DecodeLds<D>::PART_F + 2 * D;
     float *lds_ic = lds + DecodeLds<D>::PART_F + 4 * D;
     float *rp = reinterpret_cast<float *>(rec + D * RB);
@@ -723,49 +739,51 @@ __device__ __forceinline__ void kra_quantize_store(float (&x)[4][16], const floa
     __syncthreads();
     float ic[16];
     load_colvec16(lds_ic, cg, ic);
-    // ---- the two FP64 column sums, one pass each through part64
+    // ---- the two FP64 column sums in one pass: each lane sums its 4 rows,
+    //      the two bands of a lane pair (lanes t and t ^ CG of one wave) are
+    //      added by a lane exchange, and the pair sums go through LDS (A in
+    //      the first half of part64, B in the second, NB / 2 rows each)
+    double *partA = part64, *partB = part64 + (G::NB / 2) * D;
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        // the codes P are formed again in the second pass rather than kept
-        // live across the barrier (64 more VGPRs would spill)
-        if (pass == 1)
+    for (int n2 = 0; n2 < 8; ++n2) {
+        double a[2] = {0.0, 0.0}, q[2] = {0.0, 0.0};
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+        for (int e = 0; e < 2; ++e) {
+            const int n = 2 * n2 + e;
 #pragma unroll
-                for (int n = 0; n < 16; ++n) asm volatile("" : "+v"(x[m][n]));
-#pragma unroll
-        for (int n2 = 0; n2 < 8; ++n2) {
-            double acc[2] = {0.0, 0.0};
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int n = 2 * n2 + e;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const float P = __builtin_fmaf(x[m][n], ic[n], MAGIC) - MAGIC; // exact
-                    const double wp = w[m] * (double)P;
-                    acc[e] = fma(wp, pass == 0 ? (double)x[m][n] : (double)P, acc[e]);
-                }
-            }
-            *reinterpret_cast<double2 *>(part64 + part_idx<D>(band, cg, 2 * n2)) =
-                make_double2(acc[0], acc[1]);
-        }
-        __syncthreads();
-        if (t < D) {
-            double sum = 0.0;
-#pragma unroll 8
-            for (int b = 0; b < G::NB; ++b) sum += part64[part_idx<D>(b, t >> 4, t & 15)];
-            if (pass == 0) {
-                colA[t] = sum;
-            } else {
-                const double A = colA[t];
-                float c = sum > 0.0 ? (float)(A / sum) : lds_c0[t];
-                if (!(c >= FLT_MIN)) c = 0.0f;
-                cp[t] = c;
-                lds_ic[colvec4_idx(t)] = c > 0.0f ? 1.0f / c : 0.0f;
+            for (int m = 0; m < 4; ++m) {
+                const float P = __builtin_fmaf(x[m][n], ic[n], MAGIC) - MAGIC; // exact
+                const double wp = w[m] * (double)P;
+                a[e] = fma(wp, (double)x[m][n], a[e]);
+                q[e] = fma(wp, (double)P, q[e]);
             }
         }
-        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            a[e] = pair_sum<G::CG>(a[e]);
+            q[e] = pair_sum<G::CG>(q[e]);
+        }
+        if ((band & 1) == 0) {
+            const int i = part_idx<D>(band >> 1, cg, 2 * n2);
+            *reinterpret_cast<double2 *>(partA + i) = make_double2(a[0], a[1]);
+            *reinterpret_cast<double2 *>(partB + i) = make_double2(q[0], q[1]);
+        }
     }
+    __syncthreads();
+    if (t < D) {
+        double A = 0.0, Bq = 0.0;
+#pragma unroll 8
+        for (int b = 0; b < G::NB / 2; ++b) {
+            const int i = part_idx<D>(b, t >> 4, t & 15);
+            A += partA[i];
+            Bq += partB[i];
+        }
+        float c = Bq > 0.0 ? (float)(A / Bq) : lds_c0[t];
+        if (!(c >= FLT_MIN)) c = 0.0f;
+        cp[t] = c;
+        lds_ic[colvec4_idx(t)] = c > 0.0f ? 1.0f / c : 0.0f;
+    }
+    __syncthreads();
     load_colvec16(lds_ic, cg, ic);
     constexpr uint32_t MB = 0x4B400000u; // bit pattern of MAGIC
 #pragma unroll
