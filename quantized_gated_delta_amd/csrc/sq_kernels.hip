@@ -119,18 +119,18 @@ template <int BITS> struct Seg {
     uint32_t w[NWORDS];
 };
 
+// Code segments are read once per step: non-temporal loads, word by word
+// (a segment is only 4-byte aligned; the words merge into one load).
+// Measured about 1 % faster on the 6-bit step than plain loads;
+// non-temporal stores of the same segments were slower.
+template <int NW> __device__ __forceinline__ void load_words_nt(const uint8_t *p, uint32_t *w) {
+    const uint32_t *p32 = reinterpret_cast<const uint32_t *>(p);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] = __builtin_nontemporal_load(p32 + i);
+}
 template <int BITS> __device__ __forceinline__ Seg<BITS> load_seg(const uint8_t *p) {
     Seg<BITS> s;
-    if constexpr (BITS == 8) {
-        const uint4 x = *reinterpret_cast<const uint4 *>(p);
-        s.w[0] = x.x; s.w[1] = x.y; s.w[2] = x.z; s.w[3] = x.w;
-    } else if constexpr (BITS == 4) {
-        const uint2 x = *reinterpret_cast<const uint2 *>(p);
-        s.w[0] = x.x; s.w[1] = x.y;
-    } else {
-        const uint32_t *p32 = reinterpret_cast<const uint32_t *>(p);
-        s.w[0] = p32[0]; s.w[1] = p32[1]; s.w[2] = p32[2];
-    }
+    load_words_nt<Seg<BITS>::NWORDS>(p, s.w);
     return s;
 }
 
@@ -250,9 +250,8 @@ template <int D, int BITS, bool MIXED> struct Rows {
     // width branch.  A narrower row's extra bytes lie in the next row or in
     // r[] of the same record (which the same workgroup only writes later).
     __device__ __forceinline__ Seg<8> load_raw(const uint8_t *rec, int row, int cg) const {
-        const uint32_t *p = reinterpret_cast<const uint32_t *>(rec + offset(row) + cg * (2 * width(row)));
         Seg<8> s;
-        s.w[0] = p[0]; s.w[1] = p[1]; s.w[2] = p[2]; s.w[3] = p[3];
+        load_words_nt<4>(rec + offset(row) + cg * (2 * width(row)), s.w);
         return s;
     }
     __device__ __forceinline__ Seg<8> widen(const Seg<8> &raw, int row) const {
