@@ -841,12 +841,15 @@ def test_rows_kda_trajectory_256_steps():
 
 # ----------------------------------------------------------------- limits
 @pytest.mark.parametrize("gate", ["gdn", "kda"])
-def test_max_heads_and_ragged_batch(gate):
-    """The largest head count (64) with every width kind in one pool, a batch
-    of 37 requests spread over 100 slots (ragged against everything): two
-    steps on sampled rows against the oracle, spare slots untouched."""
-    H, d, B, n_slots = 64, 128, 37, 100
-    log("max heads %s" % gate)
+@pytest.mark.parametrize("H", [64, 61])
+def test_max_heads_and_ragged_batch(gate, H):
+    """The largest head count (64), and a prime one (61: the tile-to-(request,
+    head) multiplier is not a power of two), with every width kind in one
+    pool, a batch of 37 requests spread over 100 slots (ragged against
+    everything): two steps on sampled rows against the oracle, spare slots
+    untouched."""
+    d, B, n_slots = 128, 37, 100
+    log("max heads %s H=%d" % (gate, H))
     rng = np.random.default_rng(64)
     bits = rng.choice([4, 6, 8, 16, 0], H)
     rows_w = _row_widths(H, d, 64)
