@@ -16,9 +16,14 @@
  *    state is then quantized for storage (symmetric uniform quantization).
  *  - hyper.ai summary, "Method", Key-Row-Aware Dual-Axis Fitting paragraph:
  *    the state is stored as row factors x column factors x low-bit integers,
- *    each scaled entry rounded to the nearest level.  Scale rule used here:
- *    c_j = max_i |S'_ij|, r_i = max_j |S'_ij / c_j| / qmax, codes
- *    round-half-even(S'_ij / (c_j r_i)), qmax = 2^(bits-1) - 1.
+ *    each scaled entry rounded to the nearest level.  Scale rule used here,
+ *    in fp32 with one correctly rounded operation per step:
+ *        c_j  = max_i |S'_ij|,             ic_j = 1 / c_j   (0 if c_j < FLT_MIN)
+ *        s_ij = S'_ij * ic_j,              r_i  = max_j |s_ij| / qmax
+ *        ir_i = 1 / r_i (0 if r_i < FLT_MIN)
+ *        code = round-half-even of the exact product s_ij * ir_i, that is
+ *               the level nearest to s_ij / r_i,   qmax = 2^(bits-1) - 1.
+ *    Scales below FLT_MIN are stored as 0 and their codes are 0.
  *  - hyper.ai summary, "Method", last paragraph: packed-state kernels sit in
  *    a per-request recurrent-state pool; a fused kernel reconstructs tiles,
  *    applies the delta update and reads out the output.  Here the
@@ -105,13 +110,20 @@ typedef struct {
 typedef struct sq_pool sq_pool;
 
 /* Bytes of device memory a pool with this descriptor needs
- * (n_slots * slot_stride).  Defines the layout above. */
+ * (n_slots * slot_stride).  Defines the layout above: a per-request
+ * recurrent-state pool (hyper.ai summary, "Method", last paragraph) with
+ * spare slots reached through a slot index (blog.ontle.kr, efficiency
+ * paragraph).  Errors: SQ_EINVAL for a NULL or inconsistent descriptor,
+ * SQ_EUNSUPPORTED for shapes or widths outside the supported set. */
 sq_status sq_pool_bytes(const sq_pool_desc *desc, size_t *bytes);
 
 /* Wrap the caller's device buffer dev_buf (>= sq_pool_bytes, 256-byte
- * aligned) as a pool.  Host-side only: the buffer's contents are not
+ * aligned) as a pool (the per-request state pool of hyper.ai summary,
+ * "Method", last paragraph).  Host-side only: the buffer's contents are not
  * touched (initialise slots with sq_quant_state).  *out receives a handle
- * to release with sq_pool_destroy. */
+ * to release with sq_pool_destroy.  Errors: as sq_pool_bytes, plus
+ * SQ_EINVAL for a NULL or misaligned buffer and SQ_ENOMEM if bytes is too
+ * small or the host handle cannot be allocated. */
 sq_status sq_pool_create(const sq_pool_desc *desc, void *dev_buf, size_t bytes, sq_pool **out);
 
 /* Per-key-row bit widths (blog.ontle.kr, allocation paragraph: for KDA
@@ -136,7 +148,9 @@ sq_status sq_pool_bytes_rows(const sq_pool_desc *desc, const uint8_t *row_bits, 
 sq_status sq_pool_create_rows(const sq_pool_desc *desc, const uint8_t *row_bits, void *dev_buf,
                               size_t bytes, sq_pool **out);
 
-/* Release the host handle.  Never frees or touches dev_buf.  NULL is a no-op. */
+/* Release the host handle of a pool (hyper.ai summary, "Method", last
+ * paragraph: the pool is the serving system's; this library only describes
+ * its layout).  Never frees or touches dev_buf.  NULL is a no-op. */
 sq_status sq_pool_destroy(sq_pool *pool);
 
 /* Layout of a pool: slot stride in bytes, and per head its record's byte
@@ -162,28 +176,45 @@ sq_status sq_pool_layout(const sq_pool *pool, int64_t *slot_stride, int64_t *hea
 sq_status sq_pool_set_row_impact(sq_pool *pool, const float *impact);
 
 /* Quantize fp32 states S [n, H, d_k, d_v] (device) into the slots
- * slot_idx[0..n) (device int32) with each head's bit width, using the scale
- * rule above in fp32 (reciprocal-multiply; one rounding per operation).
- * Bit-exact with the documented arithmetic. */
+ * slot_idx[0..n) (device int32) with each head's bit width (hyper.ai
+ * summary, "Method", Key-Row-Aware Dual-Axis Fitting paragraph: row factors
+ * x column factors x low-bit integers, nearest level).  Arithmetic: the
+ * scale rule written out at the top of this file (or the key-row-aware fit
+ * of sq_pool_set_row_impact); FP16 pivot heads store the nearest binary16.
+ * Bit-exact with that arithmetic.  Errors: SQ_EINVAL for NULL or misaligned
+ * pointers or n < 0; nothing is enqueued then. */
 sq_status sq_quant_state(sq_pool *pool, const int32_t *slot_idx, int32_t n, const float *S,
                          hipStream_t stream);
 
-/* Reconstruct fp32 states S [n, H, d_k, d_v] = (code * r_i) * c_j (two
- * rounded fp32 products) from the slots slot_idx[0..n). */
+/* Reconstruct fp32 states S [n, H, d_k, d_v] from the slots slot_idx[0..n)
+ * (hyper.ai summary, "Method", Key-Row-Aware Dual-Axis Fitting paragraph:
+ * the state is the product of the row factor, the column factor and the
+ * integer).  Arithmetic: S_ij = (float)(((double)code_ij * r_i) * c_j), one
+ * FP64 product chain rounded once to fp32 (the FP64 value is exact for
+ * |code| <= 31 and rounded once, by at most 2^-53 relative, for 8-bit
+ * codes).  FP16 pivot heads widen their binary16 values exactly.  Errors:
+ * SQ_EINVAL for NULL or misaligned pointers or n < 0. */
 sq_status sq_dequant_state(const sq_pool *pool, const int32_t *slot_idx, int32_t n, float *S,
                            hipStream_t stream);
 
-/* One fused decode step for n requests (request b lives in slot slot_idx[b]):
- * for every (b, h): dequantize, decay by a = exp(g), look up v_old = Sd^T k,
- * u = beta (v - v_old), S' = Sd + k u^T, y = S'^T q (from the unrequantized
- * S'), then requantize S' to the head's bit width and store it in place.
- * Arithmetic (the pages say only "floating point"): a_i = (float)exp(g_i);
- * v_old and u to FP64 accuracy (the kernel forms v_old as an exact integer
- * sum and rounds it once), u_j then rounded once to fp32; the rank-1 write
- * in fp32 as S'_ij = fma(code_ij, (a_i r_i) c_j, k_i u_j), each product
- * rounded once; y = S'^T q to fp32 accuracy.  Codes are bit-exact with this
- * arithmetic except where an FP64 evaluation of the look-up lands within its
- * own rounding error of an fp32 rounding boundary of u_j.
+/* One fused decode step for n requests (request b lives in slot slot_idx[b];
+ * "Paper Explained: STEPQuant" (ta-paperlens), section "The mechanism:
+ * rewriting state with the delta rule"; hyper.ai summary, "Method", first and
+ * last paragraphs): for every (b, h): dequantize, decay by a = exp(g), look up
+ * v_old = Sd^T k, u = beta (v - v_old), S' = Sd + k u^T, y = S'^T q (from the
+ * unrequantized S'), then requantize S' to the head's bit width and store it
+ * in place.  Arithmetic (the pages say only "floating point"):
+ * a_i = (float)exp(g_i); v_old and u to FP64 accuracy (the kernel forms v_old
+ * as an exact integer sum and rounds it once), u_j then rounded once to fp32;
+ * the rank-1 write in fp32 as S'_ij = fma(code_ij, (a_i r_i) c_j, k_i u_j),
+ * each product rounded once; then the scale rule at the top of this file.
+ * y is formed from the update before S' is rounded to fp32,
+ * y_j = c_j sum_i q_i a_i r_i code_ij + u_j (k . q), to about 2^-27 relative
+ * before its rounding to y_dtype.  Codes are bit-exact with this arithmetic
+ * except where an FP64 evaluation of the look-up lands within its own
+ * rounding error of an fp32 rounding boundary of u_j; against the
+ * order-independent definition (FP64 step, S' rounded once to fp32, then the
+ * scale rule) they agree within 1 LSB on all but a few in 10^5 entries.
  *   q, k: [n, H, d_k]   v: [n, H, d_v]   beta: [n, H]
  *   g (log-gate): [n, H] for GDN, [n, H, d_k] for KDA
  *   y: [n, H, d_v] output
@@ -208,9 +239,13 @@ sq_status sq_decode_update(const sq_pool *pool, const int32_t *slot_idx, int32_t
                            sq_dtype in_dtype, void *y, sq_dtype y_dtype, float *S_out,
                            hipStream_t stream);
 
-/* The same step on an fp32 state pool state_pool [n_slots, H, d_k, d_v]
- * (the unquantized serving default), in place on the listed slots.
- * Same argument conventions as sq_decode_step. */
+/* The same step on an fp32 state pool state_pool [n_slots, H, d_k, d_v], in
+ * place on the listed slots: the unquantized serving default the pages
+ * compare against (bayesiansapien page, TL;DR: the state is kept per
+ * request in FP32).  Arithmetic: fp32 throughout (a = expf(g); the two sums
+ * over the state by fp32 partial sums folded through LDS; S'_ij =
+ * fma(k_i, u_j, a_i S_ij) with a_i S_ij rounded first).  Same argument conventions and errors as sq_decode_step;
+ * state_pool NULL or misaligned gives SQ_EINVAL. */
 sq_status sq_f32_decode_step(float *state_pool, int32_t n_slots, int32_t n_heads, int32_t d_k,
                              int32_t d_v, sq_gate gate, const int32_t *slot_idx, int32_t n,
                              const void *q, const void *k, const void *v, const void *beta,
@@ -236,7 +271,8 @@ sq_status sq_check_slots(const sq_pool *pool, const int32_t *slot_idx, int32_t n
  * milliseconds.  counts NULL gives SQ_EINVAL. */
 sq_status sq_arith_selfcheck(uint64_t *counts, hipStream_t stream);
 
-/* Text describing the last non-OK status returned on this thread. */
+/* Text describing the last non-OK status returned on this thread (error
+ * reporting of this library; the pages define no interface).  Never NULL. */
 const char *sq_last_error(void);
 
 /* Library version string. */

@@ -2,8 +2,13 @@
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the CPU
 baseline leg of the benchmark, never by the product path.  It shares no code
-with the HIP library; the arithmetic lives in ``sq_oracle.c`` (plain C, FP64
-recurrence between a pinned fp32 dequantizer and quantizer).
+with the HIP library; the arithmetic lives in ``sq_oracle.c`` (plain C).
+Two step definitions live there: the textbook one (``gated_delta_f64``,
+``f64_step``: the whole step in FP64 on the exact reconstruction, for S'
+rounded once to fp32 and then the pinned fp32 quantizer), and the trajectory
+contract (``step_update``, ``records_step``: the look-up in FP64 with u
+rounded once to fp32, the rank-1 write element-wise in fp32, then the same
+quantizer), which fixes every rounding the stored codes depend on.
 
 Pins: every function here is checked, in the CPU tests, against closed
 forms, identities, brute force on tiny inputs or an unquantized FP64
@@ -23,22 +28,34 @@ _LIB_PATH = os.path.join(_HERE, "libsq_oracle.so")
 _lib = None
 
 
-def build_lib() -> str:
-    """Compile the oracle (always recompiles).  No fast-math, no contraction."""
-    tmp = _LIB_PATH + ".tmp"
+_SAN_PATH = os.path.join(_HERE, "libsq_oracle_san.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def build_lib(sanitize: bool = False) -> str:
+    """Compile the oracle (always recompiles).  No fast-math, no contraction.
+    sanitize: AddressSanitizer + UndefinedBehaviorSanitizer build, written to
+    libsq_oracle_san.so and loaded instead when SQ_SANITIZE=1 (the process
+    must then have the ASan runtime preloaded)."""
+    out = _SAN_PATH if sanitize else _LIB_PATH
+    tmp = out + ".tmp"
     subprocess.check_call(
         ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-         "-fno-fast-math", "-pthread", _SRC, "-o", tmp, "-lm"])
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+         "-fno-fast-math", "-pthread"] + (SANITIZE_FLAGS if sanitize else []) +
+        [_SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, out)
+    return out
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build_lib()
-        L = ctypes.CDLL(_LIB_PATH)
+        san = os.environ.get("SQ_SANITIZE") == "1"
+        path = _SAN_PATH if san else _LIB_PATH
+        if not os.path.exists(path):
+            build_lib(sanitize=san)
+        L = ctypes.CDLL(path)
         i32, i64, vp, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
         L.sqo_qmax.restype = i32
         L.sqo_qmax.argtypes = [i32]
@@ -303,7 +320,8 @@ def record_unpack(bits, dk, dv, rec) -> tuple:
     Q = np.empty((dk, dv), np.int32)
     r = np.empty(dk, np.float32)
     c = np.empty(dv, np.float32)
-    lib().sqo_record_unpack(bits, dk, dv, _p(rec), _p(Q), _p(r), _p(c))
+    if lib().sqo_record_unpack(bits, dk, dv, _p(rec), _p(Q), _p(r), _p(c)) != 0:
+        raise ValueError("bad record shape")
     return Q, r, c
 
 

@@ -515,17 +515,24 @@ int sqo_record_pack_rows(const uint8_t *row_bits, int dk, int dv, const int32_t 
     return 0;
 }
 
+/* Uniform-width records.  Returns -1 for dk or dv outside [1, 2^20]. */
 int sqo_record_unpack(int bits, int dk, int dv, const uint8_t *rec, int32_t *Q, float *r, float *c) {
-    uint8_t rb[1024];
+    if (dk < 1 || dk > (1 << 20) || dv < 1 || dv > (1 << 20)) return -1;
+    uint8_t *rb = (uint8_t *)malloc((size_t)dk);
     memset(rb, bits, (size_t)dk);
-    return sqo_record_unpack_rows(rb, dk, dv, rec, Q, r, c);
+    const int st = sqo_record_unpack_rows(rb, dk, dv, rec, Q, r, c);
+    free(rb);
+    return st;
 }
 
 int sqo_record_pack(int bits, int dk, int dv, const int32_t *Q, const float *r, const float *c,
                     uint8_t *rec) {
-    uint8_t rb[1024];
+    if (dk < 1 || dk > (1 << 20) || dv < 1 || dv > (1 << 20)) return -1;
+    uint8_t *rb = (uint8_t *)malloc((size_t)dk);
     memset(rb, bits, (size_t)dk);
-    return sqo_record_pack_rows(rb, dk, dv, Q, r, c, rec);
+    const int st = sqo_record_pack_rows(rb, dk, dv, Q, r, c, rec);
+    free(rb);
+    return st;
 }
 
 /* FP16 pivot record: one step.  The step update on the exactly widened
@@ -535,16 +542,20 @@ static void f16_record_step(int kda, int dk, int dv, uint8_t *rec, const float *
                             double *y) {
     const size_t n = (size_t)dk * dv;
     uint16_t *h = (uint16_t *)rec;
+    const int nd = dk > dv ? dk : dv;
     float *Z = (float *)malloc(sizeof(float) * n);
     float *S = (float *)malloc(sizeof(float) * n);
-    float alpha[1024], one[1024];
+    float *alpha = (float *)malloc(sizeof(float) * (size_t)dk);
+    float *one = (float *)malloc(sizeof(float) * (size_t)nd);
     for (size_t e = 0; e < n; ++e) Z[e] = sqo_f16_to_f32(h[e]);
-    for (int i = 0; i < 1024; ++i) one[i] = 1.0f;
+    for (int i = 0; i < nd; ++i) one[i] = 1.0f;
     gate_alpha_f32(kda, dk, g, alpha);
     sqo_step_update(dk, dv, Z, one, one, alpha, q, k, v, beta, S, y);
     for (size_t e = 0; e < n; ++e) h[e] = sqo_f32_to_f16(S[e]);
     free(Z);
     free(S);
+    free(alpha);
+    free(one);
 }
 
 /* ------------------------------------------------------------------ */
@@ -577,8 +588,11 @@ static void run_row(const job_t *J, int row) {
     const size_t n = (size_t)dk * dv;
     const float *g = J->g ? J->g + (J->kda ? (size_t)row * dk : (size_t)row) : NULL;
     const float *imp = J->imp ? J->imp + (size_t)row * dk : NULL;
-    /* the record's row widths: per key row (bits 0) or all equal */
-    uint8_t rbw[1024];
+    /* the record's row widths: per key row (bits 0) or all equal; scratch
+     * vectors sized from dk and dv */
+    uint8_t *rbw = (uint8_t *)malloc((size_t)dk);
+    float *rr = (float *)malloc(sizeof(float) * (size_t)dk);
+    float *cc = (float *)malloc(sizeof(float) * (size_t)dv);
     if (J->bits && J->bits[row] == 0)
         memcpy(rbw, J->row_bits + (size_t)row * dk, (size_t)dk);
     else if (J->bits)
@@ -592,7 +606,6 @@ static void run_row(const job_t *J, int row) {
             break;
         }
         int32_t *Q = (int32_t *)malloc(sizeof(int32_t) * n);
-        float rr[1024], cc[1024];
         if (imp)
             sqo_quantize_kra(J->bits[row], dk, dv, J->S32 + (size_t)row * n, imp, Q, rr, cc);
         else
@@ -609,7 +622,6 @@ static void run_row(const job_t *J, int row) {
             break;
         }
         int32_t *Q = (int32_t *)malloc(sizeof(int32_t) * n);
-        float rr[1024], cc[1024];
         sqo_record_unpack_rows(rbw, dk, dv, rec, Q, rr, cc);
         sqo_dequantize(dk, dv, Q, rr, cc, J->S32 + (size_t)row * n);
         free(Q);
@@ -624,7 +636,6 @@ static void run_row(const job_t *J, int row) {
             break;
         }
         int32_t *Q = (int32_t *)malloc(sizeof(int32_t) * n);
-        float rr[1024], cc[1024];
         sqo_record_unpack_rows(rbw, dk, dv, rec, Q, rr, cc);
         sqo_quant_step_codes_rows(J->kda, rbw, dk, dv, Q, rr, cc, J->q + (size_t)row * dk,
                                   J->k + (size_t)row * dk, J->v + (size_t)row * dv, J->beta[row],
@@ -640,7 +651,10 @@ static void run_row(const job_t *J, int row) {
         float *S32 = J->op == OP_F32STEP ? J->S32 + (size_t)row * n : NULL;
         if (S32)
             for (size_t e = 0; e < n; ++e) S[e] = (double)S32[e];
-        double alpha[1024], qd[1024], kd[1024], vd[1024];
+        double *alpha = (double *)malloc(sizeof(double) * (size_t)dk);
+        double *qd = (double *)malloc(sizeof(double) * (size_t)dk);
+        double *kd = (double *)malloc(sizeof(double) * (size_t)dk);
+        double *vd = (double *)malloc(sizeof(double) * (size_t)dv);
         gate_alpha(J->kda, dk, g, alpha);
         for (int i = 0; i < dk; ++i) {
             qd[i] = J->q[(size_t)row * dk + i];
@@ -653,9 +667,16 @@ static void run_row(const job_t *J, int row) {
             for (size_t e = 0; e < n; ++e) S32[e] = (float)S[e];
             free(S);
         }
+        free(alpha);
+        free(qd);
+        free(kd);
+        free(vd);
         break;
     }
     }
+    free(rbw);
+    free(rr);
+    free(cc);
 }
 
 static void *worker(void *arg) {

@@ -26,8 +26,9 @@
 //   S'_ij   = fma(code_ij, (a_i r_i) c_j, k_i u_j)    (decay + delta write, fp32:
 //                                                      each product rounded once)
 //   y_j     = c_j sum_i (q_i a_i r_i) code_ij + u_j (k.q)   (read-out, = S'^T q)
-//   c'_j    = max_i |S'_ij|,  r'_i = max_j |S'_ij| / c'_j / qmax
-//   code'   = round_half_even((S'_ij / c'_j) / r'_i)  (pinned fp32, in place)
+//   c'_j    = max_i |S'_ij|,  s_ij = S'_ij * (1 / c'_j),  r'_i = max_j |s_ij| / qmax
+//   code'   = round half to even of the exact product s_ij * (1 / r'_i)
+//             (fp32, each division correctly rounded; stored in place)
 //
 // Variants of the same body, chosen per launch or per head:
 //   - split step (decode_update): S' goes to a workspace instead of being
@@ -833,7 +834,7 @@ __device__ __forceinline__ float gate_factor(float g) { return (float)exp((doubl
 struct TileIn {
     uint32_t w[4][4];    // the lane's 4 row segments (BITS / 2 dwords used)
     float r[4];          // row scales of the lane's rows
-    float k[4], q[4];    // k, q at the lane's rows
+    float k[4];          // k at the lane's rows
     float g;             // KDA: log-gate of row band + NB (cg & 3); GDN: the head's
     float beta;          // beta of the (b, h) row
     float cj, vj;        // c_j, v_j of the column whose look-up this lane completes
@@ -876,7 +877,6 @@ __device__ __forceinline__ void load_tile(TileIn &in, int tile, uint8_t *rec, co
         const int row = band + G::NB * m;
         in.r[m] = rp[row];
         in.k[m] = ld<TI>(k, row);
-        in.q[m] = ld<TI>(q, row);
     }
     in.g = KDA ? ld<TI>(g, row_io * D + band + G::NB * (cg & 3)) : ld<TI>(g, row_io);
     in.beta = ld<TI>(reinterpret_cast<const TI *>(io.beta), row_io);

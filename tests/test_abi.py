@@ -30,6 +30,38 @@ def test_library_exports_every_declared_symbol():
     assert "gfx950" in Q.version()
 
 
+PAGES = ("hyper.ai", "ta-paperlens", "blog.ontle.kr", "bayesiansapien", "thelatestinai")
+
+
+def _declaration_comments():
+    """Comment block right above each function declaration of include/sq.h."""
+    import re
+    text = open(S.HEADER).read()
+    out = {}
+    for m in re.finditer(r"/\*((?:[^*]|\*(?!/))*)\*/\s*\n(?:sq_status|const char \*)\s*(sq_\w+)\(",
+                         text):
+        out[m.group(2)] = m.group(1)
+    return out
+
+
+def test_boundary_calls_cite_their_passage():
+    """Every call of the boundary says which passage of the pages defines what
+    it computes, and states its errors; sq_last_error is this library's own
+    error reporting."""
+    com = _declaration_comments()
+    for name in ("sq_pool_bytes", "sq_pool_create", "sq_pool_destroy", "sq_quant_state",
+                 "sq_decode_step", "sq_dequant_state", "sq_f32_decode_step"):
+        assert name in com, name
+        assert any(p in com[name] for p in PAGES), "%s cites no page" % name
+    for name in ("sq_pool_bytes", "sq_pool_create", "sq_quant_state", "sq_dequant_state",
+                 "sq_f32_decode_step"):
+        assert "SQ_EINVAL" in com[name] or "errors" in com[name].lower(), name
+    assert "error" in com["sq_last_error"].lower()
+    # the arithmetic the header states is the one the library and the oracle use
+    assert "(float)(((double)code_ij * r_i) * c_j)" in com["sq_dequant_state"]
+    assert "exact product s_ij * ir_i" in open(S.HEADER).read()
+
+
 def _rec(b, d):
     # FP16 pivot records hold the binary16 state and no scales
     return 2 * d * d if b == 16 else d * d * b // 8 + 8 * d

@@ -40,22 +40,32 @@ _lib = None
 WARMUP_STEPS = 128
 
 
-def build_lib() -> str:
-    """Compile ``sqgen.c`` into ``libsqgen.so`` beside it (always recompiles)."""
-    tmp = _LIB_PATH + ".tmp"
+_SAN_PATH = os.path.join(_HERE, "libsqgen_san.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def build_lib(sanitize: bool = False) -> str:
+    """Compile ``sqgen.c`` into ``libsqgen.so`` beside it (always recompiles).
+    sanitize: AddressSanitizer + UndefinedBehaviorSanitizer build, written to
+    libsqgen_san.so and loaded instead when SQ_SANITIZE=1."""
+    out = _SAN_PATH if sanitize else _LIB_PATH
+    tmp = out + ".tmp"
     subprocess.check_call(
-        ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-         "-pthread", _SRC, "-o", tmp, "-lm"])
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+        ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-pthread"] +
+        (SANITIZE_FLAGS if sanitize else []) + [_SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, out)
+    return out
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build_lib()
-        L = ctypes.CDLL(_LIB_PATH)
+        san = os.environ.get("SQ_SANITIZE") == "1"
+        path = _SAN_PATH if san else _LIB_PATH
+        if not os.path.exists(path):
+            build_lib(sanitize=san)
+        L = ctypes.CDLL(path)
         u64, i64, i32 = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int
         vp = ctypes.c_void_p
         L.sqg_key.restype = u64
