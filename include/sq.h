@@ -271,6 +271,15 @@ sq_status sq_check_slots(const sq_pool *pool, const int32_t *slot_idx, int32_t n
  * milliseconds.  counts NULL gives SQ_EINVAL. */
 sq_status sq_arith_selfcheck(uint64_t *counts, hipStream_t stream);
 
+/* Measurement helper: copy `bytes` (a multiple of 16) from src to dst, both
+ * DEVICE pointers, 16-byte aligned and not overlapping, with a plain
+ * streaming kernel (16-byte non-temporal loads and stores).  Its rate is the
+ * HBM bandwidth a read-and-write stream actually reaches on this GPU, which
+ * the benchmark reports next to the published peak; the pages define no such
+ * call.  bytes = 0 is a no-op.  Errors: SQ_EINVAL for NULL or misaligned
+ * pointers or a size that is not a multiple of 16. */
+sq_status sq_device_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
+
 /* Text describing the last non-OK status returned on this thread (error
  * reporting of this library; the pages define no interface).  Never NULL. */
 const char *sq_last_error(void);

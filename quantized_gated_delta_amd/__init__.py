@@ -6,7 +6,8 @@ the C ABI in ``include/sq.h``; ``sq`` is its thin ctypes binding.
 from .sq import (SQ_BF16, SQ_EHIP, SQ_EINVAL, SQ_ENOMEM, SQ_EUNSUPPORTED, SQ_F32, SQ_GATE_GDN,
                  SQ_GATE_KDA, SQ_OK, SQError, StatePool, header_symbols, lib, sq_arith_selfcheck,
                  sq_check_slots,
-                 sq_decode_step, sq_decode_update, sq_dequant_state, sq_f32_decode_step,
+                 sq_decode_step, sq_decode_update, sq_dequant_state, sq_device_copy,
+                 sq_f32_decode_step,
                  sq_last_error, sq_pool_bytes, sq_pool_create, sq_pool_destroy, sq_pool_layout,
                  sq_pool_set_row_impact, sq_quant_state, version)
 

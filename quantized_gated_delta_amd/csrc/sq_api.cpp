@@ -352,6 +352,15 @@ sq_status sq_check_slots(const sq_pool *pool, const int32_t *slot_idx, int32_t n
     return SQ_OK;
 }
 
+sq_status sq_device_copy(const void *src, void *dst, size_t bytes, hipStream_t stream) {
+    if (bytes == 0) return SQ_OK;
+    if (!src || !dst) return fail(SQ_EINVAL, "src or dst is NULL");
+    if (!aligned(src, 16) || !aligned(dst, 16)) return fail(SQ_EINVAL, "buffers are not 16-byte aligned");
+    if (bytes % 16) return fail(SQ_EINVAL, "bytes (%zu) is not a multiple of 16", bytes);
+    const hipError_t e = sqk::launch_stream_copy(src, dst, (uint64_t)(bytes / 16), stream);
+    return e == hipSuccess ? SQ_OK : hip_fail(e, "stream copy launch");
+}
+
 sq_status sq_arith_selfcheck(uint64_t *counts, hipStream_t stream) {
     if (!counts) return fail(SQ_EINVAL, "counts is NULL");
     if (!aligned(counts, 8)) return fail(SQ_EINVAL, "counts is not 8-byte aligned");

@@ -1639,6 +1639,34 @@ hipError_t launch_arith_selfcheck(unsigned long long *counts, hipStream_t stream
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- streaming copy
+// The HBM rate a plain read-and-write stream reaches (the practical ceiling
+// the decode step is compared with): 16-byte non-temporal loads and stores,
+// four in flight per lane, grid-stride over 32768 workgroups of 256 lanes
+// (the fastest of the shapes measured on MI355X).
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void stream_copy_kernel(const u4v *__restrict__ src,
+                                                          u4v *__restrict__ dst, uint64_t n) {
+    constexpr int U = 4;
+    const uint64_t stride = (uint64_t)gridDim.x * 256 * U;
+    uint64_t i = (uint64_t)blockIdx.x * 256 * U + threadIdx.x;
+    for (; i + 256 * (U - 1) < n; i += stride) {
+        u4v v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + 256 * u);
+#pragma unroll
+        for (int u = 0; u < U; ++u) __builtin_nontemporal_store(v[u], dst + i + 256 * u);
+    }
+    // tail: the last partial group of 1024 vectors, one vector per lane
+    for (; i < n; i += 256) dst[i] = src[i];
+}
+
+hipError_t launch_stream_copy(const void *src, void *dst, uint64_t n16, hipStream_t stream) {
+    hipLaunchKernelGGL(stream_copy_kernel, dim3(32768), dim3(256), 0, stream,
+                       static_cast<const u4v *>(src), static_cast<u4v *>(dst), n16);
+    return hipGetLastError();
+}
+
 hipError_t launch_f32_decode(float *state, int64_t slot_stride_floats, int32_t n_heads, int32_t d,
                              const StepIO &io, hipStream_t stream) {
     if (d == 128)

@@ -83,6 +83,8 @@ def lib():
         L.sq_check_slots.argtypes = [vp, vp, i32, vp]
         L.sq_arith_selfcheck.restype = st
         L.sq_arith_selfcheck.argtypes = [vp, vp]
+        L.sq_device_copy.restype = st
+        L.sq_device_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
         L.sq_last_error.restype = ctypes.c_char_p
         L.sq_last_error.argtypes = []
         L.sq_version.restype = ctypes.c_char_p
@@ -256,6 +258,12 @@ def sq_f32_decode_step(state, n_slots, n_heads, d_k, d_v, gate, slot_idx, n, q, 
 def sq_check_slots(handle, slot_idx, n: int, stream=None) -> None:
     _check(lib().sq_check_slots(handle, _ptr(slot_idx), int(n), _stream(stream)),
            "sq_check_slots")
+
+
+def sq_device_copy(src, dst, nbytes: int, stream=None) -> None:
+    """Streaming copy of nbytes between two device buffers (measurement helper)."""
+    _check(lib().sq_device_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)),
+           "sq_device_copy")
 
 
 def sq_arith_selfcheck(counts, stream=None) -> None:

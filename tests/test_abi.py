@@ -193,6 +193,15 @@ def test_f32_step_validation_without_launch():
             P, P, P, P, P, P, 1, 1, 0, text="state_pool")
 
 
+def test_device_copy_validation_without_launch():
+    lib = Q.lib()
+    assert lib.sq_device_copy(None, None, 0, None) == S.SQ_OK           # no-op
+    assert lib.sq_device_copy(None, FAKE_DEV, 64, None) == S.SQ_EINVAL
+    assert lib.sq_device_copy(FAKE_DEV, FAKE_DEV + 4, 64, None) == S.SQ_EINVAL   # misaligned
+    assert lib.sq_device_copy(FAKE_DEV, FAKE_DEV + 4096, 24, None) == S.SQ_EINVAL  # not 16 x n
+    assert "multiple of 16" in Q.sq_last_error()
+
+
 def test_last_error_is_thread_local():
     _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_bytes, 4, 1, 96, 96, [6], 0)
     seen = []

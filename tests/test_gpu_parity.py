@@ -235,6 +235,18 @@ def test_arith_selfcheck():
     assert counts.cpu().tolist() == [0, 0, 0, 0]
 
 
+def test_device_copy():
+    """The streaming copy the benchmark times: bytes land unchanged, a ragged
+    tail (not a multiple of the 16 KiB group) included."""
+    log("device copy")
+    n = (1 << 20) + 16 * 37
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device=DEV)
+    dst = torch.zeros_like(src)
+    Q.sq_device_copy(src, dst, n)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+
+
 # ----------------------------------------------------------------- G1
 @pytest.mark.parametrize("d", [64, 128])
 def test_quant_dequant_bit_exact(d):
@@ -526,6 +538,51 @@ def test_step_matches_plain_definition(name, n_rows, steps):
     assert worst_y <= Hn.Y_REL_L2
 
 
+# ----------------------------------------------------------------- offline allocation on the GPU
+def test_allocation_distortions_match_oracle():
+    """The allocator's GPU-backed calibration (hyper.ai summary, Method,
+    second paragraph; blog.ontle.kr, allocation paragraphs): the per-head
+    and per-key-row distortions it measures through the pool's quant /
+    dequant kernels equal the same distortions computed from the oracle's
+    quantizer and dequantizer on the host, and calibrate() allocates from
+    them."""
+    log("allocation distortions")
+    from quantized_gated_delta_amd import allocate as A
+    wl = W.custom("kda", 6, 5, 128, [6], dtype="bf16", n_slots=6, seed=41)
+    layer = wl.layers[0]
+    rows = Hn.rows_all(wl.B, wl.H)
+    S = Hn.oracle_warmup(wl, layer, rows, steps=24)                      # [N*H, d, d]
+    S[3] *= np.exp2(-40.0).astype(np.float32)                           # one tiny head state
+    N, H, d = wl.B, wl.H, wl.d
+    states = to_dev(S.reshape(N, H, d, d))
+    cand = (4, 6, 8)
+    D_gpu = A.measure_distortion(states, cand)
+    E_gpu = A.measure_row_distortion(states, cand)
+    S64 = S.astype(np.float64)
+    energy = (S64 ** 2).sum(axis=(1, 2))
+    D_ref = np.zeros((H, len(cand)))
+    E_ref = np.zeros((H, d, len(cand)))
+    for i, b in enumerate(cand):
+        sizes = np.full(N * H, Hn.record_bytes(b, d), np.int64)
+        offs = np.arange(N * H, dtype=np.int64) * sizes[0]
+        base = np.zeros(int(sizes.sum()), np.uint8)
+        bits = np.full(N * H, b, np.uint8)
+        O.records_quantize(base, offs, bits, S, d, d)
+        back = O.records_dequantize(base, offs, bits, d, d).astype(np.float64)
+        err_rows = ((back - S64) ** 2).sum(axis=2)                        # [N*H, d]
+        D_ref[:, i] = (err_rows.sum(axis=1) / energy).reshape(N, H).mean(axis=0)
+        E_ref[:, :, i] = (err_rows / energy[:, None]).reshape(N, H, d).mean(axis=0)
+    np.testing.assert_allclose(D_gpu, D_ref, rtol=1e-9, atol=0)
+    np.testing.assert_allclose(E_gpu, E_ref, rtol=1e-9, atol=1e-300)
+    assert (np.diff(D_ref, axis=1) < 0).all()                            # more bits, less error
+    gates = np.stack([W.to_f32(wl.step_inputs(layer, t)["g"]).reshape(N, H, d).mean(axis=0)
+                      for t in range(-8, 0)])
+    cal = A.calibrate(states, gates, avg_bits=6.0, candidates=cand)
+    np.testing.assert_allclose(cal["distortion"], D_ref, rtol=1e-9, atol=0)
+    want = A.allocate_bits(D_ref, A.head_lifetime_weights(gates), 6.0, cand)
+    assert np.array_equal(cal["bits"], want)
+
+
 # ----------------------------------------------------------------- workloads
 def test_c0_trajectory_64_steps():
     log("c0 trajectory")
@@ -655,6 +712,9 @@ def test_n0_noop_and_slot_check():
 
 
 # ----------------------------------------------------------------- c4
+C4_Y_ERR = {"gdn": (0.041, 0.105), "kda": (0.052, 0.122)}
+
+
 def test_c4_two_layers_vs_fp32_state():
     """GDN and KDA layers (B = 1024, H = 32, bits 4/6/8): the quantized step
     and the fp32-state step on identical inputs from the same warm-up state;
@@ -709,7 +769,14 @@ def test_c4_two_layers_vs_fp32_state():
         assert Hn.rel_l2(got32, S_ref32) <= 1e-4
         log("c4 layer %d: y error vs fp32 state, step 1 %.3g, step %d %.3g, max %.3g"
             % (layer.index, errs[0], T, errs[-1], max(errs)))
-        assert np.isfinite(errs).all() and max(errs) < 0.5
+        # bounds from the stored 1024-step trajectory of this workload
+        # (profiles/c4_trajectory_B1024_H32.json: y rel-L2 at step 1 and 16 of
+        # 0.041 / 0.105 for GDN and 0.052 / 0.122 for KDA), with 50 % margin;
+        # the error grows for about 100 steps before it levels off
+        step1, step16 = C4_Y_ERR[layer.gate]
+        assert np.isfinite(errs).all()
+        assert 0.5 * step1 <= errs[0] <= 1.5 * step1, errs[0]
+        assert max(errs) <= 1.5 * step16, max(errs)
         side.gpu.close()
         del state
 
