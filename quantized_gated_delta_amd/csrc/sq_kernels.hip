@@ -378,9 +378,13 @@ __device__ __forceinline__ float column_scale(float cmax, float *cp_j) {
     *cp_j = ok ? cmax : 0.0f;
     float ic = recip_rn(cmax);
     // maxima of 2^126 and above (reciprocal subnormal): the IEEE division,
-    // on a wavefront-uniform branch
-    if (__builtin_amdgcn_ballot_w64(cmax >= 0x1p126f) != 0)
-        if (cmax >= 0x1p126f) ic = 1.0f / cmax;
+    // on a wavefront-uniform branch (the empty asm keeps the compiler from
+    // computing the division on every path and selecting)
+    if (__builtin_amdgcn_ballot_w64(cmax >= 0x1p126f) != 0) {
+        float x = cmax;
+        asm volatile("" : "+v"(x));
+        if (x >= 0x1p126f) ic = 1.0f / x;
+    }
     return ok ? ic : 0.0f;
 }
 
@@ -613,7 +617,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void dequant_state_kernel(PoolView pool
 //   [0, PART_F)           the tile's codes as bytes (D x D, first half) and the
 //                         column-maximum partials of S' (NB x D fp32, second
 //                         half; before them the look-up's digit-sum exchange)
-//   [DIG_F, +4 D)         digit rows of the look-up and read-out factors (16 x D bytes)
+//   [DIG_F, +4 D + 32)    digit rows of the look-up and read-out factors (16 rows of
+//                         D bytes, row pitch D + 8 bytes)
 //   [IC_F, +D)            1/c'_j
 //   [CU_F, +2 D + 32)     {c_j, u_j}, padded to 18 per 16 columns
 //   [MISC_F, +16)         the GDN gate
@@ -621,8 +626,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void dequant_state_kernel(PoolView pool
 // FP64 partials and the words after it in their own way.
 template <int D> struct DecodeLds {
     static constexpr int PART_F = 2 * Geo<D>::NB * D; // floats in the partials region
-    static constexpr int DIG_F = PART_F, IC_F = PART_F + 4 * D, CU_F = PART_F + 5 * D,
-                         MISC_F = PART_F + 7 * D + 32;
+    static constexpr int DIG_F = PART_F, IC_F = PART_F + 4 * D + 32, CU_F = IC_F + D,
+                         MISC_F = CU_F + 2 * D + 32;
     static constexpr int TOTAL = MISC_F + 16;
 };
 
@@ -679,7 +684,7 @@ __device__ __forceinline__ void kra_quantize_store(float (&x)[4][16], const floa
     double *part64 = reinterpret_cast<double *>(lds);
     float *plane = lds; // column maxima; used (and reduced) before part64
     float *lds_c0 = lds + DecodeLds<D>::PART_F + 2 * D;
-    float *lds_ic = lds + DecodeLds<D>::PART_F + 4 * D;
+    float *lds_ic = lds + DecodeLds<D>::IC_F;
     float *rp = reinterpret_cast<float *>(rec + D * RB);
     float *cp = rp + D;
     // ---- row magnitudes, reduced over the band's lanes
@@ -920,35 +925,49 @@ template <int D> __device__ __forceinline__ int code_word(int j, int kq) {
     constexpr int NQ = D / 4;
     return j * NQ + (kq ^ (code_sw<D>(j) & (NQ - 1)));
 }
-// Digit rows: row d holds digit d of every key's factor, packed the same way
-// (index swizzled with bits 0..2 of d).
+// Digit rows: row d holds digit d of every key's factor, four keys per
+// dword in the code columns' key order, rows D / 4 + 2 dwords apart.  The
+// pitch (not a swizzle) keeps the matrix-core fragment reads (16 rows x 2
+// key dwords) on distinct banks, so a lane's eight digit writes and its
+// fragment reads all sit at fixed offsets from one base address.
 template <int D> __device__ __forceinline__ int digit_word(int d, int kq) {
-    constexpr int NQ = D / 4;
-    return d * NQ + (kq ^ ((((d & 3) << 3) | (((d >> 2) & 1) << 2)) & (NQ - 1)));
+    return d * (D / 4 + 2) + kq;
 }
 
 // Wavefront maximum of non-negative ints and sum of floats: DPP within rows of
-// 16 lanes (quad exchanges, then mirrors within 8 and 16), then the four row
-// results read into scalars and folded in lane order.
-constexpr int kRowMirror = 0x140; // row_mirror: lane i <-> 15 - i within 16
+// 16 lanes (quad exchanges, then mirrors within 8 and 16), after which every
+// lane holds its row's result; then row_bcast:15 folds row 0 into row 1 and
+// row 2 into row 3, row_bcast:31 folds row 1 into rows 2 and 3, and lane 63
+// holds the wavefront's result (sum order ((r2 + r3) + (r0 + r1))).
+constexpr int kRowMirror = 0x140;   // row_mirror: lane i <-> 15 - i within 16
+constexpr int kRowBcast15 = 0x142;  // lane 15 of each row to the next row
+constexpr int kRowBcast31 = 0x143;  // lane 31 to rows 2 and 3
+template <int CTRL, int ROW_MASK> __device__ __forceinline__ uint32_t dpp_rows(uint32_t v) {
+    // rows outside ROW_MASK keep v itself (the identity of max and of the
+    // fold below, which adds 0 for them)
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
 __device__ __forceinline__ int wave_max_i(int v) {
     v = max(v, (int)dpp_u<kQuadXor1>((uint32_t)v));
     v = max(v, (int)dpp_u<kQuadXor2>((uint32_t)v));
     v = max(v, (int)dpp_u<kHalfMirror>((uint32_t)v));
     v = max(v, (int)dpp_u<kRowMirror>((uint32_t)v));
-    return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-               max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+    v = max(v, (int)dpp_rows<kRowBcast15, 0xA>((uint32_t)v));
+    v = max(v, (int)dpp_rows<kRowBcast31, 0xC>((uint32_t)v));
+    return __builtin_amdgcn_readlane(v, 63);
 }
 __device__ __forceinline__ float wave_sum_dpp(float v) {
     v += __uint_as_float(dpp_u<kQuadXor1>(__float_as_uint(v)));
     v += __uint_as_float(dpp_u<kQuadXor2>(__float_as_uint(v)));
     v += __uint_as_float(dpp_u<kHalfMirror>(__float_as_uint(v)));
     v += __uint_as_float(dpp_u<kRowMirror>(__float_as_uint(v)));
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return ((r0 + r1) + r2) + r3;
+    // rows 1 and 3: + lane 15 of rows 0 and 2; then rows 2 and 3: + lane 31
+    const int lane = threadIdx.x & 63;
+    const float b15 = __uint_as_float(dpp_rows<kRowBcast15, 0xA>(__float_as_uint(v)));
+    v = (lane & 16) ? v + b15 : v;
+    const float b31 = __uint_as_float(dpp_rows<kRowBcast31, 0xC>(__float_as_uint(v)));
+    v = (lane & 32) ? v + b31 : v;
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Biased binary exponent of an FP64 value (0 for zero and subnormals).
@@ -1129,24 +1148,24 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     v4i acc[BPW];
 #pragma unroll
     for (int b = 0; b < BPW; ++b) acc[b] = v4i{0, 0, 0, 0};
-    // byte addresses of key step 0; key step s2 moves only address bits 5 and 6
-    // (the index bits 3..4 of 8 s2, which the swizzles XOR but never carry), so
-    // step s2 is step 0 XOR (s2 << 5)
-    // (the digit rows are swizzled like code columns 0..15, and the code
-    // swizzle splits as above: column 16 c + ln is column ln XOR the
-    // wave-uniform part of c)
-    const int a_dig = 4 * digit_word<D>(ln, 2 * lg); // = 4 code_word(ln, 2 lg)
+    // byte addresses of key step 0.  Code fragments: key step s2 moves only
+    // address bits 5 and 6 (the index bits 3..4 of 8 s2, which the swizzle
+    // XORs but never carries), so step s2 is step 0 XOR (s2 << 5); the code
+    // swizzle splits as above (column 16 c + ln is column ln XOR the
+    // wave-uniform part of c).  Digit fragments: step s2 is 32 s2 bytes on.
+    const int a_dig = 4 * digit_word<D>(ln, 2 * lg);
+    const int a_cw = 4 * code_word<D>(ln, 2 * lg);
     const int wu = __builtin_amdgcn_readfirstlane(w);
     int a_code[BPW];
 #pragma unroll
     for (int b = 0; b < BPW; ++b) {
         const int c = wu * BPW + b;
-        a_code[b] = (a_dig ^ (4 * (code_sw<D>(16 * c) & (NQ - 1)))) + 64 * c * NQ;
+        a_code[b] = (a_cw ^ (4 * (code_sw<D>(16 * c) & (NQ - 1)))) + 64 * c * NQ;
     }
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
         long A = 0;
-        if (ln < 12) A = *reinterpret_cast<const long *>(dig_b + (a_dig ^ (s2 << 5)));
+        if (ln < 12) A = *reinterpret_cast<const long *>(dig_b + a_dig + 32 * s2);
 #pragma unroll
         for (int b = 0; b < BPW; ++b) {
             const long B = *reinterpret_cast<const long *>(code_b + (a_code[b] ^ (s2 << 5)));
