@@ -24,7 +24,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gdn6_B512_H48_traffic.json")
+# Vector-ALU issue peak of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one
+# (non-packed) lane operation per lane per cycle; a wave64 instruction holds a
+# SIMD for 4 cycles.  In T lane-ops/s.
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Per state element, the vector operations the fused step cannot avoid once
+# the look-up and read-out sums run on the matrix cores: extract the code,
+# widen it, form (a r_i) c_j and k_i u_j, the update FMA, the column and row
+# maxima (half of a max3 each), s = S' / c', the rounding FMA and the pack.
+# Extract and pack cost 1.06 and 1.1 for 6-bit codes (fields straddle words).
+ESSENTIAL_VALU_PER_ELEMENT = {4: 9.0, 6: 9.16, 8: 9.0, 16: 9.0}
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_B512_H48_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "quantized_gated_delta_amd", "csrc", "sq_kernels.hip")
 
 
@@ -91,6 +101,10 @@ def main():
                     help="FP16 pivot heads per layer for the --allocate comparison")
     ap.add_argument("--calib", type=int, default=256,
                     help="requests whose warm-up states calibrate the allocation")
+    ap.add_argument("--only", choices=("kda_mixed", "kda_rows", "kra"),
+                    help="time only this variant of the B=512 H=48 step (for profiling runs): "
+                         "KDA 4/6/8 per head, KDA with per-key-row widths, or the key-row-aware "
+                         "fit on the 6-bit GDN pool; prints one short JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -192,6 +206,50 @@ def main():
         launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
         return wall / args.steps * 1e3, launch_ms
 
+    def kda_setup(per_row):
+        """KDA at the c3 shape: bits 4/6/8 at 25/50/25 % per head, or 4/6/8 on
+        25/50/25 % of every head's key rows; pool quantized from the warm-up
+        state.  Returns (pool, run function, algorithmic bytes per step)."""
+        wk = W.custom("kda", B, H, d, W.mixed_bits(0, 0, H), dtype="bf16",
+                      n_slots=wl.n_slots, permute=True, seed=0, name="kda_mixed")
+        lk = wk.layers[0]
+        if per_row:
+            rb, _ = W.row_widths_by_lifetime(lk.gate_rates)
+            pk = Q.StatePool(wl.n_slots, H, d, [0] * H, "kda", device=dev, row_bits=rb)
+            kb = algo_bytes_per_step(B, H, d, [6] * H, "kda")   # 6 bits on average per head
+        else:
+            pk = Q.StatePool(wl.n_slots, H, d, lk.head_bits.tolist(), "kda", device=dev)
+            kb = algo_bytes_per_step(B, H, d, lk.head_bits, "kda")
+        sk = to_dev(lk.slot_of.astype(np.int32))
+        st = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
+        st.copy_(state[slot_l.long()])
+        pk.quant_state(sk, st)
+        del st
+        kin = [{k: to_dev(v) for k, v in wk.step_inputs(lk, t).items()} for t in range(4)]
+
+        def run_k(n, ev=None):
+            for i in range(n):
+                x = kin[i % 4]
+                if ev is not None:
+                    ev[i][0].record(stream)
+                pk.decode_step(sk, x["q"], x["k"], x["v"], x["beta"], x["g"], y)
+                if ev is not None:
+                    ev[i][1].record(stream)
+        return pk, run_k, kb
+
+    if args.only:
+        if args.only == "kra":
+            pool.set_row_impact(torch.from_numpy(impact_from_workload(wl, layer, 4)).to(dev))
+            o_ms, o_launch = timed(pool, slot)
+            ob = algo_bytes_per_step(B, H, d, layer.head_bits, layer.gate)
+        else:
+            pk, run_k, ob = kda_setup(args.only == "kda_rows")
+            o_ms, o_launch = timed(None, None, run_k)
+        print(json.dumps({"variant": args.only, "us_per_step": o_ms * 1e3,
+                          "us_per_launch": o_launch * 1e3, "algo_bytes_per_step": ob,
+                          "achieved_GBps": ob / (o_launch * 1e-3) / 1e9}), flush=True)
+        return
+
     eprint("timing the quantized decode step (%s)" % args.workload)
     ms_step, ms_launch = timed(pool, slot)
     updates = B * H
@@ -255,52 +313,19 @@ def main():
             eprint("mixed 4/8: %.2f us/step, %.1f GB/s" % (b_ms * 1e3, variants["mixed_4_8_halflife"]["achieved_GBps"]))
             pool_b.close()
             # KDA (per-key-channel gate) at the same shape, bits 4/6/8 at 25/50/25 %
-            wk = W.custom("kda", B, H, d, W.mixed_bits(0, 0, H), dtype="bf16",
-                          n_slots=wl.n_slots, permute=True, seed=0, name="kda_mixed")
-            lk = wk.layers[0]
-            pool_k, slot_k = make_pool(lk)
-            stk = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
-            stk.copy_(state[slot_l.long()])
-            pool_k.quant_state(slot_k, stk)
-            del stk
-            kin = [{k: to_dev(v) for k, v in wk.step_inputs(lk, t).items()} for t in range(4)]
-
-            def run_k(n, ev=None):
-                for i in range(n):
-                    x = kin[i % 4]
-                    if ev is not None:
-                        ev[i][0].record(stream)
-                    pool_k.decode_step(slot_k, x["q"], x["k"], x["v"], x["beta"], x["g"], y)
-                    if ev is not None:
-                        ev[i][1].record(stream)
+            pool_k, run_k, kb = kda_setup(False)
             k_ms, k_launch = timed(None, None, run_k)
-            kb = algo_bytes_per_step(B, H, d, lk.head_bits, "kda")
             variants["kda_mixed_4_6_8"] = {
                 "updates_per_s": updates / (k_ms * 1e-3), "us_per_step": k_ms * 1e3,
                 "us_per_launch": k_launch * 1e3, "algo_bytes_per_step": kb,
                 "achieved_GBps": kb / (k_launch * 1e-3) / 1e9,
                 "hbm_frac": kb / (k_launch * 1e-3) / 1e9 / HBM_PEAK_GBS}
             eprint("kda mixed: %.2f us/step, %.1f GB/s" % (k_ms * 1e3, variants["kda_mixed_4_6_8"]["achieved_GBps"]))
+            pool_k.close()
             # the same KDA step with per-key-row widths: 4/6/8 bits on 25/50/25 %
             # of every head's key rows (the KDA unit of the allocation)
-            rb, _ = W.row_widths_by_lifetime(lk.gate_rates)
-            pool_r = Q.StatePool(wl.n_slots, H, d, [0] * H, "kda", device=dev, row_bits=rb)
-            str_ = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
-            str_.copy_(state[slot_l.long()])
-            pool_r.quant_state(slot_k, str_)
-            del str_
-
-            def run_r(n, ev=None):
-                for i in range(n):
-                    x = kin[i % 4]
-                    if ev is not None:
-                        ev[i][0].record(stream)
-                    pool_r.decode_step(slot_k, x["q"], x["k"], x["v"], x["beta"], x["g"], y)
-                    if ev is not None:
-                        ev[i][1].record(stream)
+            pool_r, run_r, pb = kda_setup(True)
             p_ms, p_launch = timed(None, None, run_r)
-            # 6 bits on average per head: the 6-bit byte model with the KDA gate
-            pb = algo_bytes_per_step(B, H, d, [6] * H, "kda")
             variants["kda_per_row_4_6_8"] = {
                 "updates_per_s": updates / (p_ms * 1e-3), "us_per_step": p_ms * 1e3,
                 "us_per_launch": p_launch * 1e3, "algo_bytes_per_step": pb,
@@ -309,7 +334,6 @@ def main():
             eprint("kda per-row widths: %.2f us/step, %.1f GB/s"
                    % (p_ms * 1e3, variants["kda_per_row_4_6_8"]["achieved_GBps"]))
             pool_r.close()
-            pool_k.close()
     del state
     copy_GBps, torch_copy_GBps = device_copy_GBps(dev)
     eprint("device copy: %.0f GB/s (streaming kernel), %.0f GB/s (torch copy)"
@@ -323,12 +347,18 @@ def main():
         cpu = cpu_baseline(wl, layer, args.cpu_seconds)
         eprint("cpu oracle: %.3g updates/s on %d threads" % (cpu["value"], cpu["cores"]))
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_src_sha256_16") == kernel_hash() and tr.get("workload") == args.workload:
-            traffic = tr.get("bytes_per_launch")
+    # HBM traffic and VALU issue from the committed counter profile, while the
+    # kernel source it was taken on is the one built here
+    prof = None
+    if os.path.exists(COUNTERS_FILE):
+        with open(COUNTERS_FILE) as f:
+            cp = json.load(f)
+        if cp.get("kernel_src_sha256_16") == kernel_hash():
+            prof = cp["variants"].get(args.workload)
+    elems = B * H * d * d
+    hb = [int(b) for b in layer.head_bits]
+    ess = sum(ESSENTIAL_VALU_PER_ELEMENT[b] for b in hb) / len(hb)
+    alu_achieved = ess * elems / (ms_launch * 1e-3) / 1e12
 
     out = {
         "metric": "state-updates/s (req x head x step) and achieved HBM GB/s vs peak at B=512",
@@ -350,12 +380,19 @@ def main():
                                  "combined in f64, u rounded once to f32; update and "
                                  "requantizer in f32",
                    "gate": layer.gate},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "device_copy_GBps": copy_GBps, "torch_copy_GBps": torch_copy_GBps,
-                     "frac_of_device_copy": achieved / copy_GBps,
-                     "algo_bytes_per_launch": bytes_step, "us_per_launch": ms_launch * 1e3,
-                     "kernel": "decode_kernel<128, GDN, bf16, bf16>"},
+        "roofline": {"bound": "alu", "achieved": alu_achieved, "peak": VALU_PEAK_TOPS,
+                     "unit": "T lane-ops/s", "frac": alu_achieved / VALU_PEAK_TOPS,
+                     "traffic": None if prof is None else prof["bytes_per_launch"],
+                     "essential_valu_per_element": ess, "state_elements_per_launch": elems,
+                     "valu_insts_per_element": None if prof is None else prof["valu_insts_per_element"],
+                     "valu_issue_frac": None if prof is None else prof["valu_issue_frac"],
+                     "us_per_launch": ms_launch * 1e3,
+                     "kernel": "decode_kernel<128, %s, bf16, bf16>" % layer.gate.upper(),
+                     "hbm": {"achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": achieved / HBM_PEAK_GBS,
+                             "algo_bytes_per_launch": bytes_step,
+                             "device_copy_GBps": copy_GBps, "torch_copy_GBps": torch_copy_GBps,
+                             "frac_of_device_copy": achieved / copy_GBps}},
         "cpu_baseline": cpu,
         "variants": variants,
     }
