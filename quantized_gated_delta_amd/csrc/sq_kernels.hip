@@ -43,6 +43,10 @@
 
 #include "sq_internal.h"
 
+#ifndef SQ_DECODE_WAVES
+#define SQ_DECODE_WAVES 5
+#endif
+
 namespace sqk {
 namespace {
 
@@ -398,31 +402,38 @@ __device__ __forceinline__ void load16(const float *src, float (&v)[16]) {
     }
 }
 
-// Row part.  x holds S' on entry.  s = S' ic is formed once: |s| is the
-// pinned |S'| ic of the row maximum and s * ir is the pinned scaled entry.
+// Row part.  x holds S' on entry and ic_vec the reciprocal column scales
+// (colvec4 layout), read four columns at a time so that they are not all live
+// next to the 64 entries.  s = S' ic is formed once: |s| is the pinned |S'| ic
+// of the row maximum and s * ir is the pinned scaled entry.
 // The row maxima are reduced over the band's lanes with DPP; lane cg < 4 of
 // a band then computes the two correctly rounded divisions of row cg, and
 // the results are broadcast back with ds_swizzle.  Codes: round half to even
 // of the exact product s * ir (code_bits); |s * ir| <= qmax (1 + 2 eps), so
 // the clamp to [-qmax, qmax] can never act and is omitted.
 template <int D, int BITS, bool MIXED = false>
-__device__ __forceinline__ void quantize_rows_store(float (&x)[4][16], const float (&ic)[16],
+__device__ __forceinline__ void quantize_rows_store(float (&x)[4][16], const float *ic_vec,
                                                     uint8_t *rec, Rows<D, BITS, MIXED> rows = {}) {
 #pragma clang fp contract(off)
     using G = Geo<D>;
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     float *rp = reinterpret_cast<float *>(rec + rows.codes_bytes());
-    float rm[4];
+    float rm[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        rm[m] = 0.0f;
+    for (int n4 = 0; n4 < 4; ++n4) {
+        const float4 f = *reinterpret_cast<const float4 *>(ic_vec + colvec4_idx(16 * cg + 4 * n4));
+        const float ic[4] = {f.x, f.y, f.z, f.w};
 #pragma unroll
-        for (int n = 0; n < 16; ++n) {
-            x[m][n] = x[m][n] * ic[n];
-            rm[m] = fmaxf(rm[m], fabsf(x[m][n]));
-        }
-        rm[m] = band_max<G::CG>(rm[m]);
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = 4 * n4 + i;
+                x[m][n] = x[m][n] * ic[i];
+                rm[m] = fmaxf(rm[m], fabsf(x[m][n]));
+            }
     }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) rm[m] = band_max<G::CG>(rm[m]);
     // lane cg (< 4) of the band owns row band + NB * cg
     const float sel01 = (cg & 1) ? rm[1] : rm[0];
     const float sel23 = (cg & 1) ? rm[3] : rm[2];
@@ -474,9 +485,7 @@ __device__ __forceinline__ void quant_tile(uint8_t *rec, const float *S, float *
     __syncthreads();
     if (t < D) lds_ic[colvec4_idx(t)] = column_scale(column_max<D>(plane, t), cp + t);
     __syncthreads();
-    float ic[16];
-    load_colvec16(lds_ic, cg, ic);
-    quantize_rows_store<D, BITS, MIXED>(x, ic, rec, rows);
+    quantize_rows_store<D, BITS, MIXED>(x, lds_ic, rec, rows);
 }
 
 // ---------------------------------------------------------------- FP16 pivot records
@@ -614,20 +623,27 @@ __global__ __launch_bounds__(Geo<D>::NT) void dequant_state_kernel(PoolView pool
 
 // ---------------------------------------------------------------- decode step
 // LDS of the decode step (floats from the base):
-//   [0, PART_F)           the tile's codes as bytes (D x D, first half) and the
-//                         column-maximum partials of S' (NB x D fp32, second
-//                         half; before them the look-up's digit-sum exchange)
+//   [0, MAIN_F)           the tile's codes as bytes (D x D); after the step has
+//                         read them, the column-maximum partials of S' in the
+//                         same dwords (the dword of column j and key quad band
+//                         holds that band's partial of column j).  The FP16
+//                         pivot step uses it for its pair-summed FP64 look-up
+//                         partials and then its read-out partials.  WIDE (the
+//                         key-row-aware fit): 2 NB x D floats, its two FP64
+//                         column sums.
+//   [XCH_F, +3 NW BPW 32) the FP64 digit-sum exchange of the look-up
 //   [DIG_F, +4 D + 32)    digit rows of the look-up and read-out factors (16 rows of
 //                         D bytes, row pitch D + 8 bytes)
 //   [IC_F, +D)            1/c'_j
 //   [CU_F, +2 D + 32)     {c_j, u_j}, padded to 18 per 16 columns
 //   [MISC_F, +16)         the GDN gate
-// The FP16 pivot step and the key-row-aware fit use [0, PART_F) as NB x D
-// FP64 partials and the words after it in their own way.
-template <int D> struct DecodeLds {
-    static constexpr int PART_F = 2 * Geo<D>::NB * D; // floats in the partials region
-    static constexpr int DIG_F = PART_F, IC_F = PART_F + 4 * D + 32, CU_F = IC_F + D,
-                         MISC_F = CU_F + 2 * D + 32;
+// Without WIDE that is 23.3 KB at d = 128, so LDS does not limit a CU to
+// fewer workgroups than the register budget does.
+template <int D, bool WIDE = false> struct DecodeLds {
+    static constexpr int MAIN_F = WIDE ? 2 * Geo<D>::NB * D : D * D / 4;
+    static constexpr int XCH_F = MAIN_F;
+    static constexpr int DIG_F = XCH_F + 3 * Geo<D>::NW * (Geo<D>::CG / Geo<D>::NW) * 32;
+    static constexpr int IC_F = DIG_F + 4 * D + 32, CU_F = IC_F + D, MISC_F = CU_F + 2 * D + 32;
     static constexpr int TOTAL = MISC_F + 16;
 };
 
@@ -683,8 +699,8 @@ __device__ __forceinline__ void kra_quantize_store(float (&x)[4][16], const floa
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     double *part64 = reinterpret_cast<double *>(lds);
     float *plane = lds; // column maxima; used (and reduced) before part64
-    float *lds_c0 = lds + DecodeLds<D>::PART_F + 2 * D;
-    float *lds_ic = lds + DecodeLds<D>::IC_F;
+    float *lds_c0 = lds + DecodeLds<D, true>::DIG_F + 2 * D; // digit rows: dead by now
+    float *lds_ic = lds + DecodeLds<D, true>::IC_F;
     float *rp = reinterpret_cast<float *>(rec + D * RB);
     float *cp = rp + D;
     // ---- row magnitudes, reduced over the band's lanes
@@ -818,7 +834,7 @@ __global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(4)))
 void quant_state_kra_kernel(PoolView pool, HeadTable tab,
                                                                      const int32_t *slot,
                                                                      const float *S) {
-    __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D>::TOTAL];
+    __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D, true>::TOTAL];
     int b, h;
     tile_bh(pool, blockIdx.x, b, h);
     uint8_t *rec = pool.base + (int64_t)slot[b] * pool.slot_stride + tab.off[h];
@@ -1013,7 +1029,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
                                             Rows<D, BITS, MIXED> rows = {}) {
     static_assert(!(KRA && MIXED), "the key-row-aware fit takes uniform widths");
     using G = Geo<D>;
-    using L = DecodeLds<D>;
+    using L = DecodeLds<D, KRA>;
     constexpr int NQ = D / 4;              // dwords per code column
     constexpr int BPW = G::CG / G::NW;     // 16-column blocks per wave
     constexpr int KS = D / 32;             // key steps of the matrix-core look-up
@@ -1021,8 +1037,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     const int w = t >> 6, lg = (t >> 4) & 3, ln = t & 15;
     uint8_t *code_b = reinterpret_cast<uint8_t *>(lds);
-    float *plane_max = lds + D * D / 4;
-    double *xch = reinterpret_cast<double *>(plane_max); // digit-sum exchange, before phase 2
+    double *xch = reinterpret_cast<double *>(lds + L::XCH_F); // digit-sum exchange
     uint8_t *dig_b = reinterpret_cast<uint8_t *>(lds + L::DIG_F);
     float *lds_ic = lds + L::IC_F;
     float2 *lds_cu = reinterpret_cast<float2 *>(lds + L::CU_F); // {c_j, u_j} at 18 (j / 16) + j % 16
@@ -1202,7 +1217,10 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     }
     __syncthreads();
     // ---- decay + delta write in fp32: S'_mn = fma(code, (a_m r_m) c_n, k_m u_n),
-    //      each product rounded once; column maxima partials
+    //      each product rounded once; the column-maximum partial of the lane's
+    //      four rows replaces the code dword it was computed from (only this
+    //      lane reads that dword after the matrix cores, which finished before
+    //      the last barrier)
     float x[4][16];
     {
         float ar[4];
@@ -1213,27 +1231,25 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
         const float4 *cu4 = reinterpret_cast<const float4 *>(lds_cu + 18 * cg);
 #pragma unroll
         for (int n4 = 0; n4 < 4; ++n4) {
-            float cm[4];
             const float4 p01 = cu4[2 * n4], p23 = cu4[2 * n4 + 1];
             const float2 cup[4] = {make_float2(p01.x, p01.y), make_float2(p01.z, p01.w),
                                    make_float2(p23.x, p23.y), make_float2(p23.z, p23.w)};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int n = 4 * n4 + i;
-                const uint32_t cw = *reinterpret_cast<const uint32_t *>(code_b + cbase[n & 7] + 4 * n * NQ);
+                uint32_t *cwp = reinterpret_cast<uint32_t *>(code_b + cbase[n & 7] + 4 * n * NQ);
+                const uint32_t cw = *cwp;
                 const float2 cu = cup[i];
-                cm[i] = 0.0f;
+                float cm = 0.0f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const float code = (float)(int8_t)(cw >> (8 * m));
                     const float sf = fmaf(code, ar[m] * cu.x, cur.k[m] * cu.y);
                     x[m][n] = sf;
-                    cm[i] = fmaxf(cm[i], fabsf(sf));
+                    cm = fmaxf(cm, fabsf(sf));
                 }
+                if constexpr (!SPLIT && !KRA) *cwp = __float_as_uint(cm);
             }
-            if constexpr (!SPLIT && !KRA)
-                *reinterpret_cast<float4 *>(plane_max + plane_idx<D>(band, cg, 4 * n4)) =
-                    make_float4(cm[0], cm[1], cm[2], cm[3]);
         }
     }
     if constexpr (SPLIT) {
@@ -1254,11 +1270,21 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     if constexpr (KRA) {
         kra_quantize_store<D, BITS>(x, imp, rec, lds);
     } else {
-        if (t < D) lds_ic[colvec4_idx(t)] = column_scale(column_max<D>(plane_max, t), cp + t);
+        if (t < D) {
+            // the 32 band partials of column t: its code dwords, 16 bytes at a
+            // time (eight consecutive columns' swizzles differ in index bits
+            // 2..4, so each 16-byte read of eight lanes covers all banks)
+            const uint4 *col = reinterpret_cast<const uint4 *>(code_b + 4 * t * NQ);
+            uint32_t cmax = 0;
+#pragma unroll
+            for (int i = 0; i < NQ / 4; ++i) {
+                const uint4 v = col[i];
+                cmax = max(cmax, max(max(v.x, v.y), max(v.z, v.w)));
+            }
+            lds_ic[colvec4_idx(t)] = column_scale(__uint_as_float(cmax), cp + t);
+        }
         __syncthreads();
-        float ic[16];
-        load_colvec16(lds_ic, cg, ic);
-        quantize_rows_store<D, BITS, MIXED>(x, ic, rec, rows);
+        quantize_rows_store<D, BITS, MIXED>(x, lds_ic, rec, rows);
     }
 }
 
@@ -1269,12 +1295,11 @@ template <int D, bool KDA, bool SPLIT, typename TI, typename TO>
 __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const StepIO &io,
                                                 float *lds) {
     using G = Geo<D>;
-    constexpr int PLANE = G::NB * D;
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
-    double *part64 = reinterpret_cast<double *>(lds);
-    float *plane_y = lds + PLANE;
-    float2 *lds_cu = reinterpret_cast<float2 *>(lds + DecodeLds<D>::PART_F);
-    float *lds_misc = lds + DecodeLds<D>::PART_F + 5 * D;
+    double *part64 = reinterpret_cast<double *>(lds); // NB / 2 x D pair sums
+    float *plane_y = lds;                               // NB x D, after part64 is read
+    float2 *lds_cu = reinterpret_cast<float2 *>(lds + DecodeLds<D>::CU_F);
+    float *lds_misc = lds + DecodeLds<D>::MISC_F;
     const int64_t row_io = tile;
     const TI *k = reinterpret_cast<const TI *>(io.k) + row_io * D;
     const TI *q = reinterpret_cast<const TI *>(io.q) + row_io * D;
@@ -1307,6 +1332,8 @@ __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const St
         double ka[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) ka[m] = KDA ? (double)kf[m] * (double)am[m] : (double)kf[m];
+        // each lane sums its 4 rows, the two bands of a lane pair (lanes t
+        // and t ^ CG) are added by a lane exchange, and the even band writes
 #pragma unroll
         for (int n2 = 0; n2 < 8; ++n2) {
             double acc0 = 0.0, acc1 = 0.0;
@@ -1315,8 +1342,11 @@ __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const St
                 acc0 = fma(ka[m], (double)half_lo(w[m][n2]), acc0);
                 acc1 = fma(ka[m], (double)half_hi(w[m][n2]), acc1);
             }
-            *reinterpret_cast<double2 *>(part64 + part_idx<D>(band, cg, 2 * n2)) =
-                make_double2(acc0, acc1);
+            acc0 = pair_sum<G::CG>(acc0);
+            acc1 = pair_sum<G::CG>(acc1);
+            if ((band & 1) == 0)
+                *reinterpret_cast<double2 *>(part64 + part_idx<D>(band >> 1, cg, 2 * n2)) =
+                    make_double2(acc0, acc1);
         }
     }
     __syncthreads();
@@ -1327,7 +1357,7 @@ __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const St
     if (t < D) {
         double P = 0.0;
 #pragma unroll 8
-        for (int b = 0; b < G::NB; ++b) P += part64[part_idx<D>(b, t >> 4, t & 15)];
+        for (int b = 0; b < G::NB / 2; ++b) P += part64[part_idx<D>(b, t >> 4, t & 15)];
         if constexpr (!KDA) P *= (double)am[0];
         lds_cu[colvec2_idx(t)] = make_float2(1.0f, (float)((double)beta * ((double)vj - P)));
     }
@@ -1390,16 +1420,21 @@ __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const St
     }
 }
 
-constexpr int kDecodeWavesPerEU = 4;
-// One workgroup per (request, head) tile; four resident per CU (VGPRs and
-// LDS both sized for four 4-wave workgroups), which hides the barriers and
-// reduction phases of one tile behind the others.
+// One workgroup per (request, head) tile, as many resident per CU as the
+// register budget allows: five 4-wave workgroups (96 VGPRs, 23.3 KB of LDS
+// each), which hides the loads, barriers and reduction phases of one tile
+// behind the others.  Four with the key-row-aware fit (its FP64 column sums
+// take 32 KB of LDS) and in pools with per-key-row widths (whose mixed-width
+// body needs more than 96 VGPRs without spilling).
+template <bool KRA, bool ROWS> constexpr int decode_waves_per_eu() {
+    return KRA || ROWS ? 4 : SQ_DECODE_WAVES;
+}
 // ROWS: the pool has heads with per-key-row widths (their own kernel, so
 // that pools without them keep the register budget of the uniform bodies).
 template <int D, bool KDA, bool SPLIT, bool KRA, bool ROWS, typename TI, typename TO>
-__global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerEU)))
+__global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<KRA, ROWS>())))
 void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
-    __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D>::TOTAL];
+    __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D, KRA>::TOTAL];
     const int tile = blockIdx.x;
     // Two rounds of scalar loads before the record's address is known: the
     // pool and step arguments, then slot, offset and widths together (the
