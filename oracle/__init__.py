@@ -86,6 +86,8 @@ def lib():
                                                 vp, vp, vp]
         L.sqo_quantize_kra.restype = None
         L.sqo_quantize_kra.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+        L.sqo_quantize_kra_rows.restype = None
+        L.sqo_quantize_kra_rows.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp]
         L.sqo_reconstruct_f64.restype = None
         L.sqo_reconstruct_f64.argtypes = [i32, i32, vp, vp, vp, vp]
         L.sqo_dequantize.restype = None
@@ -237,6 +239,21 @@ def quantize_kra(bits: int, S, imp) -> tuple:
     r = np.empty(dk, np.float32)
     c = np.empty(dv, np.float32)
     lib().sqo_quantize_kra(bits, dk, dv, _p(S), _p(imp), _p(Q), _p(r), _p(c))
+    return Q, r, c
+
+
+def quantize_kra_rows(row_bits, S, imp) -> tuple:
+    """The key-row-aware fit with each key row at its own width row_bits [dk]
+    (4, 6 or 8): returns (Q int32, r f32 [dk], c f32 [dv])."""
+    rb = _c(row_bits, np.uint8)
+    S = _c(S, np.float32)
+    imp = _c(imp, np.float32)
+    dk, dv = S.shape
+    assert imp.shape == (dk,) and rb.shape == (dk,)
+    Q = np.empty((dk, dv), np.int32)
+    r = np.empty(dk, np.float32)
+    c = np.empty(dv, np.float32)
+    lib().sqo_quantize_kra_rows(_p(rb), dk, dv, _p(S), _p(imp), _p(Q), _p(r), _p(c))
     return Q, r, c
 
 

@@ -335,6 +335,88 @@ void sqo_quantize_kra(int bits, int dk, int dv, const float *S, const float *imp
 }
 
 /*
+ * The key-row-aware fit on a head whose key rows have their own widths
+ * (blog.ontle.kr, allocation paragraph: for KDA a single key row is the unit
+ * of the bit allocation; the fit as in sqo_quantize_kra).  Row i takes the
+ * levels -qmax_i .. qmax_i of its width; qref = max_i qmax_i (the head's
+ * widest rows).  Each row's factor is widened by g_i = qref / qmax_i, as the
+ * closed rule divides a row's range by its own qmax_i, so that every row
+ * spans its own levels on the shared column grid:
+ *   g_i   = qref / qmax_i                        (fp32; 1 for the widest rows)
+ *   r_i   = sqrt(mu_i / imp_i) * g_i             (0 under the rules above)
+ *   s_ij  = S_ij * ir_i
+ *   c0_j  = max_i (|s_ij| * g_i) / qref          (covers every row's range)
+ *   P_ij  = clamp(round_half_even(s_ij * ic0_j), -qmax_i, qmax_i)
+ *   A_j, B_j, c_j as in sqo_quantize_kra
+ *   Q_ij  = clamp(round_half_even(s_ij * ic_j), -qmax_i, qmax_i)
+ * With all widths equal, g_i = 1 and every step is that of sqo_quantize_kra
+ * (the clamp of P never acts there).  The argument that the weighted error
+ * never exceeds that of (c0, P) holds row by row with each row's own range.
+ */
+void sqo_quantize_kra_rows(const uint8_t *row_bits, int dk, int dv, const float *S,
+                           const float *imp, int32_t *Q, float *r, float *c) {
+    float *qm = (float *)malloc(sizeof(float) * (size_t)dk);
+    float *gi = (float *)malloc(sizeof(float) * (size_t)dk);
+    float *ir = (float *)malloc(sizeof(float) * (size_t)dk);
+    float *sc = (float *)malloc(sizeof(float) * (size_t)dk * dv);
+    float qref = 0.0f;
+    for (int i = 0; i < dk; ++i) {
+        qm[i] = (float)sqo_qmax(row_bits[i]);
+        if (qm[i] > qref) qref = qm[i];
+    }
+    for (int i = 0; i < dk; ++i) {
+        gi[i] = qref / qm[i];
+        float mu = 0.0f;
+        for (int j = 0; j < dv; ++j) {
+            const float a = fabsf(S[(size_t)i * dv + j]);
+            if (a > mu) mu = a;
+        }
+        float ri = 0.0f;
+        if (mu >= FLT_MIN) ri = sqrtf(mu / imp[i]) * gi[i];
+        if (!(ri >= FLT_MIN) || isinf(ri)) ri = 0.0f;
+        r[i] = ri;
+        ir[i] = ri > 0.0f ? 1.0f / ri : 0.0f;
+        for (int j = 0; j < dv; ++j) sc[(size_t)i * dv + j] = S[(size_t)i * dv + j] * ir[i];
+    }
+    for (int j = 0; j < dv; ++j) {
+        float m = 0.0f;
+        for (int i = 0; i < dk; ++i) {
+            const float a = fabsf(sc[(size_t)i * dv + j]) * gi[i];
+            if (a > m) m = a;
+        }
+        float c0 = m / qref, ic0 = 0.0f;
+        if (c0 >= FLT_MIN)
+            ic0 = 1.0f / c0;
+        else
+            c0 = 0.0f;
+        double A = 0.0, B = 0.0;
+        for (int i = 0; i < dk; ++i) {
+            const double sv = (double)sc[(size_t)i * dv + j];
+            double P = nearbyint(sv * (double)ic0);
+            if (P > qm[i]) P = qm[i];
+            if (P < -qm[i]) P = -qm[i];
+            const double w = (double)imp[i] * (double)r[i] * (double)r[i];
+            A += w * sv * P;
+            B += w * P * P;
+        }
+        float cj = B > 0.0 ? (float)(A / B) : c0;
+        if (!(cj >= FLT_MIN)) cj = 0.0f;
+        const float icj = cj > 0.0f ? 1.0f / cj : 0.0f;
+        c[j] = cj;
+        for (int i = 0; i < dk; ++i) {
+            double qv = nearbyint((double)sc[(size_t)i * dv + j] * (double)icj);
+            if (qv > qm[i]) qv = qm[i];
+            if (qv < -qm[i]) qv = -qm[i];
+            Q[(size_t)i * dv + j] = (int32_t)qv;
+        }
+    }
+    free(qm);
+    free(gi);
+    free(ir);
+    free(sc);
+}
+
+/*
  * Reconstruction (hyper.ai "Method" para 4: the state is the product of row
  * factors, column factors and low-bit integers): S_ij = Q_ij * r_i * c_j,
  * evaluated in FP64 as ((double)Q_ij * r_i) * c_j.  Q_ij * r_i is exact; the
@@ -452,6 +534,13 @@ void sqo_step_update(int dk, int dv, const float *Z, const float *R, const float
     free(u32);
 }
 
+/* 1 if every key row has the same width */
+static int uniform_widths(const uint8_t *row_bits, int dk) {
+    for (int i = 1; i < dk; ++i)
+        if (row_bits[i] != row_bits[0]) return 0;
+    return 1;
+}
+
 /*
  * Quantized step on one head with unpacked codes (any bits 2..24):
  * the step update above on the codes -> fp32 S' ->
@@ -469,8 +558,10 @@ void sqo_quant_step_codes_rows(int kda, const uint8_t *row_bits, int dk, int dv,
     for (size_t e = 0; e < n; ++e) Z[e] = (float)Q[e]; /* exact: |Q| < 2^24 */
     gate_alpha_f32(kda, dk, g, alpha);
     sqo_step_update(dk, dv, Z, r, c, alpha, q, k, v, beta, S, y);
-    if (imp)
-        sqo_quantize_kra(row_bits[0], dk, dv, S, imp, Q, r, c); /* uniform widths only */
+    if (imp && uniform_widths(row_bits, dk))
+        sqo_quantize_kra(row_bits[0], dk, dv, S, imp, Q, r, c);
+    else if (imp)
+        sqo_quantize_kra_rows(row_bits, dk, dv, S, imp, Q, r, c);
     else
         sqo_quantize_rows(row_bits, dk, dv, S, Q, r, c);
     free(S);
@@ -606,8 +697,10 @@ static void run_row(const job_t *J, int row) {
             break;
         }
         int32_t *Q = (int32_t *)malloc(sizeof(int32_t) * n);
-        if (imp)
+        if (imp && J->bits[row] != 0)
             sqo_quantize_kra(J->bits[row], dk, dv, J->S32 + (size_t)row * n, imp, Q, rr, cc);
+        else if (imp)
+            sqo_quantize_kra_rows(rbw, dk, dv, J->S32 + (size_t)row * n, imp, Q, rr, cc);
         else
             sqo_quantize_rows(rbw, dk, dv, J->S32 + (size_t)row * n, Q, rr, cc);
         sqo_record_pack_rows(rbw, dk, dv, Q, rr, cc, rec);
@@ -704,13 +797,11 @@ static int run_rows(job_t proto, int n_rows, int n_threads) {
     return 0;
 }
 
-/* Record widths 4, 6, 8, 16, or 0 with per-key-row widths in {4, 6, 8}
- * (which the key-row-aware fit does not take). */
-static int check_bits(int n, int dk, const uint8_t *bits, const uint8_t *row_bits,
-                      const float *imp) {
+/* Record widths 4, 6, 8, 16, or 0 with per-key-row widths in {4, 6, 8}. */
+static int check_bits(int n, int dk, const uint8_t *bits, const uint8_t *row_bits) {
     for (int i = 0; i < n; ++i) {
         if (bits[i] == 0) {
-            if (!row_bits || imp) return -1;
+            if (!row_bits) return -1;
             for (int r = 0; r < dk; ++r) {
                 const uint8_t b = row_bits[(size_t)i * dk + r];
                 if (b != 4 && b != 6 && b != 8) return -1;
@@ -729,7 +820,7 @@ static int check_bits(int n, int dk, const uint8_t *bits, const uint8_t *row_bit
 int sqo_records_quantize(int n, int dk, int dv, const uint8_t *bits, const int64_t *offs,
                          uint8_t *base, const float *S, const float *imp, const uint8_t *row_bits,
                          int n_threads) {
-    if (check_bits(n, dk, bits, row_bits, imp)) return -1;
+    if (check_bits(n, dk, bits, row_bits)) return -1;
     job_t J = {OP_QUANT, 0, dk, dv, 0, 0, bits, offs, base, (float *)S, NULL,
                NULL, NULL, NULL, NULL, NULL, NULL, imp, row_bits};
     return run_rows(J, n, n_threads);
@@ -738,7 +829,7 @@ int sqo_records_quantize(int n, int dk, int dv, const uint8_t *bits, const int64
 /* Dequantize the records into S[n, dk, dv]. */
 int sqo_records_dequantize(int n, int dk, int dv, const uint8_t *bits, const int64_t *offs,
                            const uint8_t *base, float *S, const uint8_t *row_bits, int n_threads) {
-    if (check_bits(n, dk, bits, row_bits, NULL)) return -1;
+    if (check_bits(n, dk, bits, row_bits)) return -1;
     job_t J = {OP_DEQUANT, 0, dk, dv, 0, 0, bits, offs, (uint8_t *)base, S, NULL,
                NULL, NULL, NULL, NULL, NULL, NULL, NULL, row_bits};
     return run_rows(J, n, n_threads);
@@ -750,7 +841,7 @@ int sqo_records_step(int kda, int n, int dk, int dv, const uint8_t *bits, const 
                      uint8_t *base, const float *q, const float *k, const float *v,
                      const float *beta, const float *g, const float *imp,
                      const uint8_t *row_bits, double *y, int n_threads) {
-    if (check_bits(n, dk, bits, row_bits, imp)) return -1;
+    if (check_bits(n, dk, bits, row_bits)) return -1;
     job_t J = {OP_STEP, kda, dk, dv, 0, 0, bits, offs, base, NULL, NULL, q, k, v, beta, g, y,
                imp, row_bits};
     return run_rows(J, n, n_threads);

@@ -819,6 +819,163 @@ def test_kra_drivers_and_step_compose():
         assert np.array_equal(y[i], yw)
 
 
+# ------------------------------------------------------------------ key-row-aware fit, per-row widths
+def _width_pattern(rng, dk):
+    w = np.array([4] * (dk // 4) + [6] * (dk // 2) + [8] * (dk - dk // 4 - dk // 2), np.uint8)
+    return w[rng.permutation(dk)]
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_kra_rows_uniform_widths_is_the_uniform_fit(bits):
+    """Every row at the same width: the per-row fit returns the uniform fit's
+    codes and scales bit for bit (the widening factors are 1 and the clamp of
+    the range-covering codes never acts)."""
+    rng = np.random.default_rng(110 + bits)
+    S = _rand_state(rng, 32, 24)
+    S[rng.integers(0, 32, 4), rng.integers(0, 24, 4)] *= 40
+    imp = np.exp(rng.normal(0, 1.5, 32)).astype(np.float32)
+    a = O.quantize_kra(bits, S, imp)
+    b = O.quantize_kra_rows(np.full(32, bits, np.uint8), S, imp)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_kra_rows_each_row_spans_its_own_levels():
+    """Rows of comparable magnitude and impact at widths 4, 6 and 8: each
+    row's codes stay within its own range and reach close to its own qmax
+    (a fit that ignored the widths in the row factors would leave the 8-bit
+    rows on the 4-bit rows' coarse grid, or push 4-bit codes out of range)."""
+    rng = np.random.default_rng(121)
+    dk, dv = 48, 64
+    S = rng.standard_normal((dk, dv)).astype(np.float32)
+    imp = rng.uniform(0.8, 1.25, dk).astype(np.float32)
+    rb = _width_pattern(rng, dk)
+    Q, r, c = O.quantize_kra_rows(rb, S, imp)
+    qm = np.array([O.qmax(int(b)) for b in rb])
+    top = np.abs(Q).max(axis=1)
+    assert (top <= qm).all()
+    assert (top >= 0.6 * qm).all(), (top, qm)
+
+
+def test_kra_rows_duplicate_row_error_falls_with_width():
+    """The same row stored at 4, 6 and 8 bits (equal impact): the wider copy
+    reconstructs it with a smaller error, by roughly the ratio of the level
+    counts."""
+    rng = np.random.default_rng(131)
+    dk, dv = 24, 96
+    S = _rand_state(rng, dk, dv)
+    S[8] = S[0]
+    S[16] = S[0]
+    rb = np.array([4] * 8 + [6] * 8 + [8] * 8, np.uint8)
+    imp = np.ones(dk, np.float32)
+    Q, r, c = O.quantize_kra_rows(rb, S, imp)
+    R = O.dequantize(Q, r, c).astype(np.float64)
+    e = [((R[i] - S[i]) ** 2).sum() for i in (0, 8, 16)]
+    assert e[1] < e[0] / 4 and e[2] < e[1] / 4, e
+
+
+def test_kra_rows_fit_properties():
+    """Per-row level sets: (1) every code is the nearest level in
+    [-qmax_i, qmax_i] to S_ij / (r_i c_j) (brute force over each row's
+    levels); (2) against the range-covering codes P of the reading (c0_j =
+    max_i |x_ij| g_i / qref with x = S / r, P clamped to each row's range),
+    the fitted c_j minimises the impact-weighted error of P (a 1e-3
+    perturbation either way increases it); (3) the final weighted error is
+    never above that of (c0, P)."""
+    rng = np.random.default_rng(141)
+    dk, dv = 40, 24
+    S = _rand_state(rng, dk, dv)
+    S[rng.integers(0, dk, 5), rng.integers(0, dv, 5)] *= 30
+    imp = np.exp(rng.normal(0, 1.5, dk)).astype(np.float32)
+    rb = _width_pattern(rng, dk)
+    Q, r, c = O.quantize_kra_rows(rb, S, imp)
+    qm = np.array([O.qmax(int(b)) for b in rb], np.float64)
+    Sd = S.astype(np.float64)
+    x = Sd / r.astype(np.float64)[:, None]
+    t = x / c.astype(np.float64)[None, :]
+    for i in range(dk):
+        levels = np.arange(-qm[i], qm[i] + 1)
+        best = levels[np.abs(t[i][:, None] - levels).argmin(axis=-1)]
+        assert np.array_equal(Q[i], best), i
+    g = qm.max() / qm
+    c0 = (np.abs(x) * g[:, None]).max(axis=0) / qm.max()
+    P = np.clip(np.rint(x / c0[None, :]), -qm[:, None], qm[:, None])
+    w = imp.astype(np.float64) * r.astype(np.float64) ** 2
+
+    def err_s(cc, codes):
+        return (w[:, None] * (x - cc[None, :] * codes) ** 2).sum(axis=0)
+
+    base = err_s(c.astype(np.float64), P)
+    assert (err_s(c * (1 + 1e-3), P) > base).all()
+    assert (err_s(c * (1 - 1e-3), P) > base).all()
+    assert (_weighted_err(S, imp, Q, r, c) <= _weighted_err(S, imp, P, r, c0) * (1 + 1e-9)).all()
+
+
+def test_kra_rows_scale_and_permutation_invariance():
+    """S -> 4 S doubles r and c, imp -> 4 imp halves r and doubles c, with the
+    codes unchanged; permuting the key rows together with their widths and
+    impacts permutes the codes and row factors and keeps the column scales."""
+    rng = np.random.default_rng(151)
+    dk, dv = 32, 20
+    S = _rand_state(rng, dk, dv)
+    imp = rng.uniform(0.1, 5.0, dk).astype(np.float32)
+    rb = _width_pattern(rng, dk)
+    Q, r, c = O.quantize_kra_rows(rb, S, imp)
+    Q2, r2, c2 = O.quantize_kra_rows(rb, 4 * S, imp)
+    assert np.array_equal(Q2, Q) and np.array_equal(r2, 2 * r) and np.array_equal(c2, 2 * c)
+    Q3, r3, c3 = O.quantize_kra_rows(rb, S, 4 * imp)
+    assert np.array_equal(Q3, Q) and np.array_equal(r3, r / 2) and np.array_equal(c3, 2 * c)
+    p = rng.permutation(dk)
+    Q4, r4, c4 = O.quantize_kra_rows(rb[p], S[p], imp[p])
+    assert np.array_equal(Q4, Q[p]) and np.array_equal(r4, r[p])
+    assert np.allclose(c4, c, rtol=1e-6)
+
+
+def test_kra_rows_zero_rows_and_columns():
+    rng = np.random.default_rng(161)
+    S = _rand_state(rng, 8, 6)
+    S[3, :] = 0.0
+    S[:, 2] = 0.0
+    rb = np.array([4, 4, 6, 6, 6, 8, 8, 8], np.uint8)
+    Q, r, c = O.quantize_kra_rows(rb, S, rng.uniform(0.5, 2, 8).astype(np.float32))
+    assert r[3] == 0 and (Q[3] == 0).all() and c[2] == 0 and (Q[:, 2] == 0).all()
+    assert np.isfinite(O.dequantize(Q, r, c)).all()
+
+
+def test_kra_rows_drivers_and_step_compose():
+    """records_quantize / records_step on records with per-row widths and
+    impacts equal the single-head per-row fit and its packing; the step is
+    the step update on the codes, then that fit."""
+    rng = np.random.default_rng(171)
+    d = 16
+    rbs = np.stack([_width_pattern(rng, d) for _ in range(2)])
+    S = np.stack([_rand_state(rng, d, d) for _ in range(2)])
+    imp = rng.uniform(0.1, 4, (2, d)).astype(np.float32)
+    sizes = [O.record_bytes_rows(rbs[i], d) for i in range(2)]
+    offs = np.array([0, sizes[0]], np.int64)
+    base = np.zeros(sum(sizes), np.uint8)
+    b0 = np.zeros(2, np.uint8)
+    O.records_quantize(base, offs, b0, S, d, d, imp, rbs)
+    for i in range(2):
+        Q, r, c = O.quantize_kra_rows(rbs[i], S[i], imp[i])
+        assert np.array_equal(base[offs[i]:offs[i] + sizes[i]], O.record_pack_rows(rbs[i], Q, r, c))
+    x = [_inputs(rng, d, d, kda=True) for _ in range(2)]
+    q = np.stack([t[0] for t in x]).astype(np.float32)
+    k = np.stack([t[1] for t in x]).astype(np.float32)
+    v = np.stack([t[2] for t in x]).astype(np.float32)
+    beta = np.array([t[3] for t in x], np.float32)
+    g = np.log(np.stack([t[4] for t in x])).astype(np.float32)
+    before = base.copy()
+    y = O.records_step(True, base, offs, b0, d, d, q, k, v, beta, g, imp, rbs)
+    for i in range(2):
+        Q, r, c = O.record_unpack_rows(rbs[i], d, before[offs[i]:offs[i] + sizes[i]])
+        alpha = np.exp(g[i].astype(np.float64)).astype(np.float32)
+        Sp, yw = O.step_update(Q, r, c, alpha, q[i], k[i], v[i], beta[i])
+        Q2, r2, c2 = O.quantize_kra_rows(rbs[i], Sp, imp[i])
+        assert np.array_equal(base[offs[i]:offs[i] + sizes[i]], O.record_pack_rows(rbs[i], Q2, r2, c2))
+        assert np.array_equal(y[i], yw)
+
+
 # ------------------------------------------------------------------ per-key-row widths
 def test_rows_quantizer_selects_rows_of_uniform_quantizers():
     """With a width per key row, the column scales do not depend on the
@@ -897,5 +1054,3 @@ def test_rows_drivers_and_step_compose():
         assert np.array_equal(y[i], yw)
     with pytest.raises(ValueError):   # bits 0 needs row widths
         O.records_quantize(base, offs, bits, S, d, d)
-    with pytest.raises(ValueError):   # and takes no impact scores
-        O.records_quantize(base, offs, bits, S, d, d, imp=np.ones((3, d)), row_bits=row_bits)
