@@ -139,9 +139,9 @@ sq_status sq_pool_create(const sq_pool_desc *desc, void *dev_buf, size_t bytes, 
  * alike), which leaves every output unchanged.  Record of such a head: the
  * rows' code streams back to back (each row in the format of its width),
  * then r[d_k], c[d_v] fp32, padded to a multiple of 256 bytes.  Row i's
- * codes use the closed rule with its own qmax (r_i = max_j |s_ij| / qmax_i);
- * these heads do not take the key-row-aware fit (sq_pool_set_row_impact on
- * a pool with them returns SQ_EUNSUPPORTED).  Errors: SQ_EINVAL if a
+ * codes use the closed rule with its own qmax (r_i = max_j |s_ij| / qmax_i),
+ * or the key-row-aware fit with per-row levels (sq_pool_set_row_impact).
+ * Errors: SQ_EINVAL if a
  * width-0 head has no row_bits, SQ_EUNSUPPORTED for widths outside
  * {4, 6, 8}, decreasing widths or a change off the 8/16-row grid. */
 sq_status sq_pool_bytes_rows(const sq_pool_desc *desc, const uint8_t *row_bits, size_t *bytes);
@@ -166,7 +166,12 @@ sq_status sq_pool_layout(const sq_pool *pool, int64_t *slot_stride, int64_t *hea
  * impact[h][i], calibrated offline, sets the row factor
  * r_i = sqrt(max_j |S'_ij| / impact_i), and each column scale is fitted by one
  * impact-weighted least-squares step from the range-covering scale; entries go
- * to the nearest level, clamped to +-qmax.  The record format is unchanged.
+ * to the nearest level, clamped to +-qmax.  Heads with per-key-row widths
+ * keep each row's own levels +-qmax_i: with qref the head's largest qmax,
+ * row i's factor is widened by g_i = qref / qmax_i (fp32, 1 for the widest
+ * rows) and the range-covering scale is max_i (|s_ij| g_i) / qref, so every
+ * row spans its own levels on the shared column grid.  The record format is
+ * unchanged.
  *   impact: DEVICE pointer to fp32 [n_heads][d_k], 16-byte aligned, every
  *           value finite and > 0 (others give undefined but memory-safe
  *           codes); owned by the caller and read by every later launch on

@@ -234,8 +234,6 @@ sq_status sq_pool_layout(const sq_pool *pool, int64_t *slot_stride, int64_t *hea
 sq_status sq_pool_set_row_impact(sq_pool *pool, const float *impact) {
     if (!pool) return fail(SQ_EINVAL, "pool is NULL");
     if (impact && !aligned(impact, 16)) return fail(SQ_EINVAL, "impact is not 16-byte aligned");
-    if (impact && pool->row_mixed)
-        return fail(SQ_EUNSUPPORTED, "the key-row-aware fit takes heads of uniform width only");
     pool->view.impact = impact;
     return SQ_OK;
 }

@@ -685,24 +685,38 @@ template <int CG> __device__ __forceinline__ double pair_sum(double v) {
 //   Q_ij = nearest level of s_ij / c_j, clamped to [-qmax, qmax]
 // The FP64 sums run in one pass: each lane sums its 4 rows, lane pairs add
 // their two bands, and the A and B pair sums share the 32 KB partials
-// region (the LDS footprint of the closed rule).  c_j >= c0_j / 2 (a weighted average of s / P over |P| >= 1), so
+// region.  c_j >= c0_j / 2 (a weighted average of s / P over |P| >= 1), so
 // |s / c_j| <= 2 qmax and the magic-number rounding stays exact.
-template <int D, int BITS>
+// Per-key-row widths (MIXED, blog.ontle.kr allocation paragraph): row i
+// takes its own qmax_i; with qref the head's largest, its row factor is
+// widened by g_i = qref / qmax_i (fp32) and the range-covering scale is
+// c0_j = max_i (|s_ij| g_i) / qref, so each row spans its own levels on the
+// shared column grid; the final codes clamp to each row's range.  Rounding
+// errors keep |s ic0| <= qmax_i (1 + 4 eps) < qmax_i + 1/2, so P needs no
+// clamp.  With uniform widths g_i = 1 and this is the rule above.
+template <int D, int BITS, bool MIXED = false>
 __device__ __forceinline__ void kra_quantize_store(float (&x)[4][16], const float *imp,
-                                                   uint8_t *rec, float *lds) {
+                                                   uint8_t *rec, float *lds,
+                                                   Rows<D, BITS, MIXED> rows = {}) {
 #pragma clang fp contract(off)
     using G = Geo<D>;
-    constexpr int RB = D * BITS / 8;
-    constexpr int QM = (1 << (BITS - 1)) - 1;
-    constexpr float QMAX = (float)QM;
     constexpr float MAGIC = 12582912.0f; // 1.5 * 2^23
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     double *part64 = reinterpret_cast<double *>(lds);
     float *plane = lds; // column maxima; used (and reduced) before part64
     float *lds_c0 = lds + DecodeLds<D, true>::DIG_F + 2 * D; // digit rows: dead by now
     float *lds_ic = lds + DecodeLds<D, true>::IC_F;
-    float *rp = reinterpret_cast<float *>(rec + D * RB);
+    float *rp = reinterpret_cast<float *>(rec + rows.codes_bytes());
     float *cp = rp + D;
+    // the head's widest rows (widths never decrease along the rows)
+    const float QREF = rows.qmax(D - 1);
+    float gm[4]; // g of the lane's rows (wavefront-uniform: scalar registers)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        gm[m] = QREF / rows.qmax(band + G::NB * m);
+        if constexpr (MIXED)
+            gm[m] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gm[m])));
+    }
     // ---- row magnitudes, reduced over the band's lanes
     float mu[4];
 #pragma unroll
@@ -716,9 +730,10 @@ __device__ __forceinline__ void kra_quantize_store(float (&x)[4][16], const floa
     const float sel01 = (cg & 1) ? mu[1] : mu[0];
     const float sel23 = (cg & 1) ? mu[3] : mu[2];
     const float mrow = (cg & 2) ? sel23 : sel01;
-    const float im = imp[band + G::NB * (cg & 3)];
+    const int row_own = band + G::NB * (cg & 3);
+    const float im = imp[row_own];
     float r = 0.0f;
-    if (mrow >= FLT_MIN) r = sqrtf(mrow / im);
+    if (mrow >= FLT_MIN) r = sqrtf(mrow / im) * (QREF / rows.qmax(row_own));
     if (!(r >= FLT_MIN) || r == INFINITY) r = 0.0f;
     const float ir = r > 0.0f ? 1.0f / r : 0.0f;
     if (cg < 4) rp[band + G::NB * cg] = r;
@@ -742,13 +757,13 @@ __device__ __forceinline__ void kra_quantize_store(float (&x)[4][16], const floa
 #pragma unroll
             for (int n = 0; n < 16; ++n) {
                 x[m][n] = x[m][n] * irm[m];
-                cm[n] = fmaxf(cm[n], fabsf(x[m][n]));
+                cm[n] = fmaxf(cm[n], fabsf(x[m][n]) * gm[m]);
             }
         write_band_partials<D>(plane, cm);
     }
     __syncthreads();
     if (t < D) {
-        float c0 = column_max<D>(plane, t) / QMAX;
+        float c0 = column_max<D>(plane, t) / QREF;
         float ic0 = 0.0f;
         if (c0 >= FLT_MIN)
             ic0 = 1.0f / c0;
@@ -810,37 +825,44 @@ __device__ __forceinline__ void kra_quantize_store(float (&x)[4][16], const floa
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int row = band + G::NB * m;
+        uint32_t qm = (uint32_t)rows.qmax(row);
+        if constexpr (MIXED) qm = __builtin_amdgcn_readfirstlane(qm);
         uint32_t f[16];
 #pragma unroll
         for (int n = 0; n < 16; ++n)
-            f[n] = min(max(code_bits(x[m][n], ic[n]), MB - QM), MB + QM);
-        store_seg<BITS>(rec + row * RB + cg * (2 * BITS), pack_stream<BITS>(f));
+            f[n] = min(max(code_bits(x[m][n], ic[n]), MB - qm), MB + qm);
+        rows.store(rec, row, cg, f);
     }
 }
 
-template <int D, int BITS>
+template <int D, int BITS, bool MIXED = false>
 __device__ __forceinline__ void quant_tile_kra(uint8_t *rec, const float *S, const float *imp,
-                                               float *lds) {
+                                               float *lds, Rows<D, BITS, MIXED> rows = {}) {
     using G = Geo<D>;
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     float x[4][16];
 #pragma unroll
     for (int m = 0; m < 4; ++m) load16<D>(S + (band + G::NB * m) * D + 16 * cg, x[m]);
-    kra_quantize_store<D, BITS>(x, imp, rec, lds);
+    kra_quantize_store<D, BITS, MIXED>(x, imp, rec, lds, rows);
 }
 
-template <int D>
-__global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(4)))
-void quant_state_kra_kernel(PoolView pool, HeadTable tab,
-                                                                     const int32_t *slot,
-                                                                     const float *S) {
+// ROWS: the pool has heads with per-key-row widths (their own kernel, so that
+// the uniform bodies keep their register budget).
+template <int D, bool ROWS>
+__global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(ROWS ? 3 : 4)))
+void quant_state_kra_kernel(PoolView pool, HeadTable tab, const int32_t *slot, const float *S) {
     __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D, true>::TOTAL];
     int b, h;
     tile_bh(pool, blockIdx.x, b, h);
     uint8_t *rec = pool.base + (int64_t)slot[b] * pool.slot_stride + tab.off[h];
     const float *src = S + (int64_t)blockIdx.x * D * D;
     const float *imp = pool.impact + (int64_t)h * D;
-    switch (info_bits(tab.info[h])) {
+    const uint32_t info = tab.info[h];
+    switch (info_bits(info)) {
+    case 0:
+        if constexpr (ROWS)
+            quant_tile_kra<D, 8, true>(rec, src, imp, lds, {info_n4(info), info_n6(info)});
+        break;
     case 4: quant_tile_kra<D, 4>(rec, src, imp, lds); break;
     case 6: quant_tile_kra<D, 6>(rec, src, imp, lds); break;
     case 16: quant_tile_f16<D>(rec, src); break;
@@ -1027,7 +1049,6 @@ template <int D, int BITS, bool KDA, bool SPLIT, bool KRA, typename TI, typename
 __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const StepIO &io,
                                             const float *imp, float *lds,
                                             Rows<D, BITS, MIXED> rows = {}) {
-    static_assert(!(KRA && MIXED), "the key-row-aware fit takes uniform widths");
     using G = Geo<D>;
     using L = DecodeLds<D, KRA>;
     constexpr int NQ = D / 4;              // dwords per code column
@@ -1268,7 +1289,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     }
     __syncthreads();
     if constexpr (KRA) {
-        kra_quantize_store<D, BITS>(x, imp, rec, lds);
+        kra_quantize_store<D, BITS, MIXED>(x, imp, rec, lds, rows);
     } else {
         if (t < D) {
             // the 32 band partials of column t: its code dwords, 16 bytes at a
@@ -1425,9 +1446,10 @@ __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const St
 // each), which hides the loads, barriers and reduction phases of one tile
 // behind the others.  Four with the key-row-aware fit (its FP64 column sums
 // take 32 KB of LDS) and in pools with per-key-row widths (whose mixed-width
-// body needs more than 96 VGPRs without spilling).
+// body needs more than 96 VGPRs without spilling); three with both (about
+// 140 VGPRs).
 template <bool KRA, bool ROWS> constexpr int decode_waves_per_eu() {
-    return KRA || ROWS ? 4 : SQ_DECODE_WAVES;
+    return KRA && ROWS ? 3 : (KRA || ROWS ? 4 : SQ_DECODE_WAVES);
 }
 // ROWS: the pool has heads with per-key-row widths (their own kernel, so
 // that pools without them keep the register budget of the uniform bodies).
@@ -1458,8 +1480,8 @@ void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
     switch (info_bits(info)) {
     case 0:
         if constexpr (ROWS)
-            decode_tile<D, 8, KDA, SPLIT, false, TI, TO, true>(rec, tile, io, nullptr, lds,
-                                                               {info_n4(info), info_n6(info)});
+            decode_tile<D, 8, KDA, SPLIT, KRA, TI, TO, true>(rec, tile, io, imp, lds,
+                                                             {info_n4(info), info_n6(info)});
         break;
     case 4: decode_tile<D, 4, KDA, SPLIT, KRA, TI, TO>(rec, tile, io, imp, lds); break;
     case 6: decode_tile<D, 6, KDA, SPLIT, KRA, TI, TO>(rec, tile, io, imp, lds); break;
@@ -1618,12 +1640,18 @@ hipError_t launch_quant_state(const PoolView &pool, const HeadTable &tab, const 
                               int32_t n, const float *S, hipStream_t stream) {
     const dim3 grid((unsigned)n * (unsigned)pool.n_heads);
     if (pool.impact) {
-        if (pool.d == 128)
-            hipLaunchKernelGGL(quant_state_kra_kernel<128>, grid, dim3(Geo<128>::NT), 0, stream, pool,
-                               tab, slot, S);
+        if (pool.d == 128 && pool.row_mixed)
+            hipLaunchKernelGGL((quant_state_kra_kernel<128, true>), grid, dim3(Geo<128>::NT), 0,
+                               stream, pool, tab, slot, S);
+        else if (pool.d == 128)
+            hipLaunchKernelGGL((quant_state_kra_kernel<128, false>), grid, dim3(Geo<128>::NT), 0,
+                               stream, pool, tab, slot, S);
+        else if (pool.row_mixed)
+            hipLaunchKernelGGL((quant_state_kra_kernel<64, true>), grid, dim3(Geo<64>::NT), 0,
+                               stream, pool, tab, slot, S);
         else
-            hipLaunchKernelGGL(quant_state_kra_kernel<64>, grid, dim3(Geo<64>::NT), 0, stream, pool,
-                               tab, slot, S);
+            hipLaunchKernelGGL((quant_state_kra_kernel<64, false>), grid, dim3(Geo<64>::NT), 0,
+                               stream, pool, tab, slot, S);
     } else if (pool.d == 128) {
         hipLaunchKernelGGL(quant_state_kernel<128>, grid, dim3(Geo<128>::NT), 0, stream, pool, tab, slot, S);
     } else {
@@ -1645,8 +1673,9 @@ hipError_t launch_dequant_state(const PoolView &pool, const HeadTable &tab, cons
 hipError_t launch_decode(const PoolView &pool, const HeadTable &tab, const StepIO &io,
                          hipStream_t stream) {
     // a pool with row-impact scores requantizes with the key-row-aware fit
-    // (such pools have no per-key-row widths)
-    if (pool.impact) return decode_gate_dispatch<false, true, false>(pool, tab, io, stream);
+    if (pool.impact)
+        return pool.row_mixed ? decode_gate_dispatch<false, true, true>(pool, tab, io, stream)
+                              : decode_gate_dispatch<false, true, false>(pool, tab, io, stream);
     return pool.row_mixed ? decode_gate_dispatch<false, false, true>(pool, tab, io, stream)
                           : decode_gate_dispatch<false, false, false>(pool, tab, io, stream);
 }

@@ -255,8 +255,9 @@ def test_per_row_width_layout(d):
     try:
         st, ho, rb = Q.sq_pool_layout(h, 3)
         assert rb == want and ho == [0, want[0], want[0] + want[1]] and st == sum(want)
-        # the key-row-aware fit takes uniform widths only
-        _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_set_row_impact, h, FAKE_DEV, text="uniform width")
+        # the key-row-aware fit also takes heads with per-key-row widths (no
+        # compute call here: setting and clearing the scores only)
+        Q.sq_pool_set_row_impact(h, FAKE_DEV)
         Q.sq_pool_set_row_impact(h, None)
     finally:
         Q.sq_pool_destroy(h)

@@ -982,6 +982,92 @@ def test_rows_kda_trajectory_256_steps():
     assert err <= Hn.STATE_REL_L2
 
 
+# ----------------------------------------------------------------- key-row-aware fit, per-key-row widths
+@pytest.mark.parametrize("d", [64, 128])
+def test_kra_rows_quant_state_matches_oracle(d):
+    """sq_quant_state with row-impact scores on a pool whose heads mix
+    per-key-row widths, uniform widths and FP16 pivots: the per-row fit,
+    against the oracle's."""
+    log("kra rows quant d=%d" % d)
+    rng = np.random.default_rng(170 + d)
+    H, B = 5, 4
+    bits = [0, 6, 0, 16, 8]
+    wl = W.custom("kda", B, H, d, bits, n_slots=6, permute=True, seed=13,
+                  row_bits=_row_widths(H, d, 170 + d))
+    side = Side(wl, wl.layers[0], wide_impact(H, d, d + 1))
+    S = (rng.standard_normal((B, H, d, d)) * np.exp(rng.standard_normal((B, H, d, 1)))
+         * np.exp(rng.standard_normal((B, H, 1, d)))).astype(np.float32)
+    S[0, 0] = 0.0
+    S[1, 2, 5, :] = 0.0
+    S[2, 0, :, 3] = 0.0
+    S[3, 2, 3, :4] *= 200.0                        # isolated outliers
+    side.gpu.quant_state(side.slot_dev, to_dev(S))
+    rows = Hn.rows_all(B, H)
+    offs, hb = side.rows_offsets(rows)
+    O.records_quantize(side.host.bytes, offs, hb, S.reshape(-1, d, d), d, d,
+                       side.rows_imp(rows), side.rows_row_bits(rows))
+    check_records(side, rows, side.gpu_pool(), "kra rows quant")
+
+
+@pytest.mark.parametrize("case", [
+    ("kda", 3, 4, 128, [0, 6, 0, 16], "bf16", 5),
+    ("kda", 3, 3, 64, [0, 0, 8], "f32", 4),
+    ("gdn", 2, 3, 128, [0, 4, 0], "bf16", 3),
+])
+def test_kra_rows_decode_step_small_full_compare(case):
+    """Three fused steps with the key-row-aware fit on heads with per-key-row
+    widths: every record and y against the oracle, spare slots untouched."""
+    gate, B, H, d, bits, dtype, n_slots = case
+    log("kra rows step %s" % (case,))
+    wl = W.custom(gate, B, H, d, bits, dtype=dtype, n_slots=n_slots, permute=True, seed=14,
+                  row_bits=_row_widths(H, d, B + 40))
+    side = Side(wl, wl.layers[0], wide_impact(H, d, B + 40))
+    side.gpu.buf.fill_(0xA5)
+    side.host.bytes[:] = 0xA5
+    rows = Hn.rows_all(B, H)
+    side.init_oracle_rows(rows)
+    for t in range(3):
+        side.push_rows(rows)
+        y_gpu, y_ref = side.step(t, rows)
+        pool = side.gpu_pool()
+        check_records(side, rows, pool, "kra rows step %d" % t)
+        assert Hn.rel_l2(y_gpu, y_ref) <= Hn.Y_REL_L2, t
+        used = np.zeros(pool.size, bool)
+        for sl in side.layer.slot_of:
+            used[sl * side.host.stride:(sl + 1) * side.host.stride] = True
+        assert (pool[~used] == 0xA5).all()
+
+
+def test_kra_rows_kda_trajectory_256_steps():
+    """KDA with per-key-row widths 4/6/8 at 25/50/25 % and the key-row-aware
+    fit with calibrated scores: 256 steps within the trajectory bound of the
+    oracle."""
+    log("kra rows kda trajectory")
+    base = W.make("c2")
+    H, d = base.H, base.d
+    g = 8
+    w = np.array([4] * (4 * g) + [6] * (d - 8 * g) + [8] * (4 * g), np.uint8)
+    wl = W.custom("kda", base.B, H, d, [0] * H, dtype="bf16", n_slots=base.n_slots,
+                  permute=True, seed=base.seed, row_bits=np.tile(w, (H, 1)))
+    layer = wl.layers[0]
+    side = Side(wl, layer, calibrated_impact(wl, layer))
+    side.gpu_warmup_all()
+    rows = sample_rows(wl.B, wl.H, 32, seed=4)
+    side.init_oracle_rows(rows)
+    worst_y = 0.0
+    for t in range(256):
+        y_gpu, y_ref = side.step(t, rows)
+        worst_y = max(worst_y, Hn.rel_l2(y_gpu, y_ref))
+    offs, hb = side.rows_offsets(rows)
+    rb = side.rows_row_bits(rows)
+    s_gpu = O.records_dequantize(side.gpu_pool(), offs, hb, d, d, row_bits=rb)
+    s_ref = O.records_dequantize(side.host.bytes, offs, hb, d, d, row_bits=rb)
+    err = Hn.rel_l2(s_gpu, s_ref)
+    log("kra rows kda: worst y rel-L2 %.3g, final state rel-L2 %.3g" % (worst_y, err))
+    assert worst_y <= Hn.Y_REL_L2
+    assert err <= Hn.STATE_REL_L2
+
+
 # ----------------------------------------------------------------- limits
 @pytest.mark.parametrize("gate", ["gdn", "kda"])
 @pytest.mark.parametrize("H", [64, 61])
