@@ -24,16 +24,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# Vector-ALU issue peak of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one
-# (non-packed) lane operation per lane per cycle; a wave64 instruction holds a
-# SIMD for 4 cycles.  In T lane-ops/s.
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Vector-ALU issue of MI355X: 256 CUs x 4 SIMDs, 2.4 GHz.  A wave64
+# instruction holds its SIMD for 2 cycles (fp32 add, mul and FMA; and, xor,
+# add_u32, bitop3, mov) or 4 cycles (max / med3, conversions, shifts,
+# bit-field extract, funnel shift, permute, FP64), as measured on MI355X with
+# independent chains of one opcode over the whole chip.
+SIMD_CYCLES_PER_S = 256 * 4 * 2.4e9
 # Per state element, the vector operations the fused step cannot avoid once
-# the look-up and read-out sums run on the matrix cores: extract the code,
-# widen it, form (a r_i) c_j and k_i u_j, the update FMA, the column and row
-# maxima (half of a max3 each), s = S' / c', the rounding FMA and the pack.
-# Extract and pack cost 1.06 and 1.1 for 6-bit codes (fields straddle words).
-ESSENTIAL_VALU_PER_ELEMENT = {4: 9.0, 6: 9.16, 8: 9.0, 16: 9.0}
+# the look-up and read-out sums run on the matrix cores, and their SIMD
+# cycles per 64 elements: extract the code (4; 6-bit fields that straddle
+# words add 1/16), widen it (4), form (a r_i) c_j and k_i u_j (2 + 2), the
+# update FMA (2), the column and row maxima (half a max3 each: 2 + 2),
+# s = S' / c' (2), the rounding FMA (2) and the pack (4, 6-bit + 1/16).
+# 8-bit codes need a shift for only half of the bytes (extract 2).
+ESSENTIAL_VALU_PER_ELEMENT = {4: 9.0, 6: 9.125, 8: 8.5, 16: 9.0}
+ESSENTIAL_CYCLES_PER_64 = {4: 26.0, 6: 26.5, 8: 24.0, 16: 26.0}
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_B512_H48_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "quantized_gated_delta_amd", "csrc", "sq_kernels.hip")
 
@@ -101,10 +106,11 @@ def main():
                     help="FP16 pivot heads per layer for the --allocate comparison")
     ap.add_argument("--calib", type=int, default=256,
                     help="requests whose warm-up states calibrate the allocation")
-    ap.add_argument("--only", choices=("kda_mixed", "kda_rows", "kra"),
+    ap.add_argument("--only", choices=("kda_mixed", "kda_rows", "kra", "kda_rows_kra"),
                     help="time only this variant of the B=512 H=48 step (for profiling runs): "
-                         "KDA 4/6/8 per head, KDA with per-key-row widths, or the key-row-aware "
-                         "fit on the 6-bit GDN pool; prints one short JSON line")
+                         "KDA 4/6/8 per head, KDA with per-key-row widths, the key-row-aware "
+                         "fit on the 6-bit GDN pool, or that fit on the per-key-row widths; "
+                         "prints one short JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -209,7 +215,8 @@ def main():
     def kda_setup(per_row):
         """KDA at the c3 shape: bits 4/6/8 at 25/50/25 % per head, or 4/6/8 on
         25/50/25 % of every head's key rows; pool quantized from the warm-up
-        state.  Returns (pool, run function, algorithmic bytes per step)."""
+        state.  Returns (pool, run function, algorithmic bytes per step,
+        workload, layer)."""
         wk = W.custom("kda", B, H, d, W.mixed_bits(0, 0, H), dtype="bf16",
                       n_slots=wl.n_slots, permute=True, seed=0, name="kda_mixed")
         lk = wk.layers[0]
@@ -235,7 +242,7 @@ def main():
                 pk.decode_step(sk, x["q"], x["k"], x["v"], x["beta"], x["g"], y)
                 if ev is not None:
                     ev[i][1].record(stream)
-        return pk, run_k, kb
+        return pk, run_k, kb, wk, lk
 
     if args.only:
         if args.only == "kra":
@@ -243,7 +250,9 @@ def main():
             o_ms, o_launch = timed(pool, slot)
             ob = algo_bytes_per_step(B, H, d, layer.head_bits, layer.gate)
         else:
-            pk, run_k, ob = kda_setup(args.only == "kda_rows")
+            pk, run_k, ob, wk, lk = kda_setup(args.only != "kda_mixed")
+            if args.only == "kda_rows_kra":
+                pk.set_row_impact(torch.from_numpy(impact_from_workload(wk, lk, 4)).to(dev))
             o_ms, o_launch = timed(None, None, run_k)
         print(json.dumps({"variant": args.only, "us_per_step": o_ms * 1e3,
                           "us_per_launch": o_launch * 1e3, "algo_bytes_per_step": ob,
@@ -313,7 +322,7 @@ def main():
             eprint("mixed 4/8: %.2f us/step, %.1f GB/s" % (b_ms * 1e3, variants["mixed_4_8_halflife"]["achieved_GBps"]))
             pool_b.close()
             # KDA (per-key-channel gate) at the same shape, bits 4/6/8 at 25/50/25 %
-            pool_k, run_k, kb = kda_setup(False)
+            pool_k, run_k, kb, _, _ = kda_setup(False)
             k_ms, k_launch = timed(None, None, run_k)
             variants["kda_mixed_4_6_8"] = {
                 "updates_per_s": updates / (k_ms * 1e-3), "us_per_step": k_ms * 1e3,
@@ -324,7 +333,7 @@ def main():
             pool_k.close()
             # the same KDA step with per-key-row widths: 4/6/8 bits on 25/50/25 %
             # of every head's key rows (the KDA unit of the allocation)
-            pool_r, run_r, pb = kda_setup(True)
+            pool_r, run_r, pb, wk, lk = kda_setup(True)
             p_ms, p_launch = timed(None, None, run_r)
             variants["kda_per_row_4_6_8"] = {
                 "updates_per_s": updates / (p_ms * 1e-3), "us_per_step": p_ms * 1e3,
@@ -333,6 +342,16 @@ def main():
                 "hbm_frac": pb / (p_launch * 1e-3) / 1e9 / HBM_PEAK_GBS}
             eprint("kda per-row widths: %.2f us/step, %.1f GB/s"
                    % (p_ms * 1e3, variants["kda_per_row_4_6_8"]["achieved_GBps"]))
+            # the same pool with the key-row-aware fit (scores from warm-up inputs)
+            pool_r.set_row_impact(torch.from_numpy(impact_from_workload(wk, lk, 4)).to(dev))
+            pk_ms, pk_launch = timed(None, None, run_r)
+            variants["kda_per_row_4_6_8_key_row_aware"] = {
+                "updates_per_s": updates / (pk_ms * 1e-3), "us_per_step": pk_ms * 1e3,
+                "us_per_launch": pk_launch * 1e3, "algo_bytes_per_step": pb,
+                "achieved_GBps": pb / (pk_launch * 1e-3) / 1e9,
+                "hbm_frac": pb / (pk_launch * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            eprint("kda per-row widths, key-row-aware fit: %.2f us/step, %.1f GB/s"
+                   % (pk_ms * 1e3, pb / (pk_launch * 1e-3) / 1e9))
             pool_r.close()
     del state
     copy_GBps, torch_copy_GBps = device_copy_GBps(dev)
@@ -358,7 +377,11 @@ def main():
     elems = B * H * d * d
     hb = [int(b) for b in layer.head_bits]
     ess = sum(ESSENTIAL_VALU_PER_ELEMENT[b] for b in hb) / len(hb)
+    cyc = sum(ESSENTIAL_CYCLES_PER_64[b] for b in hb) / len(hb)
+    # lane-operations per second: achieved (essential work over the launch
+    # time) and the issue limit of the same operation mix
     alu_achieved = ess * elems / (ms_launch * 1e-3) / 1e12
+    alu_peak = ess * 64 / cyc * SIMD_CYCLES_PER_S / 1e12
 
     out = {
         "metric": "state-updates/s (req x head x step) and achieved HBM GB/s vs peak at B=512",
@@ -380,12 +403,14 @@ def main():
                                  "combined in f64, u rounded once to f32; update and "
                                  "requantizer in f32",
                    "gate": layer.gate},
-        "roofline": {"bound": "alu", "achieved": alu_achieved, "peak": VALU_PEAK_TOPS,
-                     "unit": "T lane-ops/s", "frac": alu_achieved / VALU_PEAK_TOPS,
+        "roofline": {"bound": "alu", "achieved": alu_achieved, "peak": alu_peak,
+                     "unit": "T lane-ops/s", "frac": alu_achieved / alu_peak,
                      "traffic": None if prof is None else prof["bytes_per_launch"],
-                     "essential_valu_per_element": ess, "state_elements_per_launch": elems,
+                     "essential_valu_per_element": ess,
+                     "essential_simd_cycles_per_64_elements": cyc,
+                     "state_elements_per_launch": elems,
                      "valu_insts_per_element": None if prof is None else prof["valu_insts_per_element"],
-                     "valu_issue_frac": None if prof is None else prof["valu_issue_frac"],
+                     "valu_issue_frac_at_4_cycles": None if prof is None else prof["valu_issue_frac"],
                      "us_per_launch": ms_launch * 1e3,
                      "kernel": "decode_kernel<128, %s, bf16, bf16>" % layer.gate.upper(),
                      "hbm": {"achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -1250,6 +1250,13 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
         // the lane's 16 {c, u} pairs: 8 aligned 16-byte reads (stride 18 pairs
         // per column group: 4 cg + 2 n mod 32 words, no bank conflicts)
         const float4 *cu4 = reinterpret_cast<const float4 *>(lds_cu + 18 * cg);
+        // all 16 code dwords are read before the first partial overwrites one
+        // (the compiler cannot tell the addresses apart, so reads placed after
+        // a write would each wait for the LDS round trip)
+        uint32_t cws[16];
+#pragma unroll
+        for (int n = 0; n < 16; ++n)
+            cws[n] = *reinterpret_cast<const uint32_t *>(code_b + cbase[n & 7] + 4 * n * NQ);
 #pragma unroll
         for (int n4 = 0; n4 < 4; ++n4) {
             const float4 p01 = cu4[2 * n4], p23 = cu4[2 * n4 + 1];
@@ -1259,7 +1266,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
             for (int i = 0; i < 4; ++i) {
                 const int n = 4 * n4 + i;
                 uint32_t *cwp = reinterpret_cast<uint32_t *>(code_b + cbase[n & 7] + 4 * n * NQ);
-                const uint32_t cw = *cwp;
+                const uint32_t cw = cws[n];
                 const float2 cu = cup[i];
                 float cm = 0.0f;
 #pragma unroll
