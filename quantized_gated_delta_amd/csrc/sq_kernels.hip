@@ -256,7 +256,7 @@ template <int D, int BITS, bool MIXED> struct Rows {
     // r[] of the same record (which the same workgroup only writes later).
     __device__ __forceinline__ Seg<8> load_raw(const uint8_t *rec, int row, int cg) const {
         Seg<8> s;
-        load_words_nt<4>(rec + offset(row) + cg * (2 * width(row)), s.w);
+        load_words_nt<4>(rec + (uint32_t)(offset(row) + cg * (2 * width(row))), s.w);
         return s;
     }
     __device__ __forceinline__ Seg<8> widen(const Seg<8> &raw, int row) const {
@@ -275,7 +275,9 @@ template <int D, int BITS, bool MIXED> struct Rows {
     }
     __device__ __forceinline__ Seg<BITS> load(const uint8_t *rec, int row, int cg) const {
         if constexpr (!MIXED) {
-            return load_seg<BITS>(rec + offset(row) + cg * (2 * BITS));
+            // unsigned 32-bit offsets: the load takes the record's (scalar)
+            // base directly
+            return load_seg<BITS>(rec + (uint32_t)(offset(row) + cg * (2 * BITS)));
         } else {
             return widen(load_raw(rec, row, cg), row);
         }
@@ -929,9 +931,9 @@ __device__ __forceinline__ void load_tile(TileIn &in, int tile, uint8_t *rec, co
     in.cj = rp[D + jl];
     in.vj = ld<TI>(reinterpret_cast<const TI *>(io.v) + row_io * D, jl);
     const int rowf = band + G::NB * (cg & 3);
-    in.fk = ld<TI>(k, rowf);
-    in.fq = ld<TI>(q, rowf);
-    in.fr = rp[rowf];
+    in.fk = ld<TI>(k, (uint32_t)rowf);
+    in.fq = ld<TI>(q, (uint32_t)rowf);
+    in.fr = rp[(uint32_t)rowf];
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) {
         const int row = (t & 63) + 64 * i;
@@ -985,6 +987,15 @@ template <int CTRL, int ROW_MASK> __device__ __forceinline__ uint32_t dpp_rows(u
     // fold below, which adds 0 for them)
     return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+    v = max(v, dpp_u<kQuadXor1>(v));
+    v = max(v, dpp_u<kQuadXor2>(v));
+    v = max(v, dpp_u<kHalfMirror>(v));
+    v = max(v, dpp_u<kRowMirror>(v));
+    v = max(v, dpp_rows<kRowBcast15, 0xA>(v));
+    v = max(v, dpp_rows<kRowBcast31, 0xC>(v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
 __device__ __forceinline__ int wave_max_i(int v) {
     v = max(v, (int)dpp_u<kQuadXor1>((uint32_t)v));
     v = max(v, (int)dpp_u<kQuadXor2>((uint32_t)v));
@@ -1006,11 +1017,6 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
     const float b31 = __uint_as_float(dpp_rows<kRowBcast31, 0xC>(__float_as_uint(v)));
     v = (lane & 32) ? v + b31 : v;
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-// Biased binary exponent of an FP64 value (0 for zero and subnormals).
-__device__ __forceinline__ int exp_field(double x) {
-    return (int)((__double_as_longlong(x) >> 52) & 0x7FF);
 }
 
 // Signed base-256 digits d_0..d_7 of an integer-valued X, |X| < 2^62: the
@@ -1141,24 +1147,42 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
         fx[jb] = x;
     }
     // ---- the tile's exponents, computed by every wave over all D rows (no
-    //      exchange between waves): Ek >= the biased exponent of every k
-    //      factor, Eq of every q factor.  GDN: exactly the largest.  KDA: the
-    //      gate enters through a bound, a_i = exp(g_i) < 2^(ceil(g_i log2 e)
-    //      + 1), which can only make E larger, and a larger E only drops
-    //      bits far below the 53 the look-up needs (|X| < 2^62).  And k.q.
-    int ek = 0, eq = 0;
+    //      exchange between waves): Ek >= the biased FP64 exponent of every k
+    //      factor, Eq of every q factor, from the fp32 exponent fields e(.)
+    //      of k (or q) and r: |k r| < 2^(e(k) + e(r) - 252) (zero and
+    //      subnormal fields 0 included), so the FP64 field of k r is at most
+    //      e(k) + e(r) + 770, at most one above the exact one.  The fields
+    //      are added in place (bits 23..31) and shifted once after the
+    //      reduction.  KDA: the gate enters through a bound, a_i = exp(g_i) <
+    //      2^(ceil(g_i log2 e) + 1).  A larger E only drops bits far below
+    //      the 53 the look-up needs (|X| < 2^62).  And k.q.
+    constexpr uint32_t EXPM = 0x7F800000u;
+    int Ek, Eq;
     float kq = 0.0f;
+    if constexpr (KDA) {
+        int ek = 0, eq = 0;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) {
-        const double kr = (double)cur.kb[i] * (double)cur.rb[i];
-        const double qr = (double)cur.qb[i] * (double)cur.rb[i];
-        int ea = 0;
-        if constexpr (KDA) ea = (int)ceilf(cur.gb[i] * 1.44269504f) + 2;
-        ek = max(ek, exp_field(kr) + ea);
-        eq = max(eq, exp_field(qr) + ea);
-        kq = fmaf(cur.kb[i], cur.qb[i], kq);
+        for (int i = 0; i < D / 64; ++i) {
+            const uint32_t er = __float_as_uint(cur.rb[i]) & EXPM;
+            const int ea = (int)ceilf(cur.gb[i] * 1.44269504f) + 2;
+            ek = max(ek, (int)(((__float_as_uint(cur.kb[i]) & EXPM) + er) >> 23) + ea);
+            eq = max(eq, (int)(((__float_as_uint(cur.qb[i]) & EXPM) + er) >> 23) + ea);
+            kq = fmaf(cur.kb[i], cur.qb[i], kq);
+        }
+        Ek = wave_max_i(ek) + 770;
+        Eq = wave_max_i(eq) + 770;
+    } else {
+        uint32_t ek = 0, eq = 0;
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {
+            const uint32_t er = __float_as_uint(cur.rb[i]) & EXPM;
+            ek = max(ek, (__float_as_uint(cur.kb[i]) & EXPM) + er);
+            eq = max(eq, (__float_as_uint(cur.qb[i]) & EXPM) + er);
+            kq = fmaf(cur.kb[i], cur.qb[i], kq);
+        }
+        Ek = (int)(wave_max_u(ek) >> 23) + 770;
+        Eq = (int)(wave_max_u(eq) >> 23) + 770;
     }
-    const int Ek = wave_max_i(ek), Eq = wave_max_i(eq);
     kq = wave_sum_dpp(kq);
     // ---- digit rows: the k factors as integers X_i = rint(x_i 2^(61 - e)) on
     //      the tile's exponent e (|X| < 2^62, 8 digits, rows 0..7); the q
