@@ -670,7 +670,7 @@ def trajectory(args, dev):
             kra = {"uniform_6_key_row_aware",
                    "lifetime_6+%d_fp16_pivots_key_row_aware" % args.pivots}
             imp = torch.from_numpy(impact_from_workload(wl, layer, 16)).to(dev)
-        perms, row_bits = {}, {}
+        perms, row_bits, imp_of = {}, {}, {}
         if args.allocate and kda:
             # per-key-row widths (the KDA unit): key channels permuted offline
             # so each head's rows run from the fastest- to the slowest-decaying
@@ -680,6 +680,14 @@ def trajectory(args, dev):
             schemes[name] = np.zeros(H, np.uint8)
             row_bits[name] = rb
             perms[name] = torch.from_numpy(perm).to(dev)
+            # the same rows with the key-row-aware fit (scores permuted with
+            # the key channels)
+            name_k = "per_row_lifetime_4_6_8_key_row_aware"
+            schemes[name_k] = np.zeros(H, np.uint8)
+            row_bits[name_k] = rb
+            perms[name_k] = perms[name]
+            kra.add(name_k)
+            imp_of[name_k] = torch.gather(imp, 1, perms[name].long())
             # per-row widths chosen by the lifetime objective (R22-R23 at the
             # key-row unit): per-row distortion of the calibration states,
             # per-row lifetime weights from the warm-up log-gates
@@ -694,7 +702,7 @@ def trajectory(args, dev):
             pool = Q.StatePool(B, H, d, [int(b) for b in hb], layer.gate, device=dev,
                                row_bits=row_bits.get(name))
             if name in kra:
-                pool.set_row_impact(imp)
+                pool.set_row_impact(imp_of.get(name, imp).contiguous())
             if name in perms:
                 idx = perms[name][None, :, :, None].expand(B, H, d, d)
                 pool.quant_state(ident, torch.gather(state, 2, idx).contiguous())
