@@ -24,21 +24,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# Vector-ALU issue of MI355X: 256 CUs x 4 SIMDs, 2.4 GHz.  A wave64
-# instruction holds its SIMD for 2 cycles (fp32 add, mul and FMA; and, xor,
-# add_u32, bitop3, mov) or 4 cycles (max / med3, conversions, shifts,
-# bit-field extract, funnel shift, permute, FP64), as measured on MI355X with
-# independent chains of one opcode over the whole chip.
-SIMD_CYCLES_PER_S = 256 * 4 * 2.4e9
 # Per state element, the vector operations the fused step cannot avoid once
-# the look-up and read-out sums run on the matrix cores, and their SIMD
-# cycles per 64 elements: extract the code (4; 6-bit fields that straddle
-# words add 1/16), widen it (4), form (a r_i) c_j and k_i u_j (2 + 2), the
-# update FMA (2), the column and row maxima (half a max3 each: 2 + 2),
-# s = S' / c' (2), the rounding FMA (2) and the pack (4, 6-bit + 1/16).
-# 8-bit codes need a shift for only half of the bytes (extract 2).
-ESSENTIAL_VALU_PER_ELEMENT = {4: 9.0, 6: 9.125, 8: 8.5, 16: 9.0}
-ESSENTIAL_CYCLES_PER_64 = {4: 26.0, 6: 26.5, 8: 24.0, 16: 26.0}
+# the look-up and read-out sums run on the matrix cores, by opcode class:
+# extract the code (bit-field extract; at 6 bits 1/16 more for fields that
+# straddle words, at 8 bits a shift for half of the bytes), widen it (byte to
+# fp32), three products ((a r_i) c_j, k_i u_j and s = S' / c'), two FMAs (the
+# update and the rounding), one max3 (half for the column and half for the
+# row maxima, two new values each) and the pack (funnel shift; 1/16 more at
+# 6 bits).  The ALU roofline prices them at the issue rates sq_issue_probe
+# measures for each class on this GPU.
+def essential_mix(bits):
+    ext = {4: 1.0, 6: 1.0625, 8: 0.5}.get(bits, 1.0)
+    pack = {6: 1.0625}.get(bits, 1.0)
+    return {"bfe": ext, "cvt": 1.0, "mul": 3.0, "fma": 2.0, "max3": 1.0, "alignbit": pack}
+
+
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_B512_H48_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "quantized_gated_delta_amd", "csrc", "sq_kernels.hip")
 
@@ -357,6 +357,8 @@ def main():
     copy_GBps, torch_copy_GBps = device_copy_GBps(dev)
     eprint("device copy: %.0f GB/s (streaming kernel), %.0f GB/s (torch copy)"
            % (copy_GBps, torch_copy_GBps))
+    rates = issue_rates(dev)
+    eprint("issue rates (T lane-ops/s): " + ", ".join("%s %.1f" % kv for kv in rates.items()))
     if not args.no_variants:
         variants["smaller_configs"] = config_timings(dev)
 
@@ -376,12 +378,16 @@ def main():
             prof = cp["variants"].get(args.workload)
     elems = B * H * d * d
     hb = [int(b) for b in layer.head_bits]
-    ess = sum(ESSENTIAL_VALU_PER_ELEMENT[b] for b in hb) / len(hb)
-    cyc = sum(ESSENTIAL_CYCLES_PER_64[b] for b in hb) / len(hb)
+    mix = {}
+    for b in hb:
+        for k, v in essential_mix(b).items():
+            mix[k] = mix.get(k, 0.0) + v / len(hb)
+    ess = sum(mix.values())
     # lane-operations per second: achieved (essential work over the launch
-    # time) and the issue limit of the same operation mix
+    # time) and the issue limit of the same operation mix at the measured
+    # per-class rates
     alu_achieved = ess * elems / (ms_launch * 1e-3) / 1e12
-    alu_peak = ess * 64 / cyc * SIMD_CYCLES_PER_S / 1e12
+    alu_peak = ess / sum(n / rates[k] for k, n in mix.items())
 
     out = {
         "metric": "state-updates/s (req x head x step) and achieved HBM GB/s vs peak at B=512",
@@ -407,7 +413,8 @@ def main():
                      "unit": "T lane-ops/s", "frac": alu_achieved / alu_peak,
                      "traffic": None if prof is None else prof["bytes_per_launch"],
                      "essential_valu_per_element": ess,
-                     "essential_simd_cycles_per_64_elements": cyc,
+                     "essential_mix_per_element": mix,
+                     "issue_rates_T_lane_ops_per_s": rates,
                      "state_elements_per_launch": elems,
                      "valu_insts_per_element": None if prof is None else prof["valu_insts_per_element"],
                      "valu_issue_frac_at_4_cycles": None if prof is None else prof["valu_issue_frac"],
@@ -454,6 +461,33 @@ def device_copy_GBps(dev, nbytes=2 << 30, reps=10):
     tc = rate(lambda: b.copy_(a))
     del a, b
     return own, tc
+
+
+def issue_rates(dev, reps=4):
+    """Issue rate of each opcode class of the decode step's per-element work
+    (the library's sq_issue_probe: independent chains of one opcode over the
+    whole chip), timed with HIP events on the launch stream.  Returns
+    {class: T lane-operations per second}."""
+    import torch
+
+    import quantized_gated_delta_amd as Q
+    classes = {"fma": Q.SQ_PROBE_FMA_F32, "mul": Q.SQ_PROBE_MUL_F32,
+               "max3": Q.SQ_PROBE_MAX3_F32, "cvt": Q.SQ_PROBE_CVT_BYTE,
+               "bfe": Q.SQ_PROBE_BFE, "alignbit": Q.SQ_PROBE_ALIGNBIT,
+               "fma_f64": Q.SQ_PROBE_FMA_F64}
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, op in classes.items():
+        Q.sq_issue_probe(op, sink, stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            Q.sq_issue_probe(op, sink, stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        out[name] = Q.SQ_PROBE_OPS_PER_LAUNCH * reps / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
+    return out
 
 
 def config_timings(dev, K=20):

@@ -97,6 +97,26 @@ typedef enum { SQ_GATE_GDN = 0, SQ_GATE_KDA = 1 } sq_gate;
 
 typedef enum { SQ_F32 = 0, SQ_BF16 = 1 } sq_dtype;
 
+/* Opcode classes of sq_issue_probe (the decode step's per-element vector
+ * operations): fp32 FMA and fp32 multiply with every operand in a vector
+ * register (a scalar or literal operand halves their rate), fp32 max3 of
+ * absolute values, int32 to fp32 conversion (the class of the byte-to-fp32
+ * widening), signed bit-field extract, funnel shift, FP64 FMA. */
+typedef enum {
+    SQ_PROBE_FMA_F32 = 0,
+    SQ_PROBE_MUL_F32 = 1,
+    SQ_PROBE_MAX3_F32 = 2,
+    SQ_PROBE_CVT_BYTE = 3,
+    SQ_PROBE_BFE = 4,
+    SQ_PROBE_ALIGNBIT = 5,
+    SQ_PROBE_FMA_F64 = 6,
+    SQ_PROBE_COUNT = 7
+} sq_probe_op;
+
+/* Operations of its class that one sq_issue_probe launch performs
+ * (8192 workgroups x 256 lanes x 1024 iterations x 8 chains). */
+#define SQ_PROBE_OPS_PER_LAUNCH 17179869184LL
+
 typedef struct {
     int32_t n_slots;          /* pool capacity in requests (>= 1) */
     int32_t n_heads;          /* heads per request, 1..64 */
@@ -284,6 +304,20 @@ sq_status sq_arith_selfcheck(uint64_t *counts, hipStream_t stream);
  * call.  bytes = 0 is a no-op.  Errors: SQ_EINVAL for NULL or misaligned
  * pointers or a size that is not a multiple of 16. */
 sq_status sq_device_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
+
+/* Measurement helper: one launch of the issue-rate probe of opcode class op
+ * (sq_probe_op) on `stream`.  It performs SQ_PROBE_OPS_PER_LAUNCH operations
+ * of that class in eight independent dependency chains per lane over a
+ * whole-chip grid, so SQ_PROBE_OPS_PER_LAUNCH / (launch duration, timed by
+ * the caller with events on `stream`) is the rate at which the GPU issues
+ * that class: the vector-ALU ceiling the benchmark prices the decode step's
+ * per-element operations at, next to the streaming copy's bandwidth ceiling.
+ * The pages define no such call.  sink: DEVICE pointer to 4 bytes, 4-byte
+ * aligned; the probe's one store is guarded by an equality with a NaN,
+ * which never holds, so nothing is written (the guard keeps the chains'
+ * work from being removed).  Errors: SQ_EINVAL
+ * for op outside [0, SQ_PROBE_COUNT) or a NULL or misaligned sink. */
+sq_status sq_issue_probe(int op, float *sink, hipStream_t stream);
 
 /* Text describing the last non-OK status returned on this thread (error
  * reporting of this library; the pages define no interface).  Never NULL. */

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsq.so")
 ARCH = "gfx950"
 
-SOURCES = ["sq_kernels.hip", "sq_api.cpp"]
+SOURCES = ["sq_kernels.hip", "sq_probe.hip", "sq_api.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=" + ARCH,

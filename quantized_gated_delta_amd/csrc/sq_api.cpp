@@ -359,6 +359,14 @@ sq_status sq_device_copy(const void *src, void *dst, size_t bytes, hipStream_t s
     return e == hipSuccess ? SQ_OK : hip_fail(e, "stream copy launch");
 }
 
+sq_status sq_issue_probe(int op, float *sink, hipStream_t stream) {
+    if (op < 0 || op >= SQ_PROBE_COUNT) return fail(SQ_EINVAL, "op = %d is not a probe class", op);
+    if (!sink) return fail(SQ_EINVAL, "sink is NULL");
+    if (!aligned(sink, 4)) return fail(SQ_EINVAL, "sink is not 4-byte aligned");
+    const hipError_t e = sqk::launch_issue_probe(op, sink, stream);
+    return e == hipSuccess ? SQ_OK : hip_fail(e, "issue probe launch");
+}
+
 sq_status sq_arith_selfcheck(uint64_t *counts, hipStream_t stream) {
     if (!counts) return fail(SQ_EINVAL, "counts is NULL");
     if (!aligned(counts, 8)) return fail(SQ_EINVAL, "counts is not 8-byte aligned");

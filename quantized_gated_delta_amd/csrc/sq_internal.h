@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sq.h"
+
 namespace sqk {
 
 constexpr int kMaxHeads = 64;
@@ -75,6 +77,13 @@ hipError_t launch_f32_decode(float *state, int64_t slot_stride_floats, int32_t n
 
 // Streaming copy of n16 16-byte vectors (a measurement of the HBM rate).
 hipError_t launch_stream_copy(const void *src, void *dst, uint64_t n16, hipStream_t stream);
+// issue-rate probes (sq_probe.hip): SQ_PROBE_OPS_PER_LAUNCH operations of one
+// class per launch
+constexpr int kProbeWorkgroups = 8192;
+constexpr int kProbeIters = 1024;
+static_assert((long long)kProbeWorkgroups * 256 * kProbeIters * 8 == SQ_PROBE_OPS_PER_LAUNCH,
+              "probe shape");
+hipError_t launch_issue_probe(int op, float *sink, hipStream_t stream);
 
 // Exhaustive check of the quantizer's division sequences: counts[0..4)
 // (device) receive the mismatches against the IEEE division.

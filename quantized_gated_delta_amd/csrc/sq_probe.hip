@@ -1,0 +1,126 @@
+// Issue-rate probes for gfx950 (CDNA4): one opcode class per kernel, eight
+// independent dependency chains per lane over a whole-chip grid, so that the
+// rate a launch reaches is the issue limit of that class and not a latency.
+// The benchmark times them with HIP events and prices the decode step's
+// essential per-element operations at the measured rates (the vector-ALU
+// counterpart of the streaming copy as the bandwidth ceiling).
+//
+// Each launch performs kProbeWorkgroups x 256 lanes x kProbeIters x 8
+// operations of its class.  The chains' values are folded into one number per
+// lane, which is stored only if it equals `never`, a NaN (which compares equal
+// to nothing): the work cannot be removed, and nothing is written.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sq_internal.h"
+
+namespace sqk {
+namespace {
+
+constexpr int kChains = 8;
+
+template <int OP>
+__global__ __launch_bounds__(256) void issue_probe_kernel(float a, float b, float never,
+                                                          float *sink) {
+    const float t = (float)threadIdx.x * 0x1p-8f;
+    float acc;
+    if constexpr (OP == SQ_PROBE_FMA_F32 || OP == SQ_PROBE_MUL_F32 || OP == SQ_PROBE_MAX3_F32) {
+        // the fp32 multiply-add class issues two instructions per cycle pair
+        // only when every operand sits in a vector register; a scalar or
+        // literal operand halves the rate, so the arguments are moved to
+        // vector registers the compiler cannot see through
+        float av = a, bv = b;
+        asm volatile("" : "+v"(av), "+v"(bv));
+        float x[kChains];
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) x[c] = 1.0f + t + (float)c;
+        for (int i = 0; i < kProbeIters; ++i) {
+            // max3: a bound that changes every iteration (scalar integer
+            // arithmetic, no vector work), so no two steps fold into one
+            const float ai = __uint_as_float(__float_as_uint(a) + (uint32_t)i);
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) {
+                if constexpr (OP == SQ_PROBE_FMA_F32) x[c] = __builtin_fmaf(x[c], av, bv);
+                else if constexpr (OP == SQ_PROBE_MUL_F32) x[c] = x[c] * av;
+                else x[c] = fmaxf(fmaxf(fabsf(x[c]), ai), b);
+            }
+        }
+        acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) acc += x[c];
+    } else if constexpr (OP == SQ_PROBE_FMA_F64) {
+        double x[kChains];
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) x[c] = 1.0 + (double)t + (double)c;
+        for (int i = 0; i < kProbeIters; ++i) {
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) x[c] = __builtin_fma(x[c], (double)a, (double)b);
+        }
+        double s = 0.0;
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) s += x[c];
+        acc = (float)s;
+    } else {
+        // integer classes: int32 to fp32 conversion, signed bit-field
+        // extract, funnel shift (each chain also takes its neighbour's last
+        // value, so that no sequence of steps folds into one)
+        uint32_t x[kChains];
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) x[c] = threadIdx.x * 2654435761u + (uint32_t)c;
+        for (int i = 0; i < kProbeIters; ++i) {
+            uint32_t y[kChains];
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) {
+                if constexpr (OP == SQ_PROBE_CVT_BYTE)
+                    y[c] = __float_as_uint((float)(int32_t)x[c]);
+                else if constexpr (OP == SQ_PROBE_BFE)
+                    y[c] = (uint32_t)__builtin_amdgcn_sbfe((int)x[c], (int)x[(c + 1) % kChains], 6);
+                else
+                    y[c] = __builtin_amdgcn_alignbit(x[c], x[(c + 1) % kChains], 6);
+            }
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) x[c] = y[c];
+        }
+        uint32_t s = 0;
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) s ^= x[c];
+        acc = __uint_as_float(s);
+    }
+    if (acc == never) sink[0] = acc;
+}
+
+} // namespace
+
+hipError_t launch_issue_probe(int op, float *sink, hipStream_t stream) {
+    const dim3 grid(kProbeWorkgroups), block(256);
+    // a, b keep the fp32 chains finite and normal; `never` is a NaN payload
+    // no chain produces (a NaN never compares equal, so nothing is stored)
+    const float a = 0.9999f, b = 0.5f, never = __builtin_nanf("");
+    switch (op) {
+    case SQ_PROBE_FMA_F32:
+        hipLaunchKernelGGL(issue_probe_kernel<SQ_PROBE_FMA_F32>, grid, block, 0, stream, a, b, never, sink);
+        break;
+    case SQ_PROBE_MUL_F32:
+        hipLaunchKernelGGL(issue_probe_kernel<SQ_PROBE_MUL_F32>, grid, block, 0, stream, a, b, never, sink);
+        break;
+    case SQ_PROBE_MAX3_F32:
+        hipLaunchKernelGGL(issue_probe_kernel<SQ_PROBE_MAX3_F32>, grid, block, 0, stream, a, b, never, sink);
+        break;
+    case SQ_PROBE_CVT_BYTE:
+        hipLaunchKernelGGL(issue_probe_kernel<SQ_PROBE_CVT_BYTE>, grid, block, 0, stream, a, b, never, sink);
+        break;
+    case SQ_PROBE_BFE:
+        hipLaunchKernelGGL(issue_probe_kernel<SQ_PROBE_BFE>, grid, block, 0, stream, a, b, never, sink);
+        break;
+    case SQ_PROBE_ALIGNBIT:
+        hipLaunchKernelGGL(issue_probe_kernel<SQ_PROBE_ALIGNBIT>, grid, block, 0, stream, a, b, never, sink);
+        break;
+    default:
+        hipLaunchKernelGGL(issue_probe_kernel<SQ_PROBE_FMA_F64>, grid, block, 0, stream, a, b, never, sink);
+        break;
+    }
+    return hipGetLastError();
+}
+
+} // namespace sqk

@@ -85,6 +85,8 @@ def lib():
         L.sq_arith_selfcheck.argtypes = [vp, vp]
         L.sq_device_copy.restype = st
         L.sq_device_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+        L.sq_issue_probe.restype = st
+        L.sq_issue_probe.argtypes = [ctypes.c_int, vp, vp]
         L.sq_last_error.restype = ctypes.c_char_p
         L.sq_last_error.argtypes = []
         L.sq_version.restype = ctypes.c_char_p
@@ -264,6 +266,19 @@ def sq_device_copy(src, dst, nbytes: int, stream=None) -> None:
     """Streaming copy of nbytes between two device buffers (measurement helper)."""
     _check(lib().sq_device_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)),
            "sq_device_copy")
+
+
+# Opcode classes of sq_issue_probe and the operations one launch performs.
+SQ_PROBE_FMA_F32, SQ_PROBE_MUL_F32, SQ_PROBE_MAX3_F32, SQ_PROBE_CVT_BYTE = 0, 1, 2, 3
+SQ_PROBE_BFE, SQ_PROBE_ALIGNBIT, SQ_PROBE_FMA_F64, SQ_PROBE_COUNT = 4, 5, 6, 7
+SQ_PROBE_OPS_PER_LAUNCH = 17179869184
+
+
+def sq_issue_probe(op: int, sink, stream=None) -> None:
+    """One launch of the issue-rate probe of opcode class op (measurement
+    helper); sink: a device tensor of at least 4 bytes, never written in
+    practice."""
+    _check(lib().sq_issue_probe(int(op), _ptr(sink), _stream(stream)), "sq_issue_probe")
 
 
 def sq_arith_selfcheck(counts, stream=None) -> None:

@@ -202,6 +202,21 @@ def test_device_copy_validation_without_launch():
     assert "multiple of 16" in Q.sq_last_error()
 
 
+def test_issue_probe_validation_without_launch():
+    """The issue-rate probe rejects an unknown class and a missing or
+    misaligned sink before launching anything; its per-launch operation count
+    matches the header's."""
+    lib = S.lib()
+    assert lib.sq_issue_probe(-1, FAKE_DEV, None) == S.SQ_EINVAL
+    assert lib.sq_issue_probe(Q.SQ_PROBE_COUNT, FAKE_DEV, None) == S.SQ_EINVAL
+    assert "probe class" in Q.sq_last_error()
+    assert lib.sq_issue_probe(Q.SQ_PROBE_FMA_F32, None, None) == S.SQ_EINVAL
+    assert lib.sq_issue_probe(Q.SQ_PROBE_FMA_F32, FAKE_DEV + 2, None) == S.SQ_EINVAL
+    text = open(S.HEADER).read()
+    assert "#define SQ_PROBE_OPS_PER_LAUNCH %dLL" % Q.SQ_PROBE_OPS_PER_LAUNCH in text
+    assert Q.SQ_PROBE_OPS_PER_LAUNCH == 8192 * 256 * 1024 * 8
+
+
 def test_last_error_is_thread_local():
     _expect(Q.SQ_EUNSUPPORTED, Q.sq_pool_bytes, 4, 1, 96, 96, [6], 0)
     seen = []

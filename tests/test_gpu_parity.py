@@ -247,6 +247,32 @@ def test_device_copy():
     assert torch.equal(src, dst)
 
 
+def test_issue_probe_classes():
+    """The issue-rate probes the ALU roofline is priced with: every class runs
+    and writes nothing, and the classes keep their measured order on this
+    GPU: fp32 FMA and multiply issue at least 1.3x faster than max3, and the
+    conversion, bit-field, funnel-shift and FP64 classes within 30 % of max3."""
+    log("issue probes")
+    sink = torch.zeros(1, dtype=torch.float32, device=DEV)
+    stream = torch.cuda.current_stream()
+    rate = {}
+    for op in range(Q.SQ_PROBE_COUNT):
+        Q.sq_issue_probe(op, sink, stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(3):
+            Q.sq_issue_probe(op, sink, stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        rate[op] = Q.SQ_PROBE_OPS_PER_LAUNCH * 3 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
+    log("issue rates (T lane-ops/s): %s" % {k: round(v, 1) for k, v in rate.items()})
+    assert sink.item() == 0.0
+    slow = rate[Q.SQ_PROBE_MAX3_F32]
+    assert rate[Q.SQ_PROBE_FMA_F32] > 1.3 * slow and rate[Q.SQ_PROBE_MUL_F32] > 1.3 * slow
+    for op in (Q.SQ_PROBE_CVT_BYTE, Q.SQ_PROBE_BFE, Q.SQ_PROBE_ALIGNBIT, Q.SQ_PROBE_FMA_F64):
+        assert 0.7 * slow < rate[op] < 1.3 * slow, (op, rate)
+
+
 # ----------------------------------------------------------------- G1
 @pytest.mark.parametrize("d", [64, 128])
 def test_quant_dequant_bit_exact(d):
