@@ -31,12 +31,30 @@ HBM_PEAK_GBS = 8000.0
 # fp32), three products ((a r_i) c_j, k_i u_j and s = S' / c'), two FMAs (the
 # update and the rounding), one max3 (half for the column and half for the
 # row maxima, two new values each) and the pack (funnel shift; 1/16 more at
-# 6 bits).  The ALU roofline prices them at the issue rates sq_issue_probe
-# measures for each class on this GPU.
+# 6 bits).
 def essential_mix(bits):
     ext = {4: 1.0, 6: 1.0625, 8: 0.5}.get(bits, 1.0)
     pack = {6: 1.0625}.get(bits, 1.0)
     return {"bfe": ext, "cvt": 1.0, "mul": 3.0, "fma": 2.0, "max3": 1.0, "alignbit": pack}
+
+
+# Vector-ALU peak from the chip's unit counts: 256 CUs x 4 SIMDs x 64 lanes at
+# 2.4 GHz, each SIMD issuing two wave64 instructions (from two waves) per four
+# cycles, at most one of them from the single-issue classes (conversions,
+# shifts, bit-field extract, funnel shift, max / max3, FP64): 78.6 T lane-ops/s
+# for pairable instructions (the published 157.3 TFLOP/s fp32 at 2 flops per
+# FMA), 39.3 T for single-issue ones.  A mix with n_single single-issue
+# operations of n per element runs at most at
+# n / max(n_single / 39.3 T, n / 78.6 T).
+VALU_PAIR_PEAK = 256 * 4 * 64 * 2.4e9 / 2 / 1e12
+VALU_SINGLE_PEAK = VALU_PAIR_PEAK / 2
+SINGLE_ISSUE = ("bfe", "cvt", "max3", "alignbit")
+
+
+def valu_peak(mix):
+    n = sum(mix.values())
+    n_single = sum(v for k, v in mix.items() if k in SINGLE_ISSUE)
+    return n / max(n_single / VALU_SINGLE_PEAK, n / VALU_PAIR_PEAK)
 
 
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_B512_H48_counters.json")
@@ -384,10 +402,9 @@ def main():
             mix[k] = mix.get(k, 0.0) + v / len(hb)
     ess = sum(mix.values())
     # lane-operations per second: achieved (essential work over the launch
-    # time) and the issue limit of the same operation mix at the measured
-    # per-class rates
+    # time) and the unit-count issue limit of the same operation mix
     alu_achieved = ess * elems / (ms_launch * 1e-3) / 1e12
-    alu_peak = ess / sum(n / rates[k] for k, n in mix.items())
+    alu_peak = valu_peak(mix)
 
     out = {
         "metric": "state-updates/s (req x head x step) and achieved HBM GB/s vs peak at B=512",
@@ -414,6 +431,8 @@ def main():
                      "traffic": None if prof is None else prof["bytes_per_launch"],
                      "essential_valu_per_element": ess,
                      "essential_mix_per_element": mix,
+                     "single_issue_classes": list(SINGLE_ISSUE),
+                     "peak_pairable_T": VALU_PAIR_PEAK, "peak_single_issue_T": VALU_SINGLE_PEAK,
                      "issue_rates_T_lane_ops_per_s": rates,
                      "state_elements_per_launch": elems,
                      "valu_insts_per_element": None if prof is None else prof["valu_insts_per_element"],
@@ -464,17 +483,18 @@ def device_copy_GBps(dev, nbytes=2 << 30, reps=10):
 
 
 def issue_rates(dev, reps=4):
-    """Issue rate of each opcode class of the decode step's per-element work
-    (the library's sq_issue_probe: independent chains of one opcode over the
-    whole chip), timed with HIP events on the launch stream.  Returns
-    {class: T lane-operations per second}."""
+    """Measured issue rate of each opcode class of the decode step's
+    per-element work (the library's sq_issue_probe: independent chains of one
+    opcode over the whole chip; "fma+cvt" interleaves the two, which pair),
+    timed with HIP events on the launch stream, reported next to the
+    unit-count peak.  Returns {class: T lane-operations per second}."""
     import torch
 
     import quantized_gated_delta_amd as Q
     classes = {"fma": Q.SQ_PROBE_FMA_F32, "mul": Q.SQ_PROBE_MUL_F32,
                "max3": Q.SQ_PROBE_MAX3_F32, "cvt": Q.SQ_PROBE_CVT_BYTE,
                "bfe": Q.SQ_PROBE_BFE, "alignbit": Q.SQ_PROBE_ALIGNBIT,
-               "fma_f64": Q.SQ_PROBE_FMA_F64}
+               "fma_f64": Q.SQ_PROBE_FMA_F64, "fma+cvt": Q.SQ_PROBE_FMA_CVT_PAIR}
     sink = torch.zeros(1, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     out = {}

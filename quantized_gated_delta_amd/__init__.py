@@ -9,7 +9,7 @@ from .sq import (SQ_BF16, SQ_EHIP, SQ_EINVAL, SQ_ENOMEM, SQ_EUNSUPPORTED, SQ_F32
                  sq_decode_step, sq_decode_update, sq_dequant_state, sq_device_copy,
                  sq_f32_decode_step, sq_issue_probe, SQ_PROBE_OPS_PER_LAUNCH, SQ_PROBE_COUNT,
                  SQ_PROBE_FMA_F32, SQ_PROBE_MUL_F32, SQ_PROBE_MAX3_F32, SQ_PROBE_CVT_BYTE,
-                 SQ_PROBE_BFE, SQ_PROBE_ALIGNBIT, SQ_PROBE_FMA_F64,
+                 SQ_PROBE_BFE, SQ_PROBE_ALIGNBIT, SQ_PROBE_FMA_F64, SQ_PROBE_FMA_CVT_PAIR,
                  sq_last_error, sq_pool_bytes, sq_pool_create, sq_pool_destroy, sq_pool_layout,
                  sq_pool_set_row_impact, sq_quant_state, version)
 

@@ -169,6 +169,19 @@ template <int BITS> __device__ __forceinline__ int code_at(const Seg<BITS> &s, i
 __device__ __forceinline__ uint32_t code_bits(float s, float ir) {
     return __float_as_uint(__builtin_fmaf(s, ir, 12582912.0f));
 }
+// The same with the magic number passed in: from a vector register (below),
+// the FMA has no literal operand and can pair with another fp32 instruction
+// in the same issue cycle, which a literal or scalar operand prevents.
+__device__ __forceinline__ uint32_t code_bits(float s, float ir, float magic) {
+    return __float_as_uint(__builtin_fmaf(s, ir, magic));
+}
+// 1.5 * 2^23 in a vector register the compiler does not fold back into a
+// literal
+__device__ __forceinline__ float magic_vgpr() {
+    float m = 12582912.0f;
+    asm volatile("" : "+v"(m));
+    return m;
+}
 
 // Pack 16 codes (low BITS bits of f[n], garbage above) into a row segment
 // with funnel shifts: alignbit(f, acc, s) = (acc >> s) | (f << (32 - s))
@@ -702,7 +715,7 @@ __device__ __forceinline__ void kra_quantize_store(float (&x)[4][16], const floa
                                                    Rows<D, BITS, MIXED> rows = {}) {
 #pragma clang fp contract(off)
     using G = Geo<D>;
-    constexpr float MAGIC = 12582912.0f; // 1.5 * 2^23
+    const float MAGIC = magic_vgpr(); // 1.5 * 2^23
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     double *part64 = reinterpret_cast<double *>(lds);
     float *plane = lds; // column maxima; used (and reduced) before part64
@@ -832,7 +845,7 @@ __device__ __forceinline__ void kra_quantize_store(float (&x)[4][16], const floa
         uint32_t f[16];
 #pragma unroll
         for (int n = 0; n < 16; ++n)
-            f[n] = min(max(code_bits(x[m][n], ic[n]), MB - qm), MB + qm);
+            f[n] = min(max(code_bits(x[m][n], ic[n], MAGIC), MB - qm), MB + qm);
         rows.store(rec, row, cg, f);
     }
 }

@@ -270,7 +270,8 @@ def sq_device_copy(src, dst, nbytes: int, stream=None) -> None:
 
 # Opcode classes of sq_issue_probe and the operations one launch performs.
 SQ_PROBE_FMA_F32, SQ_PROBE_MUL_F32, SQ_PROBE_MAX3_F32, SQ_PROBE_CVT_BYTE = 0, 1, 2, 3
-SQ_PROBE_BFE, SQ_PROBE_ALIGNBIT, SQ_PROBE_FMA_F64, SQ_PROBE_COUNT = 4, 5, 6, 7
+SQ_PROBE_BFE, SQ_PROBE_ALIGNBIT, SQ_PROBE_FMA_F64, SQ_PROBE_FMA_CVT_PAIR = 4, 5, 6, 7
+SQ_PROBE_COUNT = 8
 SQ_PROBE_OPS_PER_LAUNCH = 17179869184
 
 

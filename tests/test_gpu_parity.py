@@ -248,10 +248,13 @@ def test_device_copy():
 
 
 def test_issue_probe_classes():
-    """The issue-rate probes the ALU roofline is priced with: every class runs
-    and writes nothing, and the classes keep their measured order on this
-    GPU: fp32 FMA and multiply issue at least 1.3x faster than max3, and the
-    conversion, bit-field, funnel-shift and FP64 classes within 30 % of max3."""
+    """The issue-rate probes reported next to the ALU roofline: every class
+    runs and writes nothing, and the classes keep their measured order on
+    this GPU: fp32 FMA and multiply issue at least 1.3x faster than max3 (two
+    waves' instructions pair), the conversion, bit-field, funnel-shift and
+    FP64 classes within 30 % of max3 (single issue), and FMA interleaved with
+    conversions at least 1.25x faster than conversions alone (a single-issue
+    instruction pairs with another wave's FMA)."""
     log("issue probes")
     sink = torch.zeros(1, dtype=torch.float32, device=DEV)
     stream = torch.cuda.current_stream()
@@ -271,6 +274,7 @@ def test_issue_probe_classes():
     assert rate[Q.SQ_PROBE_FMA_F32] > 1.3 * slow and rate[Q.SQ_PROBE_MUL_F32] > 1.3 * slow
     for op in (Q.SQ_PROBE_CVT_BYTE, Q.SQ_PROBE_BFE, Q.SQ_PROBE_ALIGNBIT, Q.SQ_PROBE_FMA_F64):
         assert 0.7 * slow < rate[op] < 1.3 * slow, (op, rate)
+    assert rate[Q.SQ_PROBE_FMA_CVT_PAIR] > 1.25 * rate[Q.SQ_PROBE_CVT_BYTE], rate
 
 
 # ----------------------------------------------------------------- G1
