@@ -510,10 +510,13 @@ def issue_rates(dev, reps=4):
     return out
 
 
-def config_timings(dev, K=20):
+def config_timings(dev, K=20, G=20, R=5):
     """The smaller workloads: c0 latency; c1 and c2 hot (K back-to-back steps)
     and flushed (a 1 GiB buffer written before each step, so the pool comes
-    from HBM rather than the 256 MB Infinity Cache).  Per-step HIP events."""
+    from HBM rather than the 256 MB Infinity Cache).  Per-step HIP events.
+    "graph": G steps captured in one HIP graph (the step allocates nothing and
+    enqueues no memset), replayed R times between two events, so the host's
+    launch path is out of the per-step time as in a serving loop."""
     import numpy as np
     import torch
 
@@ -564,6 +567,33 @@ def config_timings(dev, K=20):
                                      2 if wl.dtype == "bf16" else 4)
             res[mode] = {"us_per_step": us, "updates_per_s": B * H / (us * 1e-6),
                          "achieved_GBps": nb / (us * 1e-6) / 1e9}
+        # graph replay: capture on a side stream after an eager warm-up there
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            pool.decode_step(slot, ins[0]["q"], ins[0]["k"], ins[0]["v"], ins[0]["beta"],
+                             ins[0]["g"], y)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(G):
+                x = ins[i % 4]
+                pool.decode_step(slot, x["q"], x["k"], x["v"], x["beta"], x["g"], y)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(R):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (R * G)
+        nb = algo_bytes_per_step(B, H, d, lay.head_bits, lay.gate, 2 if wl.dtype == "bf16" else 4)
+        res["graph"] = {"us_per_step": us, "updates_per_s": B * H / (us * 1e-6),
+                        "achieved_GBps": nb / (us * 1e-6) / 1e9}
+        del g
         out[name] = res
         pool.close()
         eprint("%s: %s" % (name, {m: round(v["us_per_step"], 1) for m, v in res.items()}))
