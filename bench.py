@@ -112,6 +112,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prewarm", type=float, default=0.3,
                     help="seconds of untimed steps before the warm-up steps")
+    ap.add_argument("--timeline", action="store_true",
+                    help="only the per-phase wave timeline of the workload's step, from the "
+                         "instrumented build (python -m quantized_gated_delta_amd.build "
+                         "--timeline); prints one JSON line")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for profiles)")
     ap.add_argument("--trajectory", action="store_true",
@@ -135,6 +139,14 @@ def main():
         print("bench.py runs on one GPU only: every (request, head) update is independent "
               "and the path has no collective; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.timeline:
+        tl_lib = os.path.join(ROOT, "quantized_gated_delta_amd", "libsq_timeline.so")
+        if not os.path.exists(tl_lib):
+            print("--timeline needs the instrumented build: python -m "
+                  "quantized_gated_delta_amd.build --timeline", file=sys.stderr)
+            sys.exit(2)
+        os.environ["SQ_LIBRARY"] = tl_lib
 
     import numpy as np
     import torch
@@ -196,6 +208,10 @@ def main():
     steps_in = [{k: to_dev(v) for k, v in wl.step_inputs(layer, t).items()} for t in range(4)]
     y = torch.empty((B * H, d), dtype=io_dt, device=dev)
     stream = torch.cuda.current_stream()
+
+    if args.timeline:
+        print(json.dumps(timeline(pool, slot, steps_in, y, args, B, H)), flush=True)
+        return
 
     def run(pl, sl, n, per_launch=None):
         for i in range(n):
@@ -448,6 +464,75 @@ def main():
         "variants": variants,
     }
     print(json.dumps(out), flush=True)
+
+
+# Phases of the timeline build's stamps (slot pairs; see sq_kernels.hip)
+TL_SLOTS = 16
+TL_PHASES = [("slot resolve", 0, 1), ("tile loads in flight", 1, 2), ("codes to LDS", 2, 3),
+             ("exponent bounds, k.q", 3, 4), ("digit rows", 4, 5), ("barrier 1", 5, 6),
+             ("matrix cores, u, y", 6, 7), ("barrier 2", 7, 8), ("S', column partials", 8, 9),
+             ("barrier 3", 9, 10), ("column fold (waves 0-1)", 10, 11), ("barrier 4", 11, 12),
+             ("requantize, pack, store", 12, 13)]
+
+
+def timeline(pool, slot, steps_in, y, args, B, H):
+    """Per-wave phase durations of one decode launch from the timeline build:
+    untimed steps for --prewarm seconds, then three launches with the stamps
+    cleared before each; the last one is summarised.  Shader-clock cycles
+    (s_memtime), mean and median over the launch's tiles, per wave of the
+    workgroup.  The stamps add a few per cent to the launch time."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from quantized_gated_delta_amd import sq as S
+    L = S.lib()
+    L.sq_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    L.sq_timeline_read.restype = ctypes.c_int
+    L.sq_timeline_clear.restype = ctypes.c_int
+    n_tiles = B * H
+    if n_tiles > 24576:
+        raise SystemExit("the timeline build records the first 24576 tiles; this workload has %d"
+                         % n_tiles)
+    t0, i = time.time(), 0
+    while time.time() - t0 < max(args.prewarm, 0.3):
+        x = steps_in[i % 4]
+        i += 1
+        pool.decode_step(slot, x["q"], x["k"], x["v"], x["beta"], x["g"], y)
+    torch.cuda.synchronize()
+    buf = np.zeros(24576 * 4 * TL_SLOTS, np.uint64)
+    us = []
+    for rep in range(3):
+        if L.sq_timeline_clear() != 0:
+            raise SystemExit("sq_timeline_clear failed")
+        torch.cuda.synchronize()
+        x = steps_in[rep % 4]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pool.decode_step(slot, x["q"], x["k"], x["v"], x["beta"], x["g"], y)
+        e1.record()
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) * 1e3)
+    if L.sq_timeline_read(buf.ctypes.data, buf.nbytes) != 0:
+        raise SystemExit("sq_timeline_read failed")
+    tl = buf.reshape(24576, 4, TL_SLOTS)[:n_tiles].astype(np.int64)
+    if (tl[:, :, :14] == 0).any():
+        raise SystemExit("missing stamps: the workload's heads do not all take the uniform "
+                         "fused path this build instruments")
+    waves = {}
+    for w in range(4):
+        ph = {}
+        for name, a, b in TL_PHASES:
+            dt = tl[:, w, b] - tl[:, w, a]
+            ph[name] = {"mean": float(dt.mean()), "median": float(np.median(dt))}
+        life = tl[:, w, 13] - tl[:, w, 0]
+        ph["wave life"] = {"mean": float(life.mean()), "median": float(np.median(life))}
+        waves["wave %d" % w] = ph
+        eprint("wave %d: " % w + ", ".join("%s %.0f" % (k, v["mean"]) for k, v in ph.items()))
+    return {"timeline": "decode step, per-wave phase cycles (s_memtime)",
+            "workload": args.workload, "tiles": n_tiles, "launch_us_instrumented": us,
+            "waves": waves}
 
 
 def device_copy_GBps(dev, nbytes=2 << 30, reps=10):

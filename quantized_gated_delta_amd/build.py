@@ -16,6 +16,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsq.so")
+# the instrumented timeline build (-DSQ_TIMELINE): decode kernels that store
+# per-wave phase timestamps; loaded instead of libsq.so when SQ_LIBRARY names it
+LIB_TIMELINE = os.path.join(HERE, "libsq_timeline.so")
 ARCH = "gfx950"
 
 SOURCES = ["sq_kernels.hip", "sq_probe.hip", "sq_api.cpp"]
@@ -41,27 +44,30 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile every source and link libsq.so (always rebuilds)."""
+def build(verbose: bool = False, extra=(), timeline: bool = False) -> str:
+    """Compile every source and link libsq.so (always rebuilds); timeline:
+    the instrumented build libsq_timeline.so instead."""
     objs = []
-    build_dir = os.path.join(HERE, "_build")
+    build_dir = os.path.join(HERE, "_build_timeline" if timeline else "_build")
     os.makedirs(build_dir, exist_ok=True)
+    flags = HIP_FLAGS + (["-DSQ_TIMELINE"] if timeline else [])
+    out = LIB_TIMELINE if timeline else LIB
     for src in SOURCES:
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc()] + HIP_FLAGS + list(extra) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc()] + flags + list(extra) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.check_call(cmd)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, timeline="--timeline" in sys.argv))

@@ -50,6 +50,25 @@
 namespace sqk {
 namespace {
 
+// Timeline build (-DSQ_TIMELINE, libsq_timeline.so; never the library's
+// default build): lane 0 of each wave of the first kTlTiles tiles of a decode
+// launch stores the shader clock (s_memtime) at the phase boundaries of the
+// step, kTlSlots slots per wave, read back with sq_timeline_read.  Slots:
+// 0 kernel entry, 1 tile start (record address known), 2 the tile's loads
+// arrived, 3 codes in LDS, 4 exponent bounds and k.q, 5 / 6 before / after
+// barrier 1, 7 / 8 barrier 2, 9 / 10 barrier 3, 11 / 12 barrier 4, 13 end.
+#ifdef SQ_TIMELINE
+constexpr int kTlTiles = 24576, kTlSlots = 16;
+__device__ unsigned long long g_tl[kTlTiles * 4 * kTlSlots];
+#define SQ_TL(k)                                                                                  \
+    do {                                                                                          \
+        if ((threadIdx.x & 63) == 0 && (unsigned)tile < (unsigned)kTlTiles)                       \
+            g_tl[((unsigned)tile * 4u + (threadIdx.x >> 6)) * kTlSlots + (k)] = __builtin_amdgcn_s_memtime(); \
+    } while (0)
+#else
+#define SQ_TL(k) do { } while (0)
+#endif
+
 template <int D> struct Geo {
     static constexpr int NT = D == 128 ? 256 : 64; // lanes per workgroup
     static constexpr int CG = D / 16;              // column groups
@@ -1082,8 +1101,14 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     float *lds_ic = lds + L::IC_F;
     float2 *lds_cu = reinterpret_cast<float2 *>(lds + L::CU_F); // {c_j, u_j} at 18 (j / 16) + j % 16
     float *misc = lds + L::MISC_F; // [15]: GDN gate
+    SQ_TL(1);
     TileIn cur;
     load_tile<D, BITS, KDA, TI, MIXED>(cur, tile, rec_in, io, rows);
+#ifdef SQ_TIMELINE
+    asm volatile("" ::"v"(cur.w[0][0]), "v"(cur.w[3][0]), "v"(cur.kb[1]), "v"(cur.qb[1]), "v"(cur.cj),
+                 "v"(cur.vj), "v"(cur.fk), "v"(cur.fq), "v"(cur.fr), "v"(cur.beta));
+#endif
+    SQ_TL(2);
     uint8_t *rec = cur.rec;
     float *cp = reinterpret_cast<float *>(rec + rows.codes_bytes()) + D;
     const int64_t row_io = tile;
@@ -1112,39 +1137,72 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     }
     // ---- the lane's codes into LDS, one byte each
     if constexpr (MIXED) {
-        // per row, one wavefront-uniform branch on its width
-        lds_u8 *cb = (lds_u8 *)code_b;
+        // per row, one wavefront-uniform branch on its width; rows 0, 1 and
+        // then 2, 3 are gathered into the column dwords, which go to LDS as
+        // in the uniform case below
+        uint32_t pk[16];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int wd = __builtin_amdgcn_readfirstlane(rows.width(band + G::NB * m));
-            const Seg<8> raw = seg_of<8>(cur, m);
-            if (wd == 4) {
-                const Seg<4> sg = as_seg<4>(raw);
+        for (int mp = 0; mp < 2; ++mp) {
+            int c[2][16];
 #pragma unroll
-                for (int n = 0; n < 16; ++n) cb[cbase[n & 7] + 4 * n * NQ + m] = (uint8_t)code_at<4>(sg, n);
-            } else if (wd == 6) {
-                const Seg<6> sg = as_seg<6>(raw);
+            for (int e = 0; e < 2; ++e) {
+                const int m = 2 * mp + e;
+                const int wd = __builtin_amdgcn_readfirstlane(rows.width(band + G::NB * m));
+                const Seg<8> raw = seg_of<8>(cur, m);
+                if (wd == 4) {
+                    const Seg<4> sg = as_seg<4>(raw);
 #pragma unroll
-                for (int n = 0; n < 16; ++n) cb[cbase[n & 7] + 4 * n * NQ + m] = (uint8_t)code_at<6>(sg, n);
-            } else {
+                    for (int n = 0; n < 16; ++n) c[e][n] = code_at<4>(sg, n);
+                } else if (wd == 6) {
+                    const Seg<6> sg = as_seg<6>(raw);
 #pragma unroll
-                for (int n = 0; n < 16; ++n) cb[cbase[n & 7] + 4 * n * NQ + m] = (uint8_t)code_at<8>(raw, n);
+                    for (int n = 0; n < 16; ++n) c[e][n] = code_at<6>(sg, n);
+                } else {
+#pragma unroll
+                    for (int n = 0; n < 16; ++n) c[e][n] = code_at<8>(raw, n);
+                }
             }
+#pragma unroll
+            for (int n = 0; n < 16; ++n) {
+                if (mp == 0)
+                    pk[n] = __builtin_amdgcn_perm((uint32_t)c[1][n], (uint32_t)c[0][n], 0x0c0c0400u);
+                else
+                    pk[n] |= __builtin_amdgcn_perm((uint32_t)c[1][n], (uint32_t)c[0][n], 0x04000c0cu);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            uint32_t *cw = reinterpret_cast<uint32_t *>(code_b + cbase[n] + 4 * n * NQ);
+            cw[0] = pk[n];
+            cw[8 * NQ] = pk[n + 8];
         }
     } else {
         Seg<BITS> seg[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) seg[m] = seg_of<BITS>(cur, m);
-        // single-byte LDS writes (volatile: merged into words, the bytes
-        // would have to be assembled with VALU instructions first)
-        lds_u8 *cb = (lds_u8 *)code_b;
+        // one dword per column: the four rows' codes gathered by two byte
+        // permutes and an OR, one LDS write (single-byte writes, four per
+        // column, kept the LDS busy longer than the three instructions take)
+        // columns n and n + 8 share the address base cbase[n & 7], 8 d / 4
+        // dwords apart, so their two writes issue as one paired write
 #pragma unroll
-        for (int n = 0; n < 16; ++n) {
+        for (int n = 0; n < 8; ++n) {
+            uint32_t wd[2];
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                cb[cbase[n & 7] + 4 * n * NQ + m] = (uint8_t)code_at<BITS>(seg[m], n);
+            for (int h = 0; h < 2; ++h) {
+                uint32_t b[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) b[m] = (uint32_t)code_at<BITS>(seg[m], n + 8 * h);
+                const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u); // b0, b1 in bytes 0, 1
+                const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu); // b2, b3 in bytes 2, 3
+                wd[h] = lo | hi;
+            }
+            uint32_t *cw = reinterpret_cast<uint32_t *>(code_b + cbase[n] + 4 * n * NQ);
+            cw[0] = wd[0];
+            cw[8 * NQ] = wd[1];
         }
     }
+    SQ_TL(3);
     // ---- factors of key k = 4 band + m in FP64: look-up k_i r_i, read-out
     //      q_i r_i (times a_i for KDA; the GDN gate scales the sums).  D = 128:
     //      lane cg < 4 takes the k factor of row m = cg, cg >= 4 the q factor of
@@ -1197,6 +1255,10 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
         Eq = (int)(wave_max_u(eq) >> 23) + 770;
     }
     kq = wave_sum_dpp(kq);
+#ifdef SQ_TIMELINE
+    asm volatile("" ::"v"(kq), "s"(Ek), "s"(Eq));
+#endif
+    SQ_TL(4);
     // ---- digit rows: the k factors as integers X_i = rint(x_i 2^(61 - e)) on
     //      the tile's exponent e (|X| < 2^62, 8 digits, rows 0..7); the q
     //      factors likewise with |X| < 2^30 (4 digits, rows 8..11).  One code
@@ -1211,7 +1273,9 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
         for (int d = 0; d < 8; ++d)
             dig_b[4 * digit_word<D>(r0 + d, band) + jm] = (uint8_t)(dg >> (8 * d));
     }
+    SQ_TL(5);
     __syncthreads();
+    SQ_TL(6);
     if constexpr (!KDA) {
         const float a = misc[15];
         am[0] = am[1] = am[2] = am[3] = a;
@@ -1273,7 +1337,9 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
         lds_cu[18 * cbk + ln] = make_float2(cur.cj, u);
         st<TO>(reinterpret_cast<TO *>(io.y) + row_io * D, j, (float)fma((double)u, (double)kq, Y * cj));
     }
+    SQ_TL(7);
     __syncthreads();
+    SQ_TL(8);
     // ---- decay + delta write in fp32: S'_mn = fma(code, (a_m r_m) c_n, k_m u_n),
     //      each product rounded once; the column-maximum partial of the lane's
     //      four rows replaces the code dword it was computed from (only this
@@ -1294,17 +1360,48 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
 #pragma unroll
         for (int n = 0; n < 16; ++n)
             cws[n] = *reinterpret_cast<const uint32_t *>(code_b + cbase[n & 7] + 4 * n * NQ);
+        if constexpr (D == 128) {
+            // columns n and n + 8 one after the other, so that their two
+            // partials (same address base, 8 d / 4 dwords apart) are written
+            // as one paired write
 #pragma unroll
-        for (int n4 = 0; n4 < 4; ++n4) {
-            const float4 p01 = cu4[2 * n4], p23 = cu4[2 * n4 + 1];
-            const float2 cup[4] = {make_float2(p01.x, p01.y), make_float2(p01.z, p01.w),
-                                   make_float2(p23.x, p23.y), make_float2(p23.z, p23.w)};
+            for (int n2 = 0; n2 < 4; ++n2) {
+                const float4 pa = cu4[n2], pb = cu4[n2 + 4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int n = 4 * n4 + i;
+                for (int e = 0; e < 2; ++e) {
+                    const int n = 2 * n2 + e;
+                    float cmv[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int nn = n + 8 * h;
+                        const float4 p = h ? pb : pa;
+                        const float2 cu = e ? make_float2(p.z, p.w) : make_float2(p.x, p.y);
+                        const uint32_t cw = cws[nn];
+                        float cm = 0.0f;
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            const float code = (float)(int8_t)(cw >> (8 * m));
+                            const float sf = fmaf(code, ar[m] * cu.x, cur.k[m] * cu.y);
+                            x[m][nn] = sf;
+                            cm = fmaxf(cm, fabsf(sf));
+                        }
+                        cmv[h] = cm;
+                    }
+                    if constexpr (!SPLIT && !KRA) {
+                        uint32_t *cwp = reinterpret_cast<uint32_t *>(code_b + cbase[n] + 4 * n * NQ);
+                        cwp[0] = __float_as_uint(cmv[0]);
+                        cwp[8 * NQ] = __float_as_uint(cmv[1]);
+                    }
+                }
+            }
+        } else {
+            // d = 64 (one wave): column by column, which keeps its
+            // register budget without spills
+#pragma unroll
+            for (int n = 0; n < 16; ++n) {
+                const float2 cu = reinterpret_cast<const float2 *>(cu4)[n];
                 uint32_t *cwp = reinterpret_cast<uint32_t *>(code_b + cbase[n & 7] + 4 * n * NQ);
                 const uint32_t cw = cws[n];
-                const float2 cu = cup[i];
                 float cm = 0.0f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -1331,7 +1428,9 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
         }
         return;
     }
+    SQ_TL(9);
     __syncthreads();
+    SQ_TL(10);
     if constexpr (KRA) {
         kra_quantize_store<D, BITS, MIXED>(x, imp, rec, lds, rows);
     } else {
@@ -1348,8 +1447,11 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
             }
             lds_ic[colvec4_idx(t)] = column_scale(__uint_as_float(cmax), cp + t);
         }
+        SQ_TL(11);
         __syncthreads();
+        SQ_TL(12);
         quantize_rows_store<D, BITS, MIXED>(x, lds_ic, rec, rows);
+        SQ_TL(13);
     }
 }
 
@@ -1502,6 +1604,7 @@ __global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(deco
 void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
     __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D, KRA>::TOTAL];
     const int tile = blockIdx.x;
+    SQ_TL(0);
     // Two rounds of scalar loads before the record's address is known: the
     // pool and step arguments, then slot, offset and widths together (the
     // empty asm statements keep the compiler from spreading them over more
@@ -1804,3 +1907,18 @@ hipError_t launch_f32_decode(float *state, int64_t slot_stride_floats, int32_t n
 }
 
 } // namespace sqk
+
+#ifdef SQ_TIMELINE
+// Timeline build only: copy the stamps out (bytes <= the buffer's size) or
+// clear them; both synchronous, on the null stream.  Return hipError_t codes.
+extern "C" int sq_timeline_read(void *dst, size_t bytes) {
+    if (bytes > sizeof(sqk::g_tl)) return (int)hipErrorInvalidValue;
+    return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(sqk::g_tl), bytes, 0, hipMemcpyDeviceToHost);
+}
+extern "C" int sq_timeline_clear() {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(sqk::g_tl));
+    if (e != hipSuccess) return (int)e;
+    return (int)hipMemset(p, 0, sizeof(sqk::g_tl));
+}
+#endif

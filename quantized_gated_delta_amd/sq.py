@@ -15,7 +15,9 @@ import re
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsq.so")
+# the in-tree build; SQ_LIBRARY may name another build of the same sources
+# (the instrumented timeline build, libsq_timeline.so)
+LIB_PATH = os.environ.get("SQ_LIBRARY") or os.path.join(HERE, "libsq.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "sq.h")
 
 SQ_OK, SQ_EINVAL, SQ_EUNSUPPORTED, SQ_ENOMEM, SQ_EHIP = 0, 1, 2, 3, 4
@@ -45,7 +47,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError("libsq.so not built at %s: run __graft_entry__.build() or "
+            raise ImportError("library not built at %s: run __graft_entry__.build() or "
                               "python quantized_gated_delta_amd/build.py" % LIB_PATH)
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64

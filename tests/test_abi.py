@@ -6,6 +6,7 @@ suite runs without a GPU.
 """
 import ctypes
 import functools
+import os
 import threading
 
 import pytest
@@ -215,6 +216,22 @@ def test_issue_probe_validation_without_launch():
     text = open(S.HEADER).read()
     assert "#define SQ_PROBE_OPS_PER_LAUNCH %dLL" % Q.SQ_PROBE_OPS_PER_LAUNCH in text
     assert Q.SQ_PROBE_OPS_PER_LAUNCH == 8192 * 256 * 1024 * 8
+
+
+def test_timeline_symbols_only_in_the_timeline_build():
+    """The default library carries no timeline instrumentation; the
+    instrumented build (libsq_timeline.so, behind bench.py --timeline)
+    exports its two read-back calls next to the whole ABI."""
+    import ctypes
+    default = ctypes.CDLL(S.LIB_PATH)
+    for name in ("sq_timeline_read", "sq_timeline_clear"):
+        assert not hasattr(default, name), name
+    tl_path = os.path.join(os.path.dirname(S.LIB_PATH), "libsq_timeline.so")
+    if not os.path.exists(tl_path):
+        pytest.skip("timeline build not present")
+    tl = ctypes.CDLL(tl_path)
+    for name in ("sq_timeline_read", "sq_timeline_clear") + tuple(Q.header_symbols()):
+        assert hasattr(tl, name), name
 
 
 def test_last_error_is_thread_local():
