@@ -1091,7 +1091,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     using L = DecodeLds<D, KRA>;
     constexpr int NQ = D / 4;              // dwords per code column
     constexpr int BPW = G::CG / G::NW;     // 16-column blocks per wave
-    constexpr int KS = D / 32;             // key steps of the matrix-core look-up
+    constexpr int KS = D / 64;             // key steps of the matrix-core look-up (64 keys)
     static_assert(G::CG % G::NW == 0 && BPW <= 4, "column blocks per wave");
     const int t = threadIdx.x, cg = t % G::CG, band = t / G::CG;
     const int w = t >> 6, lg = (t >> 4) & 3, ln = t & 15;
@@ -1285,13 +1285,18 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     v4i acc[BPW];
 #pragma unroll
     for (int b = 0; b < BPW; ++b) acc[b] = v4i{0, 0, 0, 0};
-    // byte addresses of key step 0.  Code fragments: key step s2 moves only
-    // address bits 5 and 6 (the index bits 3..4 of 8 s2, which the swizzle
-    // XORs but never carries), so step s2 is step 0 XOR (s2 << 5); the code
-    // swizzle splits as above (column 16 c + ln is column ln XOR the
-    // wave-uniform part of c).  Digit fragments: step s2 is 32 s2 bytes on.
-    const int a_dig = 4 * digit_word<D>(ln, 2 * lg);
-    const int a_cw = 4 * code_word<D>(ln, 2 * lg);
+    // byte addresses of key step 0; lane group lg takes keys 16 lg .. 16 lg
+    // + 15 of each step, in A and in B alike (the sum does not depend on how
+    // the matrix core orders the keys within a group, as long as both
+    // operands use the same keys).  Code fragments: 16 aligned bytes (the
+    // swizzle moves whole 4-dword groups); key step s2 moves only address
+    // bit 6 (index bit 4 of 16 s2, which the swizzle XORs but never
+    // carries), so step s2 is step 0 XOR (s2 << 6); the code swizzle splits
+    // as above (column 16 c + ln is column ln XOR the wave-uniform part of
+    // c).  Digit fragments: 8-byte aligned (row pitch d + 8 bytes), read as
+    // two 8-byte halves; step s2 is 64 s2 bytes on.
+    const int a_dig = 4 * digit_word<D>(ln, 4 * lg);
+    const int a_cw = 4 * code_word<D>(ln, 4 * lg);
     const int wu = __builtin_amdgcn_readfirstlane(w);
     int a_code[BPW];
 #pragma unroll
@@ -1301,12 +1306,16 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     }
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
-        long A = 0;
-        if (ln < 12) A = *reinterpret_cast<const long *>(dig_b + a_dig + 32 * s2);
+        v4i A = v4i{0, 0, 0, 0};
+        if (ln < 12) {
+            const long *pa = reinterpret_cast<const long *>(dig_b + a_dig + 64 * s2);
+            const long a0 = pa[0], a1 = pa[1];
+            A = v4i{(int)a0, (int)(a0 >> 32), (int)a1, (int)(a1 >> 32)};
+        }
 #pragma unroll
         for (int b = 0; b < BPW; ++b) {
-            const long B = *reinterpret_cast<const long *>(code_b + (a_code[b] ^ (s2 << 5)));
-            acc[b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, acc[b], 0, 0, 0);
+            const v4i B = *reinterpret_cast<const v4i *>(code_b + (a_code[b] ^ (s2 << 6)));
+            acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, acc[b], 0, 0, 0);
         }
     }
     // lane (lg, ln) holds digits 4 lg .. 4 lg + 3 of column 16 cb + ln: their
