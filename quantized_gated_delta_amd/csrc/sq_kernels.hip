@@ -318,10 +318,11 @@ template <int D, int BITS, bool MIXED> struct Rows {
     __device__ __forceinline__ void store(uint8_t *rec, int row, int cg,
                                          const uint32_t (&f)[16]) const {
         if constexpr (!MIXED) {
-            store_seg<BITS>(rec + offset(row) + cg * (2 * BITS), pack_stream<BITS>(f));
+            // unsigned 32-bit offset from the record base, as for the loads
+            store_seg<BITS>(rec + (uint32_t)(offset(row) + cg * (2 * BITS)), pack_stream<BITS>(f));
         } else {
             const int w = __builtin_amdgcn_readfirstlane(width(row));
-            uint8_t *p = rec + offset(row) + cg * (2 * w);
+            uint8_t *p = rec + (uint32_t)(offset(row) + cg * (2 * w));
             if (w == 4)
                 store_seg<4>(p, pack_stream<4>(f));
             else if (w == 6)
@@ -481,7 +482,7 @@ __device__ __forceinline__ void quantize_rows_store(float (&x)[4][16], const flo
         r = 0.0f;
         ir = 0.0f;
     }
-    if (cg < 4) rp[band + G::NB * cg] = r;
+    if (cg < 4) rp[(uint32_t)(band + G::NB * cg)] = r;
     float irm[4];
     // broadcast lane (band base + m) to the band: ds_swizzle bit mode,
     // lane' = (lane & and_mask) | or_mask within 32 lanes
@@ -770,7 +771,7 @@ __device__ __forceinline__ void kra_quantize_store(float (&x)[4][16], const floa
     if (mrow >= FLT_MIN) r = sqrtf(mrow / im) * (QREF / rows.qmax(row_own));
     if (!(r >= FLT_MIN) || r == INFINITY) r = 0.0f;
     const float ir = r > 0.0f ? 1.0f / r : 0.0f;
-    if (cg < 4) rp[band + G::NB * cg] = r;
+    if (cg < 4) rp[(uint32_t)(band + G::NB * cg)] = r;
     constexpr int AND_MASK = 0x1F & ~(G::CG - 1);
     float irm[4], wm_r[4], wm_i[4];
 #define SQ_BCAST(v, m) __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), AND_MASK | ((m) << 5)))
@@ -1135,7 +1136,11 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     } else {
         if (t == 0) misc[15] = gate_factor(cur.g);
     }
-    // ---- the lane's codes into LDS, one byte each
+    // ---- the lane's codes into LDS: per column n a dword of its four rows'
+    //      code bytes, at d = 128 also kept in cws[n] for the update after the
+    //      matrix cores (no second read of LDS; at d = 64 the register budget
+    //      does not allow it and the update reads them back)
+    uint32_t cws[16];
     if constexpr (MIXED) {
         // per row, one wavefront-uniform branch on its width; rows 0, 1 and
         // then 2, 3 are gathered into the column dwords, which go to LDS as
@@ -1176,6 +1181,10 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
             cw[0] = pk[n];
             cw[8 * NQ] = pk[n + 8];
         }
+        if constexpr (D == 128) {
+#pragma unroll
+            for (int n = 0; n < 16; ++n) cws[n] = pk[n];
+        }
     } else {
         Seg<BITS> seg[4];
 #pragma unroll
@@ -1200,6 +1209,10 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
             uint32_t *cw = reinterpret_cast<uint32_t *>(code_b + cbase[n] + 4 * n * NQ);
             cw[0] = wd[0];
             cw[8 * NQ] = wd[1];
+            if constexpr (D == 128) {
+                cws[n] = wd[0];
+                cws[n + 8] = wd[1];
+            }
         }
     }
     SQ_TL(3);
@@ -1362,13 +1375,14 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
         // the lane's 16 {c, u} pairs: 8 aligned 16-byte reads (stride 18 pairs
         // per column group: 4 cg + 2 n mod 32 words, no bank conflicts)
         const float4 *cu4 = reinterpret_cast<const float4 *>(lds_cu + 18 * cg);
-        // all 16 code dwords are read before the first partial overwrites one
-        // (the compiler cannot tell the addresses apart, so reads placed after
-        // a write would each wait for the LDS round trip)
-        uint32_t cws[16];
+        if constexpr (D != 128) {
+            // all 16 code dwords are read before the first partial overwrites
+            // one (the compiler cannot tell the addresses apart, so reads placed
+            // after a write would each wait for the LDS round trip)
 #pragma unroll
-        for (int n = 0; n < 16; ++n)
-            cws[n] = *reinterpret_cast<const uint32_t *>(code_b + cbase[n & 7] + 4 * n * NQ);
+            for (int n = 0; n < 16; ++n)
+                cws[n] = *reinterpret_cast<const uint32_t *>(code_b + cbase[n & 7] + 4 * n * NQ);
+        }
         if constexpr (D == 128) {
             // columns n and n + 8 one after the other, so that their two
             // partials (same address base, 8 d / 4 dwords apart) are written
@@ -1454,7 +1468,7 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
                 const uint4 v = col[i];
                 cmax = max(cmax, max(max(v.x, v.y), max(v.z, v.w)));
             }
-            lds_ic[colvec4_idx(t)] = column_scale(__uint_as_float(cmax), cp + t);
+            lds_ic[colvec4_idx(t)] = column_scale(__uint_as_float(cmax), cp + (uint32_t)t);
         }
         SQ_TL(11);
         __syncthreads();
@@ -1602,14 +1616,15 @@ __device__ __forceinline__ void decode_tile_f16(uint8_t *rec, int tile, const St
 // behind the others.  Four with the key-row-aware fit (its FP64 column sums
 // take 32 KB of LDS) and in pools with per-key-row widths (whose mixed-width
 // body needs more than 96 VGPRs without spilling); three with both (about
-// 140 VGPRs).
-template <bool KRA, bool ROWS> constexpr int decode_waves_per_eu() {
-    return KRA && ROWS ? 3 : (KRA || ROWS ? 4 : SQ_DECODE_WAVES);
+// 140 VGPRs).  d = 64 tiles (one wave each, small heads) keep four waves
+// per SIMD too: their body spills a few registers at 96.
+template <int D, bool KRA, bool ROWS> constexpr int decode_waves_per_eu() {
+    return KRA && ROWS ? 3 : (KRA || ROWS || D == 64 ? 4 : SQ_DECODE_WAVES);
 }
 // ROWS: the pool has heads with per-key-row widths (their own kernel, so
 // that pools without them keep the register budget of the uniform bodies).
 template <int D, bool KDA, bool SPLIT, bool KRA, bool ROWS, typename TI, typename TO>
-__global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<KRA, ROWS>())))
+__global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<D, KRA, ROWS>())))
 void decode_kernel(PoolView pool, HeadTable tab, StepIO io) {
     __shared__ __attribute__((aligned(16))) float lds[DecodeLds<D, KRA>::TOTAL];
     const int tile = blockIdx.x;
