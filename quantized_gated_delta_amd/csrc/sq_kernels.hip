@@ -1459,13 +1459,16 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
     } else {
         if (t < D) {
             // the 32 band partials of column t: its code dwords, 16 bytes at a
-            // time (eight consecutive columns' swizzles differ in index bits
-            // 2..4, so each 16-byte read of eight lanes covers all banks)
+            // time, in the order of the column's own swizzle (chunk i XOR the
+            // swizzle's chunk bits: eight consecutive columns' swizzles differ
+            // in index bits 2..4, so each 16-byte read of eight lanes covers
+            // all banks; in plain order every lane would read the same four)
             const uint4 *col = reinterpret_cast<const uint4 *>(code_b + 4 * t * NQ);
+            const int sc = (code_sw<D>(t) & (NQ - 1)) >> 2;
             uint32_t cmax = 0;
 #pragma unroll
             for (int i = 0; i < NQ / 4; ++i) {
-                const uint4 v = col[i];
+                const uint4 v = col[i ^ sc];
                 cmax = max(cmax, max(max(v.x, v.y), max(v.z, v.w)));
             }
             lds_ic[colvec4_idx(t)] = column_scale(__uint_as_float(cmax), cp + (uint32_t)t);
