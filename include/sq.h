@@ -34,8 +34,9 @@
  * Memory and ownership
  *  - Every tensor argument is a DEVICE pointer to contiguous row-major
  *    memory that the caller owns (e.g. a torch tensor); the library never
- *    allocates or frees device memory.  Pointers must be 16-byte aligned and
- *    the pool buffer 256-byte aligned.
+ *    allocates or frees device memory (its one buffer of its own, the static
+ *    per-GPU array behind sq_split_step_noalloc, comes with the code object).
+ *    Pointers must be 16-byte aligned and the pool buffer 256-byte aligned.
  *  - Host pointers: the descriptor, head_bits, and the layout outputs.
  *  - An sq_pool is a small host-side handle describing how a caller-owned
  *    device buffer is laid out; destroying it never touches the buffer.
@@ -266,6 +267,31 @@ sq_status sq_decode_update(const sq_pool *pool, const int32_t *slot_idx, int32_t
                            const void *k, const void *v, const void *beta, const void *g,
                            sq_dtype in_dtype, void *y, sq_dtype y_dtype, float *S_out,
                            hipStream_t stream);
+
+/* Bytes of the static per-GPU buffer behind sq_split_step_noalloc. */
+#define SQ_SPLIT_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc): the split
+ * step (sq_decode_update, then sq_quant_state of its S') with S' staged in
+ * a buffer of the library's own instead of a caller workspace.  Both
+ * launches go on `stream`, in that order; afterwards the listed slots hold
+ * exactly the records, and y exactly the values, that sq_decode_update
+ * followed by sq_quant_state of its S_out would give (and so sq_decode_step).
+ * The call allocates nothing: the buffer is a static device array of
+ * SQ_SPLIT_SCRATCH_BYTES (64 MiB) per GPU, which each GPU the library runs
+ * on holds until the process ends; its device address is looked up once per
+ * device on the first call there.  Limit: n * n_heads * d_k * d_v * 4 bytes
+ * of S' must fit, i.e. n * n_heads <= 1024 at d = 128 (4096 at d = 64);
+ * larger n returns SQ_ENOMEM and enqueues nothing.  Every call on one GPU
+ * shares its buffer: calls on one stream are ordered, but calls that
+ * overlap on one GPU (other streams, other threads, other pools) race and
+ * corrupt each other's S'.  The buffer keeps the last call's S'; each call
+ * writes all of the S' it reads, so nothing is cleared.  Arguments, errors
+ * and in-place semantics otherwise as sq_decode_step. */
+sq_status sq_split_step_noalloc(sq_pool *pool, const int32_t *slot_idx, int32_t n, const void *q,
+                                const void *k, const void *v, const void *beta, const void *g,
+                                sq_dtype in_dtype, void *y, sq_dtype y_dtype, hipStream_t stream);
 
 /* The same step on an fp32 state pool state_pool [n_slots, H, d_k, d_v], in
  * place on the listed slots: the unquantized serving default the pages

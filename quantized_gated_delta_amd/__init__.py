@@ -11,6 +11,7 @@ from .sq import (SQ_BF16, SQ_EHIP, SQ_EINVAL, SQ_ENOMEM, SQ_EUNSUPPORTED, SQ_F32
                  SQ_PROBE_FMA_F32, SQ_PROBE_MUL_F32, SQ_PROBE_MAX3_F32, SQ_PROBE_CVT_BYTE,
                  SQ_PROBE_BFE, SQ_PROBE_ALIGNBIT, SQ_PROBE_FMA_F64, SQ_PROBE_FMA_CVT_PAIR,
                  sq_last_error, sq_pool_bytes, sq_pool_create, sq_pool_destroy, sq_pool_layout,
-                 sq_pool_set_row_impact, sq_quant_state, version)
+                 sq_pool_set_row_impact, sq_quant_state, sq_split_step_noalloc,
+                 SQ_SPLIT_SCRATCH_BYTES, version)
 
 __all__ = [n for n in dir() if n.startswith(("sq_", "SQ", "StatePool", "lib", "header", "version"))]

@@ -298,6 +298,36 @@ sq_status sq_decode_update(const sq_pool *pool, const int32_t *slot_idx, int32_t
     return e == hipSuccess ? SQ_OK : hip_fail(e, "decode_update launch");
 }
 
+sq_status sq_split_step_noalloc(sq_pool *pool, const int32_t *slot_idx, int32_t n, const void *q,
+                                const void *k, const void *v, const void *beta, const void *g,
+                                sq_dtype in_dtype, void *y, sq_dtype y_dtype, hipStream_t stream) {
+    sq_status st = check_rows(pool, slot_idx, n);
+    if (st) return st;
+    if (n == 0) return SQ_OK;
+    const uint64_t need = (uint64_t)n * (uint64_t)pool->desc.n_heads * (uint64_t)pool->desc.d_k *
+                          (uint64_t)pool->desc.d_v * sizeof(float);
+    if (need > (uint64_t)SQ_SPLIT_SCRATCH_BYTES)
+        return fail(SQ_ENOMEM,
+                    "S' of %d requests x %d heads needs %llu bytes, the static buffer holds %llu "
+                    "(at most %llu requests of this pool per call)",
+                    n, pool->desc.n_heads, (unsigned long long)need,
+                    (unsigned long long)SQ_SPLIT_SCRATCH_BYTES,
+                    (unsigned long long)(SQ_SPLIT_SCRATCH_BYTES /
+                                         ((uint64_t)pool->desc.n_heads * pool->desc.d_k *
+                                          pool->desc.d_v * sizeof(float))));
+    if ((st = check_step_io(q, k, v, beta, g, in_dtype, y, y_dtype))) return st;
+    sqk::StepIO io;
+    io.slot = slot_idx;
+    io.q = q; io.k = k; io.v = v; io.beta = beta; io.g = g; io.y = y;
+    io.n = n;
+    io.in_bf16 = in_dtype == SQ_BF16;
+    io.y_bf16 = y_dtype == SQ_BF16;
+    io.kda = pool->desc.gate == SQ_GATE_KDA;
+    io.s_out = nullptr;
+    const hipError_t e = sqk::launch_split_step_scratch(pool->view, pool->tab, io, stream);
+    return e == hipSuccess ? SQ_OK : hip_fail(e, "split_step_noalloc launch");
+}
+
 sq_status sq_f32_decode_step(float *state_pool, int32_t n_slots, int32_t n_heads, int32_t d_k,
                              int32_t d_v, sq_gate gate, const int32_t *slot_idx, int32_t n,
                              const void *q, const void *k, const void *v, const void *beta,

@@ -72,6 +72,15 @@ hipError_t launch_decode(const PoolView &pool, const HeadTable &tab, const StepI
 // The decode step without its requantization: S' (fp32) goes to io.s_out.
 hipError_t launch_decode_update(const PoolView &pool, const HeadTable &tab, const StepIO &io,
                                 hipStream_t stream);
+// The split step with S' staged in the library's static per-device buffer
+// (sq_split_step_noalloc): launch_decode_update into it, then
+// launch_quant_state from it, both on `stream`.  io.s_out is ignored.  The
+// caller has checked n * n_heads * d * d * 4 <= SQ_SPLIT_SCRATCH_BYTES.
+hipError_t launch_split_step_scratch(const PoolView &pool, const HeadTable &tab, const StepIO &io,
+                                     hipStream_t stream);
+// Device address of that buffer on the current device (looked up once per
+// device).
+hipError_t scratch_address(float **out);
 hipError_t launch_f32_decode(float *state, int64_t slot_stride_floats, int32_t n_heads, int32_t d,
                              const StepIO &io, hipStream_t stream);
 

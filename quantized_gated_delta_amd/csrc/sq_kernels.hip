@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "sq_internal.h"
 
 #ifndef SQ_DECODE_WAVES
@@ -1933,6 +1935,53 @@ hipError_t launch_f32_decode(float *state, int64_t slot_stride_floats, int32_t n
                   : f32_dispatch<64, false>(state, slot_stride_floats, n_heads, io, stream);
 }
 
+} // namespace sqk
+
+// ---------------------------------------------------------------- split step without allocation
+// Staging buffer of sq_split_step_noalloc: the split step's S' (fp32
+// [n, H, d, d]) between its two launches.  One copy per GPU, placed by the
+// runtime with the code object and held until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: host code
+// uses only the per-device address from hipGetSymbolAddress below.
+static __device__ __align__(256) float scratch[SQ_SPLIT_SCRATCH_BYTES / sizeof(float)];
+
+namespace sqk {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_dev[kMaxDevices]; // device address of `scratch` per device, once looked up
+} // namespace
+
+hipError_t scratch_address(float **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        // first call on this device, with it current: look up this device's copy
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_dev[dev] = static_cast<float *>(p);
+    }
+    *out = g_scratch_dev[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_split_step_scratch(const PoolView &pool, const HeadTable &tab, const StepIO &io_in,
+                                     hipStream_t stream) {
+    float *S = nullptr;
+    hipError_t e = scratch_address(&S);
+    if (e != hipSuccess) return e;
+    // every tile writes its whole d x d block of S' before the second launch
+    // (same stream) reads it, so nothing needs clearing between calls
+    StepIO io = io_in;
+    io.s_out = S;
+    e = launch_decode_update(pool, tab, io, stream);
+    if (e != hipSuccess) return e;
+    return launch_quant_state(pool, tab, io.slot, io.n, S, stream);
+}
 } // namespace sqk
 
 #ifdef SQ_TIMELINE

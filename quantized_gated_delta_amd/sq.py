@@ -78,6 +78,9 @@ def lib():
         L.sq_decode_update.restype = st
         L.sq_decode_update.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, ctypes.c_int, vp,
                                        ctypes.c_int, vp, vp]
+        L.sq_split_step_noalloc.restype = st
+        L.sq_split_step_noalloc.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, ctypes.c_int, vp,
+                                            ctypes.c_int, vp]
         L.sq_f32_decode_step.restype = st
         L.sq_f32_decode_step.argtypes = [vp, i32, i32, i32, i32, ctypes.c_int, vp, i32, vp, vp,
                                          vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp]
@@ -249,6 +252,15 @@ def sq_decode_update(handle, slot_idx, n: int, q, k, v, beta, g, y, S_out, in_dt
                                   _stream(stream)), "sq_decode_update")
 
 
+def sq_split_step_noalloc(handle, slot_idx, n: int, q, k, v, beta, g, y, in_dtype=None,
+                          y_dtype=None, stream=None) -> None:
+    in_dtype = _dtype_code(q) if in_dtype is None else in_dtype
+    y_dtype = _dtype_code(y) if y_dtype is None else y_dtype
+    _check(lib().sq_split_step_noalloc(handle, _ptr(slot_idx), int(n), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(beta), _ptr(g), in_dtype, _ptr(y), y_dtype,
+                                       _stream(stream)), "sq_split_step_noalloc")
+
+
 def sq_f32_decode_step(state, n_slots, n_heads, d_k, d_v, gate, slot_idx, n, q, k, v, beta, g,
                        y, in_dtype=None, y_dtype=None, stream=None) -> None:
     in_dtype = _dtype_code(q) if in_dtype is None else in_dtype
@@ -275,6 +287,7 @@ SQ_PROBE_FMA_F32, SQ_PROBE_MUL_F32, SQ_PROBE_MAX3_F32, SQ_PROBE_CVT_BYTE = 0, 1,
 SQ_PROBE_BFE, SQ_PROBE_ALIGNBIT, SQ_PROBE_FMA_F64, SQ_PROBE_FMA_CVT_PAIR = 4, 5, 6, 7
 SQ_PROBE_COUNT = 8
 SQ_PROBE_OPS_PER_LAUNCH = 17179869184
+SQ_SPLIT_SCRATCH_BYTES = 64 << 20   # the static per-GPU buffer of sq_split_step_noalloc
 
 
 def sq_issue_probe(op: int, sink, stream=None) -> None:
@@ -362,6 +375,12 @@ class StatePool:
         _need(S_out, "S_out", slot_idx.numel() * self.n_heads * self.d * self.d, (torch.float32,))
         sq_decode_update(self.handle, slot_idx, slot_idx.numel(), q, k, v, beta, g, y, S_out,
                          stream=stream)
+
+    def split_step_noalloc(self, slot_idx, q, k, v, beta, g, y, stream=None):
+        """Split step with S' in the library's static buffer: no allocation."""
+        self._step_args(slot_idx, q, k, v, beta, g, y)
+        sq_split_step_noalloc(self.handle, slot_idx, slot_idx.numel(), q, k, v, beta, g, y,
+                              stream=stream)
 
     def check_slots(self, slot_idx, stream=None):
         sq_check_slots(self.handle, slot_idx, slot_idx.numel(), stream)

@@ -179,6 +179,31 @@ def test_split_update_validation_without_launch(pool):
             text="y is NULL")
 
 
+def test_split_noalloc_validation_without_launch():
+    """The no-allocation split step refuses a batch whose S' exceeds its
+    static buffer before any HIP call; n = 0 is a no-op."""
+    P = FAKE_DEV + 4096
+    H, d = 64, 128
+    fit = Q.SQ_SPLIT_SCRATCH_BYTES // (H * d * d * 4)      # 16 requests of 64 heads
+    n_slots = fit + 1
+    h = Q.sq_pool_create(n_slots, H, d, d, [6] * H, 0, FAKE_DEV,
+                         Q.sq_pool_bytes(n_slots, H, d, d, [6] * H, 0))
+    try:
+        Q.sq_split_step_noalloc(h, None, 0, P, P, P, P, P, P, in_dtype=1, y_dtype=1, stream=0)
+        e = _expect(Q.SQ_ENOMEM, Q.sq_split_step_noalloc, h, P, fit + 1, P, P, P, P, P, P, 1, 1,
+                    0, text="static buffer")
+        assert "at most %d requests" % fit in e.text
+        _expect(Q.SQ_EINVAL, Q.sq_split_step_noalloc, h, P, 2, None, P, P, P, P, P, 1, 1, 0,
+                text="q is NULL")
+        _expect(Q.SQ_EINVAL, Q.sq_split_step_noalloc, None, P, 2, P, P, P, P, P, P, 1, 1, 0,
+                text="pool is NULL")
+    finally:
+        Q.sq_pool_destroy(h)
+    # the binding's constant is the header's
+    assert "#define SQ_SPLIT_SCRATCH_BYTES ((size_t)64 << 20)" in open(S.HEADER).read()
+    assert Q.SQ_SPLIT_SCRATCH_BYTES == 64 << 20
+
+
 def test_f32_step_validation_without_launch():
     P = FAKE_DEV
     Q.sq_f32_decode_step(P, 4, 2, 128, 128, 0, None, 0, P, P, P, P, P, P, 1, 1, 0)
