@@ -212,6 +212,15 @@ __device__ __forceinline__ float magic_vgpr() {
 // shift (32 + bits already written) drops the part written before.
 template <int BITS> __device__ __forceinline__ Seg<BITS> pack_stream(const uint32_t (&f)[16]) {
     Seg<BITS> s;
+    if constexpr (BITS == 8) {
+        // whole bytes: the low bytes of four codes gathered by two byte
+        // permutes and an OR per word (three instructions for four codes)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            s.w[q] = __builtin_amdgcn_perm(f[4 * q + 1], f[4 * q], 0x0c0c0400u) |
+                     __builtin_amdgcn_perm(f[4 * q + 3], f[4 * q + 2], 0x04000c0cu);
+        return s;
+    }
     uint32_t acc = 0;
     int fill = 0, word = 0;
 #pragma unroll
@@ -1066,6 +1075,28 @@ __device__ __forceinline__ uint64_t digits8(double X) {
     return K ^ 0x8080808080808080ull;
 }
 
+// 4 x 4 byte transpose: byte m of o[e] = byte e of row word m (a, b, c, d
+// for m = 0..3), by two rounds of byte permutes.
+__device__ __forceinline__ void byte_transpose4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                                uint32_t (&o)[4]) {
+    const uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u); // a0 b0 a1 b1
+    const uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u); // a2 b2 a3 b3
+    const uint32_t cd_lo = __builtin_amdgcn_perm(d, c, 0x05010400u); // c0 d0 c1 d1
+    const uint32_t cd_hi = __builtin_amdgcn_perm(d, c, 0x07030602u); // c2 d2 c3 d3
+    o[0] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);          // a0 b0 c0 d0
+    o[1] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);          // a1 b1 c1 d1
+    o[2] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);          // a2 b2 c2 d2
+    o[3] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);          // a3 b3 c3 d3
+}
+
+// Each byte's low nibble, a 4-bit two's-complement code n, sign-extended to
+// the whole byte: n ^ 8 is in [0, 15], + 0x78 stays below 0x100 (no carry
+// into the next byte), and flipping bit 7 of (n ^ 8) + 0x78 = c + 0x80
+// gives c mod 256 for the code c.
+__device__ __forceinline__ uint32_t sext_low_nibbles(uint32_t x) {
+    return (((x & 0x0F0F0F0Fu) ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
+}
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) volatile uint8_t lds_u8;
 
@@ -1186,6 +1217,43 @@ __device__ __forceinline__ void decode_tile(uint8_t *rec_in, int tile, const Ste
         if constexpr (D == 128) {
 #pragma unroll
             for (int n = 0; n < 16; ++n) cws[n] = pk[n];
+        }
+    } else if constexpr (BITS == 8 || BITS == 4) {
+        // 8 and 4 bits: the code fields sit on byte (nibble) boundaries, so
+        // the column dwords are a 4 x 4 byte transpose of the rows' segment
+        // words (8 byte permutes per 4 dwords), at 4 bits followed by the
+        // sign extension of each byte's low or high nibble (SWAR, 7
+        // instructions per 8 codes) instead of one bit-field extract per code
+        uint32_t cd[16]; // cd[n]: the dword of column 16 cg + n
+        if constexpr (BITS == 8) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t o[4];
+                byte_transpose4(cur.w[0][q], cur.w[1][q], cur.w[2][q], cur.w[3][q], o);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cd[4 * q + e] = o[e];
+            }
+        } else {
+#pragma unroll
+            for (int hw = 0; hw < 2; ++hw) {
+                uint32_t o[4]; // byte m of o[e]: the two codes of columns 8 hw + 2 e, + 1 of row m
+                byte_transpose4(cur.w[0][hw], cur.w[1][hw], cur.w[2][hw], cur.w[3][hw], o);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    cd[8 * hw + 2 * e] = sext_low_nibbles(o[e]);
+                    cd[8 * hw + 2 * e + 1] = sext_low_nibbles(o[e] >> 4);
+                }
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            uint32_t *cw = reinterpret_cast<uint32_t *>(code_b + cbase[n] + 4 * n * NQ);
+            cw[0] = cd[n];
+            cw[8 * NQ] = cd[n + 8];
+            if constexpr (D == 128) {
+                cws[n] = cd[n];
+                cws[n + 8] = cd[n + 8];
+            }
         }
     } else {
         Seg<BITS> seg[4];
