@@ -281,7 +281,8 @@ sq_status sq_decode_update(const sq_pool *pool, const int32_t *slot_idx, int32_t
  * The call allocates nothing: the buffer is a static device array of
  * SQ_SPLIT_SCRATCH_BYTES (64 MiB) per GPU, which each GPU the library runs
  * on holds until the process ends; its device address is looked up once per
- * device on the first call there.  Limit: n * n_heads * d_k * d_v * 4 bytes
+ * device on the first call there (make that first call outside graph
+ * capture; later calls record into a graph like any other launch).  Limit: n * n_heads * d_k * d_v * 4 bytes
  * of S' must fit, i.e. n * n_heads <= 1024 at d = 128 (4096 at d = 64);
  * larger n returns SQ_ENOMEM and enqueues nothing.  Every call on one GPU
  * shares its buffer: calls on one stream are ordered, but calls that
