@@ -452,7 +452,10 @@ def main():
                      "issue_rates_T_lane_ops_per_s": rates,
                      "state_elements_per_launch": elems,
                      "valu_insts_per_element": None if prof is None else prof["valu_insts_per_element"],
-                     "valu_issue_frac_at_4_cycles": None if prof is None else prof["valu_issue_frac"],
+                     "valu_issue_frac": None if prof is None else prof["valu_issue_frac"],
+                     "valu_issue_frac_at_4_cycles":
+                         None if prof is None else prof["valu_issue_frac_at_4_cycles"],
+                     "kernel_src_sha256_16": kernel_hash(),
                      "us_per_launch": ms_launch * 1e3,
                      "kernel": "decode_kernel<128, %s, bf16, bf16>" % layer.gate.upper(),
                      "hbm": {"achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
