@@ -68,6 +68,11 @@
  *  - The decode step updates the listed slots in place.  The entries of
  *    slot_idx must be distinct and in [0, n_slots); slots not listed are
  *    never read or written.  Overlapping calls on the same slots race.
+ *    Debug mode: with the environment variable SQ_DEBUG set (to anything
+ *    but "0"; read at each call), every compute entry point on a pool first
+ *    runs sq_check_slots on its slot indices, which synchronises the stream,
+ *    and returns SQ_EINVAL without enqueueing anything if one is out of
+ *    range or repeated.
  *  - n = 0 is a valid no-op.
  *  - Supported shapes: d_k = d_v = d in {64, 128}; bits in {4, 6, 8, 16},
  *    or 0 with per-key-row widths (sq_pool_create_rows);

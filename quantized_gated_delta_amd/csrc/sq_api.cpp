@@ -9,6 +9,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -130,6 +131,16 @@ sq_status check_rows(const sq_pool *p, const int32_t *slot_idx, int32_t n) {
     return SQ_OK;
 }
 
+// Debug mode: with SQ_DEBUG set to a value other than "0" in the
+// environment (read at each call), every compute entry point on a pool first
+// runs sq_check_slots on its slot indices (which synchronises the stream) and
+// enqueues nothing if one is out of range or repeated: overlapping slots would
+// make the in-place update race.
+bool debug_slots() {
+    const char *v = std::getenv("SQ_DEBUG");
+    return v && v[0] && !(v[0] == '0' && v[1] == 0);
+}
+
 sq_status check_io(const char *name, const void *p, bool need) {
     if (!need) return SQ_OK;
     if (!p) return fail(SQ_EINVAL, "%s is NULL", name);
@@ -243,6 +254,7 @@ sq_status sq_quant_state(sq_pool *pool, const int32_t *slot_idx, int32_t n, cons
     sq_status st = check_rows(pool, slot_idx, n);
     if (st) return st;
     if (n == 0) return SQ_OK;
+    if (debug_slots() && (st = sq_check_slots(pool, slot_idx, n, stream))) return st;
     if ((st = check_io("S", S, true))) return st;
     const hipError_t e = sqk::launch_quant_state(pool->view, pool->tab, slot_idx, n, S, stream);
     return e == hipSuccess ? SQ_OK : hip_fail(e, "quant_state launch");
@@ -253,6 +265,7 @@ sq_status sq_dequant_state(const sq_pool *pool, const int32_t *slot_idx, int32_t
     sq_status st = check_rows(pool, slot_idx, n);
     if (st) return st;
     if (n == 0) return SQ_OK;
+    if (debug_slots() && (st = sq_check_slots(pool, slot_idx, n, stream))) return st;
     if ((st = check_io("S", S, true))) return st;
     const hipError_t e = sqk::launch_dequant_state(pool->view, pool->tab, slot_idx, n, S, stream);
     return e == hipSuccess ? SQ_OK : hip_fail(e, "dequant_state launch");
@@ -264,6 +277,7 @@ sq_status sq_decode_step(sq_pool *pool, const int32_t *slot_idx, int32_t n, cons
     sq_status st = check_rows(pool, slot_idx, n);
     if (st) return st;
     if (n == 0) return SQ_OK;
+    if (debug_slots() && (st = sq_check_slots(pool, slot_idx, n, stream))) return st;
     if ((st = check_step_io(q, k, v, beta, g, in_dtype, y, y_dtype))) return st;
     sqk::StepIO io;
     io.slot = slot_idx;
@@ -284,6 +298,7 @@ sq_status sq_decode_update(const sq_pool *pool, const int32_t *slot_idx, int32_t
     sq_status st = check_rows(pool, slot_idx, n);
     if (st) return st;
     if (n == 0) return SQ_OK;
+    if (debug_slots() && (st = sq_check_slots(pool, slot_idx, n, stream))) return st;
     if ((st = check_step_io(q, k, v, beta, g, in_dtype, y, y_dtype))) return st;
     if ((st = check_io("S_out", S_out, true))) return st;
     sqk::StepIO io;
@@ -304,6 +319,7 @@ sq_status sq_split_step_noalloc(sq_pool *pool, const int32_t *slot_idx, int32_t 
     sq_status st = check_rows(pool, slot_idx, n);
     if (st) return st;
     if (n == 0) return SQ_OK;
+    if (debug_slots() && (st = sq_check_slots(pool, slot_idx, n, stream))) return st;
     const uint64_t need = (uint64_t)n * (uint64_t)pool->desc.n_heads * (uint64_t)pool->desc.d_k *
                           (uint64_t)pool->desc.d_v * sizeof(float);
     if (need > (uint64_t)SQ_SPLIT_SCRATCH_BYTES)

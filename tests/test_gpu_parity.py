@@ -1181,3 +1181,33 @@ def test_decode_step_in_a_hip_graph():
         torch.cuda.synchronize()
         assert torch.equal(graph_pool.buf, side.gpu.buf), t
         assert torch.equal(y_g, y_e), t
+
+
+def test_debug_mode_rejects_bad_slots(monkeypatch):
+    """SQ_DEBUG=1: a repeated or out-of-range slot index is refused before
+    anything is enqueued (pool and y untouched); valid indices still step."""
+    log("debug mode")
+    d, H, B = 128, 2, 4
+    wl = W.custom("gdn", B, H, d, [6, 4], dtype="bf16", n_slots=6, permute=True, seed=31)
+    side = Side(wl, wl.layers[0])
+    side.gpu.buf.fill_(0x5A)
+    x = dev_inputs(wl.step_inputs(wl.layers[0], 0))
+    y = torch.full((B * H, d), 7.0, dtype=torch.bfloat16, device=DEV)
+    monkeypatch.setenv("SQ_DEBUG", "1")
+    for bad, text in (([0, 2, 2, 5], "repeated"), ([0, 1, 6, 3], "outside")):
+        slot = torch.tensor(bad, dtype=torch.int32, device=DEV)
+        with pytest.raises(Q.SQError) as e:
+            side.gpu.decode_step(slot, x["q"], x["k"], x["v"], x["beta"], x["g"], y)
+        assert e.value.status == Q.SQ_EINVAL and text in e.value.text, e.value.text
+        S = torch.zeros((B, H, d, d), dtype=torch.float32, device=DEV)
+        with pytest.raises(Q.SQError):
+            side.gpu.quant_state(slot, S)
+        torch.cuda.synchronize()
+        assert bool((side.gpu.buf == 0x5A).all())
+        assert bool((y.float() == 7.0).all())
+    # valid indices pass the check and run
+    S = torch.zeros((B, H, d, d), dtype=torch.float32, device=DEV)
+    side.gpu.quant_state(side.slot_dev, S)
+    side.gpu.decode_step(side.slot_dev, x["q"], x["k"], x["v"], x["beta"], x["g"], y)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("SQ_DEBUG")
