@@ -54,20 +54,45 @@ def warm_pool(wl, layer, pools):
     torch.cuda.synchronize()
 
 
+def row_widths(H, d, seed):
+    """Per head a non-decreasing 4/6/8 width pattern on the layout's grain."""
+    rng = np.random.default_rng(500 + seed)
+    g = 8 if d == 128 else 16
+    out = []
+    for _ in range(H):
+        cuts = np.sort(rng.integers(0, d // g + 1, 2)) * g
+        out.append([4] * cuts[0] + [6] * (cuts[1] - cuts[0]) + [8] * (d - cuts[1]))
+    return np.array(out, np.uint8)
+
+
 CASES = [
-    # gate, B, H, d, head bits, io dtype
-    ("gdn", 24, 8, 128, [6, 4, 8, 16, 6, 6, 4, 8], "bf16"),   # 192 tiles, 12 MiB of S'
-    ("kda", 40, 6, 64, [4, 6, 8, 16, 6, 4], "f32"),           # 240 tiles at d = 64
+    # gate, B, H, d, head bits (0: per-key-row widths), io dtype, key-row-aware fit
+    ("gdn", 24, 8, 128, [6, 4, 8, 16, 6, 6, 4, 8], "bf16", False),   # 192 tiles, 12 MiB of S'
+    ("kda", 40, 6, 64, [4, 6, 8, 16, 6, 4], "f32", False),           # 240 tiles at d = 64
+    ("kda", 12, 3, 128, [0, 8, 0], "bf16", False),                   # per-key-row widths
+    ("gdn", 10, 4, 128, [6, 16, 4, 8], "bf16", True),                # key-row-aware fit
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "%s-d%d" % (c[0], c[3]))
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "%s-d%d-%s%s" % (
+    c[0], c[3], "rows" if 0 in c[4] else "heads", "-kra" if c[6] else ""))
 def test_noalloc_matches_split_and_fused(case):
-    gate, B, H, d, bits, dtype = case
+    gate, B, H, d, bits, dtype, kra = case
     log("noalloc %s" % (case,))
-    wl = W.custom(gate, B, H, d, bits, dtype=dtype, n_slots=B + 7, permute=True, seed=21)
+    rb = row_widths(H, d, B) if 0 in bits else None
+    wl = W.custom(gate, B, H, d, bits, dtype=dtype, n_slots=B + 7, permute=True, seed=21,
+                  row_bits=rb)
     layer = wl.layers[0]
-    mk = lambda: Q.StatePool(wl.n_slots, H, d, bits, gate)
+    imp = None
+    if kra:   # row-impact scores over about three decades, kept alive for every launch
+        rng = np.random.default_rng(77)
+        imp = torch.from_numpy(np.exp(rng.normal(0.0, 1.5, (H, d))).astype(np.float32)).to(DEV)
+
+    def mk():
+        p = Q.StatePool(wl.n_slots, H, d, bits, gate, row_bits=layer.row_bits)
+        if imp is not None:
+            p.set_row_impact(imp)
+        return p
     na, sp, fu = mk(), mk(), mk()
     warm_pool(wl, layer, [na, sp, fu])
     ydt = torch.float32 if dtype == "f32" else torch.bfloat16
