@@ -128,11 +128,12 @@ def main():
                     help="FP16 pivot heads per layer for the --allocate comparison")
     ap.add_argument("--calib", type=int, default=256,
                     help="requests whose warm-up states calibrate the allocation")
-    ap.add_argument("--only", choices=("kda_mixed", "kda_rows", "kra", "kda_rows_kra"),
+    ap.add_argument("--only", choices=("kda_mixed", "kda_rows", "kra", "kda_rows_kra",
+                                       "fp32_state"),
                     help="time only this variant of the B=512 H=48 step (for profiling runs): "
                          "KDA 4/6/8 per head, KDA with per-key-row widths, the key-row-aware "
-                         "fit on the 6-bit GDN pool, or that fit on the per-key-row widths; "
-                         "prints one short JSON line")
+                         "fit on the 6-bit GDN pool, that fit on the per-key-row widths, or "
+                         "the fp32-state comparator; prints one short JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -279,7 +280,19 @@ def main():
         return pk, run_k, kb, wk, lk
 
     if args.only:
-        if args.only == "kra":
+        if args.only == "fp32_state":
+            def run_f(n, ev=None):
+                for i in range(n):
+                    x = steps_in[i % 4]
+                    if ev is not None:
+                        ev[i][0].record(stream)
+                    Q.sq_f32_decode_step(state, wl.n_slots, H, d, d, int(kda), slot_l, B, x["q"],
+                                         x["k"], x["v"], x["beta"], x["g"], y)
+                    if ev is not None:
+                        ev[i][1].record(stream)
+            o_ms, o_launch = timed(None, None, run_f)
+            ob = f32_bytes_per_step(B, H, d, layer.gate, 2 if wl.dtype == "bf16" else 4)
+        elif args.only == "kra":
             pool.set_row_impact(torch.from_numpy(impact_from_workload(wl, layer, 4)).to(dev))
             o_ms, o_launch = timed(pool, slot)
             ob = algo_bytes_per_step(B, H, d, layer.head_bits, layer.gate)

@@ -101,6 +101,10 @@ DECODE_VARIANTS = {
             "GDN 6-bit with the key-row-aware fit in the requantizer", "gdn6_kra"),
     "kda_rows_kra": ("--only kda_rows_kra", "decode_kernel<128, true, false, true, true",
                      "KDA, 4/6/8-bit key rows with the key-row-aware fit", "kda468rows_kra"),
+    # the unquantized comparator (the same step on an fp32 state pool); its
+    # launches include the warm-up's, which have the same shape
+    "fp32_state": ("--only fp32_state", "f32_decode_kernel<128, false, unsigned short",
+                   "fp32 state pool, the unquantized comparator (GDN)", "f32state"),
 }
 PMC_SETS = [
     "SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_VALU2 SQ_BUSY_CYCLES SQ_WAVE_CYCLES "
@@ -247,6 +251,7 @@ def decode_main(o: str, outdir: str, variants: list) -> None:
             "c3b": bench.algo_bytes_per_step(B, H, d, c3b.head_bits, "gdn"),
             "kda_mixed": bench.algo_bytes_per_step(B, H, d, kda, "kda"),
             "kda_rows": bench.algo_bytes_per_step(B, H, d, [6] * H, "kda")}
+    algo["fp32_state"] = bench.f32_bytes_per_step(B, H, d, "gdn")
     algo["kra"] = algo["c3a"]
     algo["kda_rows_kra"] = algo["kda_rows"]
     variants = variants or list(DECODE_VARIANTS)
